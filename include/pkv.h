@@ -1,0 +1,251 @@
+/*
+ * pkv.h -- C ABI of libpkv: single-token decode attention over a paged KV cache
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages), cited by tag and section:
+ *   [SMTS] "Sub-Millisecond Token Scheduling: Inside Disaggregated KV-Cache
+ *          Paging for Frontier LLMs" (factnode.online)
+ *   [LLMI] "LLM inference: prefill, decode, KV cache" (systemcraft.online, c03)
+ *   [MTKV] "Architecting Multi-Tier Disaggregated KV-Cache Hierarchies for
+ *          Terabyte-Scale LLM Inference" (ultrainstinct.tech)
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are caller-owned, contiguous, row-major device memory. The
+ *     library never allocates device memory in these calls and never
+ *     synchronises: each call enqueues kernels on `stream` (a hipStream_t
+ *     passed as void*; NULL means the null stream) and returns.
+ *   - Results are status codes; no exception crosses the ABI.
+ *     pkv_status_string() gives text. Arguments are validated on the host
+ *     before anything is enqueued; an invalid call enqueues nothing.
+ *   - Values living in device memory (block ids, slots, lengths, scales) cannot
+ *     be validated on the host. The kernels never access memory outside the
+ *     caches for an out-of-range block id or slot: a write to one is skipped,
+ *     and a read of one reads block 0 instead; results for such inputs are
+ *     unspecified.
+ *   - Launch errors reported by the HIP runtime are returned as PKV_ERR_HIP.
+ *
+ * Cache layout ([MTKV] "High-Throughput Paged Attention Kernel Integration",
+ * K_Buffer / V_Buffer shape): K and V caches are separate arrays
+ * [num_blocks, n_kv, block_size, d_head]; element type bfloat16, or OCP FP8
+ * E4M3FN codes (one byte) with one fp32 scale per KV head for K and one for
+ * V ([SMTS] "Technical Q&A", per-head scaling factors). One (block, head)
+ * tile of block_size * d_head elements is contiguous.
+ *
+ * Supported geometry: block_size in {16, 32}; d_head in {64, 128};
+ * n_q = G * n_kv with G in {1, 2, 4, 8, 16} or any multiple of 16.
+ * Anything else returns PKV_ERR_UNSUPPORTED.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,
+  PKV_ERR_UNSUPPORTED = 2,
+  PKV_ERR_OUT_OF_BLOCKS = 3,
+  PKV_ERR_WORKSPACE_TOO_SMALL = 4,
+  PKV_ERR_HIP = 5
+} pkv_status;
+
+typedef enum { PKV_BF16 = 0, PKV_FP8_E4M3 = 1, PKV_FP32 = 2 } pkv_dtype;
+
+/* Geometry of one layer's K/V pools (both share it). kv_dtype is a pkv_dtype:
+ * PKV_BF16 or PKV_FP8_E4M3. */
+typedef struct {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t n_kv;
+  int32_t d_head;
+  int32_t kv_dtype;
+} pkv_cache_desc;
+
+/* Text for a status code (static storage). */
+const char* pkv_status_string(pkv_status s);
+
+/* Library version string, e.g. "pkv 0.1 gfx950". */
+const char* pkv_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Slot mapping ([LLMI] "PagedAttention & Memory Management (vLLM)": logical
+ * block pos / block_size of a sequence maps through its block-table row to a
+ * physical block; the token sits at offset pos % block_size).
+ *
+ *   slots_out[b] = block_tables[b * max_blocks_per_seq + positions[b] / bs] * bs
+ *                  + positions[b] % bs                       (int64)
+ * positions[b] < 0, or positions[b] / bs >= max_blocks_per_seq, gives -1.
+ * block_tables: int32 [B, max_blocks_per_seq]; positions: int32 [B];
+ * slots_out: int64 [B]. All device pointers. B == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* positions, int32_t B, int32_t block_size,
+                            int64_t* slots_out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kv_append ([LLMI] flow step 5 and "Why We Need the Key-Value (KV) Cache":
+ * the new token's key and value are appended to the cache before attention).
+ *
+ * For each token t < T and head h < n_kv:
+ *   k_cache[slot / bs, h, slot % bs, :] = store(k_new[t, h, :], k_scale[h])
+ *   (same for V), with slot = slot_mapping[t] (int64, device).
+ * store() copies the bfloat16 pattern for a BF16 cache; for an FP8 cache it is
+ * E4M3FN(round-to-nearest-even, saturating at +-448)(float32(x) / k_scale[h]),
+ * the division in IEEE binary32; NaN stores 0x7F.
+ * k_new, v_new: bfloat16 [T, n_kv, d_head] (device). k_scale, v_scale: fp32
+ * [n_kv] device pointers, required for FP8, ignored for BF16.
+ * A negative slot is skipped (padding). A slot >= num_blocks * bs is skipped.
+ * Two tokens with the same slot: the stored value is unspecified.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_kv_append(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
+                         const void* k_new, const void* v_new,
+                         const int64_t* slot_mapping, int32_t T,
+                         const float* k_scale, const float* v_scale, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Paged decode attention ([MTKV] "High-Throughput Paged Attention Kernel
+ * Integration": one query token per sequence attends over its cached tokens
+ * through the block table; query head h reads KV head h / G; [MTKV]
+ * "Mathematical Formulation of Block Salience": weights are
+ * softmax(scale * q . k)).
+ *
+ *   out[b, h, :] = sum_{t < ctx_b} w_t * V_b[t, h / G, :],
+ *   w = softmax_t(scale * q[b, h, :] . K_b[t, h / G, :]),
+ * with K_b[t, g, :] = k_cache[block_tables[b, t / bs], g, t % bs, :]
+ * (times k_scale[g] for FP8; likewise V with v_scale). ctx_b == 0 gives zeros.
+ * Slots past ctx_b in a sequence's last block never contribute, whatever they
+ * hold (NaN included); table entries past cdiv(ctx_b, bs) are never read.
+ *
+ * q: bfloat16 [B, n_q, d_head]. out: [B, n_q, d_head] of out_dtype (PKV_FP32
+ * or PKV_BF16). block_tables: int32 [B, max_blocks_per_seq].
+ * context_lens: int32 [B]. max_context_len: an upper bound of context_lens
+ * supplied by the host (no device-to-host read is made); it must satisfy
+ * max_context_len <= max_blocks_per_seq * block_size.
+ *
+ * Split-K: the context is cut into partitions of partition_size tokens (a
+ * multiple of block_size; 0 picks a size from the geometry and the GPU). With
+ * more than one partition, per-partition statistics go to `workspace` and a
+ * log-sum-exp merge (pkv_splitk_reduce) runs after; `workspace_bytes` must be
+ * at least pkv_decode_workspace_bytes(...) for the same arguments, else
+ * PKV_ERR_WORKSPACE_TOO_SMALL. With one partition the workspace is unused and
+ * may be NULL.
+ * Accumulation is fp32. Calls that share a workspace must not overlap.
+ * ------------------------------------------------------------------------- */
+size_t pkv_decode_workspace_bytes(int32_t B, int32_t n_q, int32_t d_head,
+                                  int32_t max_context_len, int32_t partition_size);
+
+/* The partition size partition_size == 0 resolves to (a multiple of the block
+ * size), for inspection and for sizing the workspace. */
+int32_t pkv_default_partition_size(const pkv_cache_desc* desc, int32_t B, int32_t n_q,
+                                   int32_t max_context_len);
+
+pkv_status pkv_paged_decode_attention(const pkv_cache_desc* desc, void* out, int32_t out_dtype,
+                                      const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t B, int32_t n_q,
+                                      int32_t max_context_len, float scale,
+                                      const float* k_scale, const float* v_scale,
+                                      int32_t partition_size, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * The two halves of pkv_paged_decode_attention, callable on their own (for
+ * timing each kernel and checking partial statistics).
+ *
+ * pkv_paged_decode_partials writes, for every sequence b, head h and
+ * partition j < cdiv(ctx_b, P) (P = the resolved partition size):
+ *   m[b, h, j]    = log2(e) * max_{t in j} scale * q . k_t     (fp32)
+ *   l[b, h, j]    = sum_{t in j} exp(scale * q . k_t - m / log2(e))
+ *   o[b, h, j, :] = sum_{t in j} exp(...) v_t / l[b, h, j]
+ * into three arrays carved from `workspace` in that order (m, then l, each
+ * fp32 [B, n_q, P_max], then o fp32 [B, n_q, P_max, d_head], with
+ * P_max = cdiv(max_context_len, P)). Entries j >= cdiv(ctx_b, P) are not
+ * written. pkv_splitk_reduce merges them ([MTKV] kernel's running max / sum /
+ * rescaled accumulator, applied across partitions):
+ *   M = max_j m_j,  w_j = l_j * 2^(m_j - M),  out = sum_j w_j o_j / sum_j w_j
+ * over j < cdiv(ctx_b, partition_size); ctx_b == 0 gives zeros.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_paged_decode_partials(const pkv_cache_desc* desc, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t B, int32_t n_q,
+                                     int32_t max_context_len, float scale,
+                                     const float* k_scale, const float* v_scale,
+                                     int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+pkv_status pkv_splitk_reduce(void* out, int32_t out_dtype, const float* m, const float* l,
+                             const float* o, const int32_t* context_lens, int32_t B,
+                             int32_t n_q, int32_t d_head, int32_t max_partitions,
+                             int32_t partition_size, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Copy-on-write block copy ([SMTS] "Paged KV-Cache with Radix Tree Prefix
+ * Cache": sequences sharing a prefix point at the same physical blocks through
+ * copy-on-write pointers; a shared block is copied before it is written).
+ * pairs: int32 [n_pairs, 2] (src, dst) on the device. Every head's tile of
+ * block src is copied to block dst in both caches. Destinations must be
+ * distinct and must not be sources of the same call. Ids outside the pool are
+ * skipped.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_copy_blocks(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
+                           const int32_t* pairs, int32_t n_pairs, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Gather (test export): dense copies of one sequence's cache rows,
+ *   k_out[t, h, :] = k_cache[block_table_row[t / bs], h, t % bs, :]
+ * for t < context_len (raw element patterns, no conversion).
+ * k_out, v_out: [context_len, n_kv, d_head] of the cache's element type.
+ * block_table_row: int32 [>= cdiv(context_len, bs)] on the device.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_gather_kv(const pkv_cache_desc* desc, void* k_out, void* v_out,
+                         const void* k_cache, const void* v_cache,
+                         const int32_t* block_table_row, int32_t context_len, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host block manager ([SMTS] "Paged KV-Cache with Radix Tree Prefix Cache":
+ * physical blocks with reference counts, slot allocation popping the free
+ * pool, exhaustion asking the scheduler to preempt; copy-on-write sharing).
+ * Host memory only, owned by the handle. Not thread-safe.
+ *
+ * Pool of num_blocks blocks starts as [0, 1, ..., num_blocks-1]; allocation
+ * pops the last entry; freed blocks are pushed back in the sequence's logical
+ * order. Sequences are named by caller-chosen int64 ids.
+ *
+ * append_slot(seq): reserves the sequence's next token position (creating the
+ * sequence on first use). At a block boundary a fresh block is allocated;
+ * otherwise the last block is written, and if it is shared (ref_count > 1) a
+ * private block is allocated first and *cow_src / *cow_dst name the copy to
+ * make (pkv_copy_blocks) -- else both are -1. *slot receives the token's slot.
+ * On exhaustion nothing changes and PKV_ERR_OUT_OF_BLOCKS is returned.
+ * fork(parent, child): child shares every block of parent (ref_count + 1).
+ * free(seq): ref_count - 1 on each block; blocks reaching 0 return to the pool.
+ * export_table: rows of block ids for `seqs`, padded with 0 (never read),
+ * into host int32 [B, max_blocks]; a sequence wider than max_blocks is an
+ * invalid argument.
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_bm pkv_bm;
+
+pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size, pkv_bm** out);
+void pkv_bm_destroy(pkv_bm* bm);
+pkv_status pkv_bm_append_slot(pkv_bm* bm, int64_t seq, int64_t* slot, int32_t* cow_src,
+                              int32_t* cow_dst);
+pkv_status pkv_bm_fork(pkv_bm* bm, int64_t parent, int64_t child);
+pkv_status pkv_bm_free(pkv_bm* bm, int64_t seq);
+pkv_status pkv_bm_export_table(const pkv_bm* bm, const int64_t* seqs, int32_t B,
+                               int32_t max_blocks, int32_t* host_table);
+/* Token count of a sequence (-1 if unknown), free-pool size, a block's count. */
+int64_t pkv_bm_seq_len(const pkv_bm* bm, int64_t seq);
+int32_t pkv_bm_num_free(const pkv_bm* bm);
+int32_t pkv_bm_ref_count(const pkv_bm* bm, int32_t block);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

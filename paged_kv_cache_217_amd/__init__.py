@@ -1,0 +1,30 @@
+"""MI355X-native paged KV cache and single-token decode attention.
+
+The compute path is libpkv.so (hand-written HIP for gfx950 behind the C ABI
+in include/pkv.h); this package is its Python binding. Importing it loads the
+in-tree library and fails loudly if it has not been built.
+"""
+
+from ._lib import (  # noqa: F401
+    BlockManager,
+    CacheDesc,
+    OutOfBlocks,
+    PkvError,
+    cache_desc,
+    copy_blocks,
+    decode_workspace_bytes,
+    default_partition_size,
+    gather_kv,
+    kv_append,
+    lib,
+    make_workspace,
+    paged_decode_attention,
+    paged_decode_partials,
+    partial_views,
+    slot_mapping,
+    splitk_reduce,
+    status_string,
+    version,
+)
+
+lib()

@@ -1,0 +1,278 @@
+// C ABI of libpkv: host-side validation, workspace carving, launch geometry.
+// The operations and their sources are documented in include/pkv.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+using pkv::kMaxReducePartitions;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+pkv_status from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+pkv_status check_desc(const pkv_cache_desc* d) {
+  if (!d || d->num_blocks <= 0 || d->n_kv <= 0) return PKV_ERR_INVALID_ARG;
+  if (d->kv_dtype != PKV_BF16 && d->kv_dtype != PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+  if (d->block_size != 16 && d->block_size != 32) return PKV_ERR_UNSUPPORTED;
+  if (d->d_head != 64 && d->d_head != 128) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+// Heads served by one workgroup of the decode kernel for a group of G.
+int head_tile(int G) { return G <= 8 ? G : 8; }
+
+int32_t pick_partition(const pkv_cache_desc* d, int32_t B, int32_t n_q, int32_t max_ctx) {
+  // Aim for >= 2048 workgroups (8 per CU on 256 CUs) without going below 256
+  // tokens per partition (each of 4 waves then still owns several blocks).
+  const int G = n_q / d->n_kv;
+  const int64_t units = static_cast<int64_t>(B) * d->n_kv * (G / head_tile(G));
+  int64_t P = 256;
+  while (P < max_ctx && P < 4096 && units * cdiv(max_ctx, 2 * P) >= 2048) P *= 2;
+  while (cdiv(max_ctx, P) > kMaxReducePartitions) P *= 2;
+  return static_cast<int32_t>(P);
+}
+
+struct Workspace {
+  float* m;
+  float* l;
+  float* o;
+};
+
+size_t workspace_bytes(int64_t B, int64_t n_q, int64_t d, int64_t P_max) {
+  const size_t ml = align256(static_cast<size_t>(B * n_q * P_max) * sizeof(float));
+  const size_t o = align256(static_cast<size_t>(B * n_q * P_max * d) * sizeof(float));
+  return 2 * ml + o;
+}
+
+Workspace carve(void* ws, int64_t B, int64_t n_q, int64_t P_max) {
+  const size_t ml = align256(static_cast<size_t>(B * n_q * P_max) * sizeof(float));
+  char* base = static_cast<char*>(ws);
+  return {reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + ml),
+          reinterpret_cast<float*>(base + 2 * ml)};
+}
+
+// Shared validation of the decode entry points; fills `a` and the resolved
+// partition count.
+pkv_status prepare_decode(const pkv_cache_desc* desc, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t B,
+                          int32_t n_q, int32_t max_context_len, float scale,
+                          const float* k_scale, const float* v_scale, int32_t partition_size,
+                          pkv::DecodeArgs* a) {
+  pkv_status st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (B < 0 || n_q <= 0 || n_q % desc->n_kv != 0) return PKV_ERR_INVALID_ARG;
+  if (max_context_len < 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_context_len) >
+      static_cast<int64_t>(max_blocks_per_seq) * desc->block_size)
+    return PKV_ERR_INVALID_ARG;
+  if (partition_size < 0 || (partition_size > 0 && partition_size % desc->block_size != 0))
+    return PKV_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return PKV_ERR_INVALID_ARG;
+  if (B > 0 && (!q || !k_cache || !v_cache || !block_tables || !context_lens))
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
+  if (desc->kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  const int G = n_q / desc->n_kv;
+  if (!pkv::decode_supported(desc->d_head, desc->block_size, G, desc->kv_dtype))
+    return PKV_ERR_UNSUPPORTED;
+  if (B > 65535) return PKV_ERR_UNSUPPORTED;
+
+  const int32_t P = partition_size > 0 ? partition_size
+                                       : pick_partition(desc, B, n_q, max_context_len);
+  const int64_t P_max = std::max<int64_t>(1, cdiv(max_context_len, P));
+  if (P_max > kMaxReducePartitions) return PKV_ERR_UNSUPPORTED;
+
+  *a = pkv::DecodeArgs{};
+  a->q = static_cast<const uint16_t*>(q);
+  a->k_cache = static_cast<const uint8_t*>(k_cache);
+  a->v_cache = static_cast<const uint8_t*>(v_cache);
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->k_scale = k_scale;
+  a->v_scale = v_scale;
+  a->B = B;
+  a->n_q = n_q;
+  a->n_kv = desc->n_kv;
+  a->d = desc->d_head;
+  a->bs = desc->block_size;
+  a->num_blocks = desc->num_blocks;
+  a->max_blocks = max_blocks_per_seq;
+  a->kv_dtype = desc->kv_dtype;
+  a->partition = P;
+  a->P_max = static_cast<int>(P_max);
+  a->scale = scale;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported geometry or dtype";
+    case PKV_ERR_OUT_OF_BLOCKS: return "KV block pool exhausted (preempt a sequence)";
+    case PKV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PKV_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
+
+pkv_status pkv_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* positions, int32_t B, int32_t block_size,
+                            int64_t* slots_out, void* stream) {
+  if (B < 0 || max_blocks_per_seq <= 0 || block_size <= 0) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  if (!block_tables || !positions || !slots_out) return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_slot_mapping(block_tables, max_blocks_per_seq, positions, B,
+                                           block_size, slots_out, as_stream(stream)));
+}
+
+pkv_status pkv_kv_append(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
+                         const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                         int32_t T, const float* k_scale, const float* v_scale, void* stream) {
+  pkv_status st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (T < 0) return PKV_ERR_INVALID_ARG;
+  if (T == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return PKV_ERR_INVALID_ARG;
+  if (desc->kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_kv_append(*desc, k_cache, v_cache, k_new, v_new, slot_mapping, T,
+                                        k_scale, v_scale, as_stream(stream)));
+}
+
+size_t pkv_decode_workspace_bytes(int32_t B, int32_t n_q, int32_t d_head,
+                                  int32_t max_context_len, int32_t partition_size) {
+  if (B <= 0 || n_q <= 0 || d_head <= 0 || max_context_len < 0 || partition_size <= 0) return 0;
+  const int64_t P_max = std::max<int64_t>(1, cdiv(max_context_len, partition_size));
+  return workspace_bytes(B, n_q, d_head, P_max);
+}
+
+int32_t pkv_default_partition_size(const pkv_cache_desc* desc, int32_t B, int32_t n_q,
+                                   int32_t max_context_len) {
+  if (check_desc(desc) != PKV_OK || B < 0 || n_q <= 0 || n_q % desc->n_kv != 0 ||
+      max_context_len < 0)
+    return 0;
+  return pick_partition(desc, B, n_q, max_context_len);
+}
+
+pkv_status pkv_paged_decode_attention(const pkv_cache_desc* desc, void* out, int32_t out_dtype,
+                                      const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t B, int32_t n_q,
+                                      int32_t max_context_len, float scale,
+                                      const float* k_scale, const float* v_scale,
+                                      int32_t partition_size, void* workspace,
+                                      size_t workspace_bytes_, void* stream) {
+  pkv::DecodeArgs a;
+  pkv_status st = prepare_decode(desc, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                                 context_lens, B, n_q, max_context_len, scale, k_scale, v_scale,
+                                 partition_size, &a);
+  if (st != PKV_OK) return st;
+  if (out_dtype != PKV_FP32 && out_dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  if (!out) return PKV_ERR_INVALID_ARG;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  if (a.P_max == 1) {
+    a.write_partials = false;
+    return from_hip(pkv::launch_decode_partition(a, as_stream(stream)));
+  }
+  const size_t need = workspace_bytes(B, n_q, a.d, a.P_max);
+  if (!workspace || workspace_bytes_ < need) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(workspace)) return PKV_ERR_INVALID_ARG;
+  const Workspace w = carve(workspace, B, n_q, a.P_max);
+  a.ws_m = w.m;
+  a.ws_l = w.l;
+  a.ws_o = w.o;
+  a.write_partials = true;
+  hipError_t e = pkv::launch_decode_partition(a, as_stream(stream));
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  return from_hip(pkv::launch_splitk_reduce(out, out_dtype, w.m, w.l, w.o, context_lens, B, n_q,
+                                            a.d, a.P_max, a.partition, as_stream(stream)));
+}
+
+pkv_status pkv_paged_decode_partials(const pkv_cache_desc* desc, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t B, int32_t n_q,
+                                     int32_t max_context_len, float scale,
+                                     const float* k_scale, const float* v_scale,
+                                     int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes_, void* stream) {
+  pkv::DecodeArgs a;
+  pkv_status st = prepare_decode(desc, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                                 context_lens, B, n_q, max_context_len, scale, k_scale, v_scale,
+                                 partition_size, &a);
+  if (st != PKV_OK) return st;
+  if (B == 0) return PKV_OK;
+  const size_t need = workspace_bytes(B, n_q, a.d, a.P_max);
+  if (!workspace || workspace_bytes_ < need) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(workspace)) return PKV_ERR_INVALID_ARG;
+  const Workspace w = carve(workspace, B, n_q, a.P_max);
+  a.ws_m = w.m;
+  a.ws_l = w.l;
+  a.ws_o = w.o;
+  a.write_partials = true;
+  return from_hip(pkv::launch_decode_partition(a, as_stream(stream)));
+}
+
+pkv_status pkv_splitk_reduce(void* out, int32_t out_dtype, const float* m, const float* l,
+                             const float* o, const int32_t* context_lens, int32_t B,
+                             int32_t n_q, int32_t d_head, int32_t max_partitions,
+                             int32_t partition_size, void* stream) {
+  if (B < 0 || n_q <= 0 || d_head <= 0 || max_partitions <= 0 || partition_size <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (out_dtype != PKV_FP32 && out_dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
+  if (max_partitions > kMaxReducePartitions) return PKV_ERR_UNSUPPORTED;
+  if (B == 0) return PKV_OK;
+  if (!out || !m || !l || !o || !context_lens) return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_splitk_reduce(out, out_dtype, m, l, o, context_lens, B, n_q,
+                                            d_head, max_partitions, partition_size,
+                                            as_stream(stream)));
+}
+
+pkv_status pkv_copy_blocks(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
+                           const int32_t* pairs, int32_t n_pairs, void* stream) {
+  pkv_status st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (n_pairs < 0) return PKV_ERR_INVALID_ARG;
+  if (n_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !pairs) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_copy_blocks(*desc, k_cache, v_cache, pairs, n_pairs,
+                                          as_stream(stream)));
+}
+
+pkv_status pkv_gather_kv(const pkv_cache_desc* desc, void* k_out, void* v_out,
+                         const void* k_cache, const void* v_cache,
+                         const int32_t* block_table_row, int32_t context_len, void* stream) {
+  pkv_status st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (context_len < 0) return PKV_ERR_INVALID_ARG;
+  if (context_len == 0) return PKV_OK;
+  if (!k_out || !v_out || !k_cache || !v_cache || !block_table_row) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_out) || !aligned16(v_out) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_gather(*desc, k_out, v_out, k_cache, v_cache, block_table_row,
+                                     context_len, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Launchers shared between the kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Largest partition count per sequence the split-K reduce accepts (its LDS
+// holds one weight per partition).
+constexpr int kMaxReducePartitions = 8192;
+
+// Arguments of one decode launch after host-side validation.
+struct DecodeArgs {
+  const uint16_t* q;          // bf16 [B, n_q, d]
+  const uint8_t* k_cache;     // raw bytes [num_blocks, n_kv, bs, d]
+  const uint8_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const float* k_scale;       // FP8 only
+  const float* v_scale;
+  float* ws_m;                // [B, n_q, P_max] (partials mode)
+  float* ws_l;
+  float* ws_o;                // [B, n_q, P_max, d]
+  void* out;                  // final output (single-partition mode)
+  int out_dtype;
+  int B, n_q, n_kv, d, bs, num_blocks, max_blocks;
+  int kv_dtype;
+  int partition;              // tokens per partition (multiple of bs)
+  int P_max;                  // partitions launched per sequence
+  float scale;
+  bool write_partials;        // true: (m, l, o) to workspace; false: out directly
+};
+
+hipError_t launch_decode_partition(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_splitk_reduce(void* out, int out_dtype, const float* m, const float* l,
+                                const float* o, const int32_t* context_lens, int B, int n_q,
+                                int d, int P_max, int partition, hipStream_t stream);
+
+hipError_t launch_slot_mapping(const int32_t* block_tables, int max_blocks,
+                               const int32_t* positions, int B, int bs, int64_t* slots,
+                               hipStream_t stream);
+hipError_t launch_kv_append(const pkv_cache_desc& d, void* k_cache, void* v_cache,
+                            const void* k_new, const void* v_new, const int64_t* slots, int T,
+                            const float* k_scale, const float* v_scale, hipStream_t stream);
+hipError_t launch_copy_blocks(const pkv_cache_desc& d, void* k_cache, void* v_cache,
+                              const int32_t* pairs, int n_pairs, hipStream_t stream);
+hipError_t launch_gather(const pkv_cache_desc& d, void* k_out, void* v_out, const void* k_cache,
+                         const void* v_cache, const int32_t* table, int ctx, hipStream_t stream);
+
+// Whether the decode kernels were built for this (d, bs, G, dtype) combination.
+bool decode_supported(int d, int bs, int G, int kv_dtype);
+
+}  // namespace pkv
