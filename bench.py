@@ -1,0 +1,286 @@
+"""Benchmark: paged single-token decode attention on one MI355X.
+
+Default workload (one line of JSON on stdout): 70B-class GQA decode step,
+64 sequences x 8192 tokens, 64 query / 8 KV heads, d_head 128, block size 16,
+bf16 KV in 80 per-layer pools (160 GiB), randomly permuted blocks. One step is,
+for every layer: kv_append of one new token per sequence (position 8191),
+then paged decode attention over 8192 tokens (partition kernel + split-K
+reduce). Inputs are resident in HBM before timing starts.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--partition P]
+
+value = KV bytes read per step / step time (GB/s, 1e9 B/s). The roofline
+entry is for the dominant kernel (the decode partition kernel): its
+algorithmic bytes per launch over its average duration, measured with HIP
+events recorded on the stream it runs on, against MI355X's 8 TB/s HBM peak.
+cpu_baseline times the float64 oracle on a bounded sample of the same
+workload on this host's cores.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention: KV GB/s and % of HBM peak; decode tokens/s"
+COUNTERS = os.path.join(ROOT, "profiles", "decode_partition_counters.json")
+KERNEL_SOURCES = ["paged_kv_cache_217_amd/csrc/decode_attention.hip",
+                  "paged_kv_cache_217_amd/csrc/pkv_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gqa_70b",
+                    choices=["gqa_70b", "mha_7b", "gqa_70b_fp8", "long_prefix", "tiny"])
+    ap.add_argument("--layers", type=int, default=0, help="override layer count (0: workload's)")
+    ap.add_argument("--partition", type=int, default=0, help="split-K partition (0: library)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget for the oracle CPU baseline (0 disables it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB block copy (for scaling HBM counters) and exit")
+    return ap.parse_args()
+
+
+def copy_calibration(pkv, torch):
+    """pkv_copy_blocks over 16384 pairs of 64 KiB blocks: 1 GiB read + 1 GiB written."""
+    n_kv, bs, d = 8, 16, 128
+    nb = 2 * 16384
+    k = torch.empty((nb, n_kv, bs, d), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    k.fill_(1.0)
+    v.fill_(2.0)
+    pairs = torch.stack([torch.arange(16384), torch.arange(16384) + 16384], 1).to(
+        torch.int32).cuda().contiguous()
+    for _ in range(3):
+        pkv.copy_blocks(k, v, pairs)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": 2 * 16384 * 32768,
+                                           "bytes_written": 2 * 16384 * 32768,
+                                           "launches": 3}}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_217_amd as pkv
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(pkv, torch)
+        return
+
+    w = W.ALL[args.workload]()
+    layers = args.layers or w.layers
+    B, n_q, n_kv, d, bs = w.B, w.n_q, w.n_kv, w.d, w.bs
+    max_ctx = int(w.context_lens.max())
+    fp8 = w.kv_dtype == W.FP8
+    log(f"[bench] workload {w.name}: B={B} n_q={n_q} n_kv={n_kv} d={d} bs={bs} "
+        f"{w.kv_dtype} layers={layers} tokens={w.total_tokens} pool={w.num_blocks} blocks/layer")
+
+    # ---------------------------------------------------------------- resident inputs
+    t_setup = time.perf_counter()
+    caches = []
+    for layer in range(layers):
+        kc, vc, ks, vs = W.make_cache(w, device=dev, seed_offset=1000 * layer,
+                                      poison_unused=False)
+        caches.append((kc, vc, ks, vs))
+        if layer % 10 == 9:
+            log(f"[bench] generated {layer + 1}/{layers} layer pools")
+    q = W.make_query(w, device=dev, layers=layers) if layers > 1 else \
+        W.make_query(w, device=dev)[None]
+    k_new, v_new = W.make_new_tokens(w, T=layers * B, device=dev)
+    k_new = k_new.view(layers, B, n_kv, d)
+    v_new = v_new.view(layers, B, n_kv, d)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    cl = torch.from_numpy(w.context_lens).to(dev)
+    pos = torch.from_numpy((w.context_lens - 1).astype(np.int32)).to(dev)
+    P = args.partition or pkv.default_partition_size(caches[0][0], B, n_q, max_ctx)
+    P_max = max(1, -(-max_ctx // P))
+    ws, _ = pkv.make_workspace(caches[0][0], B, n_q, max_ctx, P)
+    m_, l_, o_ = pkv.partial_views(ws, B, n_q, d, P_max)
+    out = torch.empty((B, n_q, d), dtype=torch.float32, device=dev)
+    slots = torch.empty(B, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s; partition {P} tokens, "
+        f"{P_max} partitions/seq")
+
+    stream = torch.cuda.current_stream()
+    split = P_max > 1
+
+    def step(ev=None):
+        pkv.slot_mapping(bt, pos, bs, out=slots)
+        for layer in range(layers):
+            kc, vc, ks, vs = caches[layer]
+            if ev is not None:
+                ev[layer][0].record(stream)
+            pkv.kv_append(kc, vc, k_new[layer], v_new[layer], slots, ks, vs)
+            if ev is not None:
+                ev[layer][1].record(stream)
+            if split:
+                pkv.paged_decode_partials(q[layer], kc, vc, bt, cl, w.scale, max_ctx, P,
+                                          k_scale=ks, v_scale=vs, workspace=ws)
+                if ev is not None:
+                    ev[layer][2].record(stream)
+                pkv.splitk_reduce(m_, l_, o_, cl, P, out=out)
+            else:
+                pkv.paged_decode_attention(q[layer], kc, vc, bt, cl, w.scale, max_ctx,
+                                           k_scale=ks, v_scale=vs, partition_size=P, out=out,
+                                           workspace=ws)
+                if ev is not None:
+                    ev[layer][2].record(stream)
+            if ev is not None:
+                ev[layer][3].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(layers)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(args.steps):
+        step(events[s])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+    log(f"[bench] {args.steps} timed steps: {ms_step:.3f} ms/step (host wall {wall:.3f}s)")
+
+    t_append, t_part, t_reduce = [], [], []
+    for s in range(args.steps):
+        for layer in range(layers):
+            e = events[s][layer]
+            t_append.append(e[0].elapsed_time(e[1]))
+            t_part.append(e[1].elapsed_time(e[2]))
+            t_reduce.append(e[2].elapsed_time(e[3]))
+    avg = lambda x: sum(x) / len(x)
+    ms_part = avg(t_part)
+
+    # ---------------------------------------------------------------- accounting
+    p = w.p
+    tokens = w.total_tokens
+    kv_bytes_layer = tokens * n_kv * d * p * 2
+    nP = [max(1, -(-int(c) // P)) if c > 0 else 0 for c in w.context_lens]
+    part_bytes = (kv_bytes_layer                                  # K and V
+                  + B * n_q * d * 2                               # q
+                  + sum(-(-int(c) // bs) for c in w.context_lens) * 4   # block-table entries
+                  + (sum(nP) * n_q * (d + 2) * 4 if split else B * n_q * d * 4)  # partials/out
+                  + (2 * n_kv * 4 if fp8 else 0))                 # FP8 scales
+    achieved = part_bytes / (ms_part * 1e-3) / 1e9
+    kv_gbs = kv_bytes_layer * layers / (ms_step * 1e-3) / 1e9
+    tok_s = B / (ms_step * 1e-3)
+
+    traffic = None
+    if os.path.exists(COUNTERS):
+        c = json.load(open(COUNTERS))
+        if c.get("kernel_hash") == kernel_hash() and c.get("workload") == w.name \
+                and c.get("partition") == P:
+            traffic = c.get("traffic_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if not fp8 else "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "context": max_ctx if len(set(
+            w.context_lens.tolist())) == 1 else "varied", "tokens_per_layer": tokens,
+            "n_q": n_q, "n_kv": n_kv, "d_head": d, "block_size": bs, "layers": layers,
+            "kv_dtype": w.kv_dtype, "partition_size": P, "accumulate": "fp32"},
+        "hbm_peak_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
+        "decode_tokens_per_s": round(tok_s, 1),
+        "kernels_ms": {"kv_append": round(avg(t_append), 5),
+                       "decode_partition": round(ms_part, 5),
+                       "splitk_reduce": round(avg(t_reduce), 5)},
+        "roofline": {"bound": "hbm", "kernel": "decode_partition",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": part_bytes,
+                     "traffic": traffic},
+    }
+
+    # ---------------------------------------------------------------- oracle on the CPU
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(w, caches[0], q[0], args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, layer_cache, q0, budget):
+    """The float64 oracle, as it stands, on whole sequences of layer 0 until the budget is spent."""
+    import numpy as np
+    import threadpoolctl
+
+    import workloads as W
+    from oracle import paged as ref
+
+    kc, vc, ks, vs = layer_cache
+    log("[bench] copying layer 0 to the host for the oracle")
+    kb, vb, qb = W.bits(kc), W.bits(vc), W.bits(q0)
+    ksn = None if ks is None else ks.cpu().numpy()
+    vsn = None if vs is None else vs.cpu().numpy()
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] + [1])
+    done_tokens = 0
+    n = 0
+    t0 = time.perf_counter()
+    while n < w.B and time.perf_counter() - t0 < budget:
+        ref.decode_attention(qb[n:n + 1], kb, vb, w.block_tables[n:n + 1],
+                             w.context_lens[n:n + 1], w.scale, w.kv_dtype, ksn, vsn)
+        done_tokens += int(w.context_lens[n])
+        n += 1
+    dt = time.perf_counter() - t0
+    kv = done_tokens * w.n_kv * w.d * w.p * 2
+    log(f"[bench] oracle: {n} sequences in {dt:.1f}s")
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"layer 0, sequences 0..{n - 1} ({done_tokens} tokens, all {w.n_q} query "
+                      f"heads), numpy float64, 1 process, {dt:.1f} s; host has "
+                      f"{os.cpu_count()} logical CPUs"}
+
+
+if __name__ == "__main__":
+    main()

@@ -28,14 +28,15 @@ pkv_status check_desc(const pkv_cache_desc* d) {
   return PKV_OK;
 }
 
-// Heads served by one workgroup of the decode kernel for a group of G.
-int head_tile(int G) { return G <= 8 ? G : 8; }
+// Heads served by one workgroup of the decode kernel for a group of G
+// (the matrix-core kernel's head tile is 16 wide).
+int head_tile(int G) { return G <= 16 ? G : 16; }
 
 int32_t pick_partition(const pkv_cache_desc* d, int32_t B, int32_t n_q, int32_t max_ctx) {
   // Aim for >= 2048 workgroups (8 per CU on 256 CUs) without going below 256
   // tokens per partition (each of 4 waves then still owns several blocks).
   const int G = n_q / d->n_kv;
-  const int64_t units = static_cast<int64_t>(B) * d->n_kv * (G / head_tile(G));
+  const int64_t units = static_cast<int64_t>(B) * d->n_kv * ((G + head_tile(G) - 1) / head_tile(G));
   int64_t P = 256;
   while (P < max_ctx && P < 4096 && units * cdiv(max_ctx, 2 * P) >= 2048) P *= 2;
   while (cdiv(max_ctx, P) > kMaxReducePartitions) P *= 2;

@@ -22,6 +22,7 @@
 //   * masked slots (past the sequence length, possibly NaN) are removed by
 //     selection, never by multiplying with zero.
 #include <float.h>
+#include <stdlib.h>
 
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -326,7 +327,7 @@ bool decode_supported(int d, int bs, int G, int kv_dtype) {
   return G > 0 && G % 8 == 0;
 }
 
-hipError_t launch_decode_partition(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_partition_valu(const DecodeArgs& a, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
   const int GT = head_tile(G);
   const dim3 grid(a.P_max, a.n_kv * (G / GT), a.B);
@@ -339,6 +340,20 @@ hipError_t launch_decode_partition(const DecodeArgs& a, hipStream_t s) {
   if (a.bs == 16) return fp8 ? launch_gt<64, 16, true>(a, GT, grid, s)
                              : launch_gt<64, 16, false>(a, GT, grid, s);
   return fp8 ? launch_gt<64, 32, true>(a, GT, grid, s) : launch_gt<64, 32, false>(a, GT, grid, s);
+}
+
+// The matrix-core kernel serves every supported shape; PKV_DECODE_KERNEL=valu
+// selects the vector-ALU kernel instead (kept for A/B measurement).
+static bool use_valu() {
+  static const bool v = [] {
+    const char* e = getenv("PKV_DECODE_KERNEL");
+    return e && e[0] == 'v';
+  }();
+  return v;
+}
+
+hipError_t launch_decode_partition(const DecodeArgs& a, hipStream_t s) {
+  return use_valu() ? launch_decode_partition_valu(a, s) : launch_decode_partition_mfma(a, s);
 }
 
 hipError_t launch_splitk_reduce(void* out, int out_dtype, const float* m, const float* l,

@@ -1,0 +1,416 @@
+// Paged decode attention, partition kernel on the gfx950 matrix cores.
+//
+// Same computation as the VALU partition kernel (see decode_attention.hip and
+// [MTKV] "Architecting Multi-Tier Disaggregated KV-Cache Hierarchies for
+// Terabyte-Scale LLM Inference", section "High-Throughput Paged Attention
+// Kernel Integration"): per (sequence, KV head, partition), online softmax of
+// scale * q . k over the partition's tokens for all query heads of the group,
+// accumulating the weighted sum of V, with the K/V tiles fetched through the
+// block table.
+//
+// Why MFMA: with G = 8 query heads per KV head every bf16 K/V element feeds
+// 8 fp32 FMAs plus a conversion; on the vector ALU that is ~80% of its issue
+// rate at 70% of HBM bandwidth. v_mfma_f32_16x16x32_bf16 consumes the bf16
+// tiles as loaded (no conversion) and does the contraction of 16 heads in one
+// instruction; heads beyond G are zero columns.
+//
+// Register layout (lane l: column c = l % 16, k-group g4 = l / 16):
+//   scores  S = K . Q^T : A = K tile (m = token c of a 16-token row group,
+//           k = 8 dims 32kk + 8*g4), B = Q^T (n = head c). The result puts
+//           head c's scores for tokens 4*g4 .. 4*g4+3 in lane l.
+//   output  O^T = V^T . P^T : B = P^T (n = head c, k = those same 8 tokens of
+//           the two row groups) -- already in the lane, no data movement;
+//           A = V^T (m = dim DPL*c + j, k = the 8 tokens), built by loading
+//           8 token rows of DPL dims (whole rows per load instruction across
+//           16 lanes) and transposing 16-bit pairs with v_perm_b32.
+//   Every lane therefore owns one head's softmax state (its 4 k-group lanes
+//   share a max through two cross-lane exchanges) and that head's output
+//   accumulator for D/4 dims.
+// P is fed to the matrix core as bf16 hi + lo parts (two MFMAs), which keeps
+// the weights to ~16 significant bits; the row sums use the fp32 weights.
+// The running max is refreshed lazily: only when a chunk's max exceeds the
+// reference by more than 2^8 are the accumulators rescaled (weights stay
+// <= 256, far inside bf16 and fp32 range); the true max is tracked and the
+// partition's statistics are rebased on it at the end.
+#include <float.h>
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyRescale = 8.0f;     // log2 of the largest weight allowed before rescaling
+
+template <int BYTES>
+struct Vec;
+template <>
+struct Vec<16> {
+  using T = uint4;
+};
+template <>
+struct Vec<8> {
+  using T = uint2;
+};
+template <>
+struct Vec<4> {
+  using T = uint32_t;
+};
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ uint32_t word(const uint2& v, int i) { return i == 0 ? v.x : v.y; }
+__device__ __forceinline__ uint32_t word(const uint32_t& v, int) { return v; }
+
+// 2 FP8 E4M3FN codes (bytes 0,1 or 2,3 of w) -> 2 bf16 in one word, exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  auto r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  uint4 u = make_uint4(a, b, c, d);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+}  // namespace
+
+template <int D, int BS, bool FP8, int NW, bool SPLIT_P>
+__global__ __launch_bounds__(NW * 64) void decode_partition_mfma(DecodeArgs a) {
+  constexpr int NKK = D / 32;                 // QK MFMAs per 16-token row group
+  constexpr int NJ = D / 16;                  // PV MFMAs (16 output dims each)
+  constexpr int DPL = D / 16;                 // dims per lane per V row
+  constexpr int BPC = 32 / BS;                // blocks per 32-token chunk
+  constexpr int EB = FP8 ? 1 : 2;             // bytes per element
+  constexpr int KB = 8 * EB;                  // bytes per K load (8 dims)
+  constexpr int VB = DPL * EB;                // bytes per V load (DPL dims)
+  using KT = typename Vec<KB>::T;
+  using VT = typename Vec<VB>::T;
+  constexpr int VW = (DPL * 2) / 4;           // bf16 words per V row slice (after conversion)
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15;
+  const int g4 = lane >> 4;
+
+  const int G = a.n_q / a.n_kv;
+  const int tiles = (G + 15) / 16;
+  const int j = blockIdx.x;
+  const int g = blockIdx.y / tiles;
+  const int tile = blockIdx.y % tiles;
+  const int h0 = g * G + tile * 16;
+  const int nh = min(16, G - tile * 16);
+  const int b = blockIdx.z;
+  const int ctx = min(a.context_lens[b], a.max_blocks * BS);
+  const int t0 = j * a.partition;
+
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+  __shared__ float sm_acc[NW][16][D + 4];
+
+  if (t0 >= ctx) {
+    if (!a.write_partials && j == 0) {
+      for (int i = threadIdx.x; i < nh * D; i += blockDim.x) {
+        const int64_t o = (static_cast<int64_t>(b) * a.n_q + h0 + i / D) * D + i % D;
+        if (a.out_dtype == PKV_FP32)
+          static_cast<float*>(a.out)[o] = 0.0f;
+        else
+          static_cast<uint16_t*>(a.out)[o] = 0;
+      }
+    }
+    return;
+  }
+  const int t1 = min(t0 + a.partition, ctx);
+  const int blk0 = t0 / BS;
+  const int blk1 = (t1 + BS - 1) / BS;
+  const int n_ch = (blk1 - blk0 + BPC - 1) / BPC;
+
+  // Q^T operand: lane (c, g4) holds q[h0 + c][32kk + 8*g4 .. +8] for each kk
+  bf16x8_t qop[NKK];
+  {
+    const bool live = c < nh;
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * a.n_q + h0 + (live ? c : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      uint4 w = *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * g4);
+      if (!live) w = make_uint4(0, 0, 0, 0);
+      qop[kk] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+  float qscale = a.scale * kLog2e;
+  if constexpr (FP8) qscale *= a.k_scale[g];
+
+  const int64_t tile_bytes = static_cast<int64_t>(BS) * D * EB;
+  const int64_t head_off = static_cast<int64_t>(g) * tile_bytes;
+  const int64_t block_stride = static_cast<int64_t>(a.n_kv) * tile_bytes;
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
+
+  // per-lane byte offsets inside a chunk's tiles
+  // K: row group rg, step kk -> token rg*16 + c, dims 32kk + 8*g4
+  // V: slot s -> token (s < 4 ? 4*g4 + s : 16 + 4*g4 + s - 4), dims DPL*c
+  auto k_off = [&](int rg, int kk) -> int {
+    const int tok = rg * 16 + c;                          // token within the chunk
+    return ((tok % BS) * D + 32 * kk + 8 * g4) * EB;
+  };
+  auto v_off = [&](int s) -> int {
+    const int tok = (s < 4 ? 4 * g4 + s : 16 + 4 * g4 + s - 4);
+    return ((tok % BS) * D + DPL * c) * EB;
+  };
+
+  struct Chunk {
+    KT k[2][NKK];
+    VT v[8];
+  };
+
+  auto load = [&](Chunk& ch, int ci) {
+    const int bA = blk0 + ci * BPC;
+    int pA = bt[bA];
+    if (pA < 0 || pA >= a.num_blocks) pA = 0;
+    const uint8_t* kA = a.k_cache + pA * block_stride + head_off;
+    const uint8_t* vA = a.v_cache + pA * block_stride + head_off;
+    const uint8_t* kB = kA;
+    const uint8_t* vB = vA;
+    bool haveB = true;
+    if constexpr (BPC == 2) {
+      haveB = bA + 1 < blk1;
+      int pB = haveB ? bt[bA + 1] : 0;
+      if (pB < 0 || pB >= a.num_blocks) pB = 0;
+      kB = a.k_cache + pB * block_stride + head_off;
+      vB = a.v_cache + pB * block_stride + head_off;
+    }
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const uint8_t* base = (BPC == 2 && rg == 1) ? kB : kA;
+        if (BPC == 2 && rg == 1 && !haveB)
+          ch.k[rg][kk] = KT{};
+        else
+          ch.k[rg][kk] = *reinterpret_cast<const KT*>(base + k_off(rg, kk));
+      }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint8_t* base = (BPC == 2 && s >= 4) ? vB : vA;
+      if (BPC == 2 && s >= 4 && !haveB)
+        ch.v[s] = VT{};
+      else
+        ch.v[s] = *reinterpret_cast<const VT*>(base + v_off(s));
+    }
+  };
+
+  float m_ref = -INFINITY;      // reference max of this lane's head (base-2 units)
+  float m_true = -INFINITY;
+  float l = 0.0f;               // this lane's share of the row sum
+  f32x4_t acc[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) acc[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](Chunk& ch, int ci) {
+    const int tok0 = (blk0 + ci * BPC) * BS;             // first token of the chunk
+    // ---- scores
+    f32x4_t sc[2];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      sc[rg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        bf16x8_t kop;
+        if constexpr (!FP8) {
+          kop = __builtin_bit_cast(bf16x8_t, ch.k[rg][kk]);
+        } else {
+          const uint2 w = ch.k[rg][kk];
+          kop = as_bf16x8(fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x),
+                          fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y));
+        }
+        sc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sc[rg], 0, 0, 0);
+      }
+    }
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] = sc[0][i] * qscale;
+      s[4 + i] = sc[1][i] * qscale;
+    }
+    const bool tail = tok0 + 32 > t1;
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int tok = tok0 + (i < 4 ? 4 * g4 + i : 16 + 4 * g4 + i - 4);
+        s[i] = tok < t1 ? s[i] : -INFINITY;
+      }
+#pragma unroll
+      for (int si = 0; si < 8; ++si) {
+        const int tok = tok0 + (si < 4 ? 4 * g4 + si : 16 + 4 * g4 + si - 4);
+        if (tok >= t1) ch.v[si] = VT{};
+      }
+    }
+    // ---- online softmax for head c (shared by the 4 k-group lanes)
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    m_true = fmaxf(m_true, mx);
+    const bool need = mx > m_ref + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_new = need ? mx : m_ref;
+      const float alpha = fast_exp2(m_ref - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) acc[jj] *= alpha;
+      m_ref = m_new;
+    }
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = fast_exp2(s[i] - m_ref);
+      l += p[i];
+    }
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      ph[t] = pack_bf16(p[2 * t], p[2 * t + 1]);
+      if constexpr (SPLIT_P) {
+        float h0f, h1f;
+        bf16x2_to_f32(ph[t], h0f, h1f);
+        pl[t] = pack_bf16(p[2 * t] - h0f, p[2 * t + 1] - h1f);
+      }
+    }
+    const bf16x8_t pop_hi = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
+    bf16x8_t pop_lo;
+    if constexpr (SPLIT_P) pop_lo = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
+
+    // ---- V^T operand: vb[s][w] = bf16 pair (dims DPL*c + 2w, +1) of token slot s
+    uint32_t vb[8][VW];
+#pragma unroll
+    for (int si = 0; si < 8; ++si) {
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int w = 0; w < VW; ++w) vb[si][w] = word(ch.v[si], w);
+      } else {
+#pragma unroll
+        for (int w = 0; w < VW / 2; ++w) {
+          const uint32_t x = word(ch.v[si], w);
+          vb[si][2 * w] = fp8x2_to_bf16x2<false>(x);
+          vb[si][2 * w + 1] = fp8x2_to_bf16x2<true>(x);
+        }
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int w = jj >> 1;
+      const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t t4[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        t4[t] = __builtin_amdgcn_perm(vb[2 * t + 1][w], vb[2 * t][w], sel);
+      const bf16x8_t vop = as_bf16x8(t4[0], t4[1], t4[2], t4[3]);
+      acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi, acc[jj], 0, 0, 0);
+      if constexpr (SPLIT_P)
+        acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo, acc[jj], 0, 0, 0);
+    }
+  };
+
+  // ---- main loop: this wave's chunks wave, wave + NW, ...; next chunk's loads in flight
+  {
+    Chunk A, B;
+    int ci = wave;
+    if (ci < n_ch) load(A, ci);
+    for (; ci < n_ch; ci += 2 * NW) {
+      if (ci + NW < n_ch) load(B, ci + NW);
+      compute(A, ci);
+      if (ci + NW >= n_ch) break;
+      if (ci + 2 * NW < n_ch) load(A, ci + 2 * NW);
+      compute(B, ci + NW);
+    }
+  }
+
+  // ---- wave totals for head c, rebased on the true max
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  const float f = m_true == -INFINITY ? 0.0f : fast_exp2(m_ref - m_true);
+  l *= f;
+  if (g4 == 0) {
+    sm_m[wave][c] = m_true;
+    sm_l[wave][c] = l;
+  }
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm_acc[wave][c][DPL * (4 * g4 + i) + jj] = acc[jj][i] * f;
+  __syncthreads();
+
+  // ---- merge the waves; write (m, l, o) or the final output
+  const float vscale = FP8 ? a.v_scale[g] : 1.0f;
+  for (int i = threadIdx.x; i < nh * D; i += blockDim.x) {
+    const int h = i / D;
+    const int e = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float fw = sm_m[w][h] == -INFINITY ? 0.0f : fast_exp2(sm_m[w][h] - M);
+      L = fmaf(sm_l[w][h], fw, L);
+      O = fmaf(sm_acc[w][h][e], fw, O);
+    }
+    const float o = O / L * vscale;
+    const int hq = h0 + h;
+    if (a.write_partials) {
+      const int64_t mi = (static_cast<int64_t>(b) * a.n_q + hq) * a.P_max + j;
+      if (e == 0) {
+        a.ws_m[mi] = M;
+        a.ws_l[mi] = L;
+      }
+      a.ws_o[mi * D + e] = o;
+    } else {
+      const int64_t oi = (static_cast<int64_t>(b) * a.n_q + hq) * D + e;
+      if (a.out_dtype == PKV_FP32)
+        static_cast<float*>(a.out)[oi] = o;
+      else
+        static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_rne(o);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dispatch
+
+constexpr int kMfmaWaves = 4;
+
+template <int D, int BS, bool FP8>
+static hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  decode_partition_mfma<D, BS, FP8, kMfmaWaves, true><<<grid, kMfmaWaves * 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_partition_mfma(const DecodeArgs& a, hipStream_t s) {
+  const int G = a.n_q / a.n_kv;
+  const dim3 grid(a.P_max, a.n_kv * ((G + 15) / 16), a.B);
+  const bool fp8 = a.kv_dtype == PKV_FP8_E4M3;
+  if (a.d == 128) {
+    if (a.bs == 16) return fp8 ? launch_mfma<128, 16, true>(a, grid, s)
+                               : launch_mfma<128, 16, false>(a, grid, s);
+    return fp8 ? launch_mfma<128, 32, true>(a, grid, s) : launch_mfma<128, 32, false>(a, grid, s);
+  }
+  if (a.bs == 16) return fp8 ? launch_mfma<64, 16, true>(a, grid, s)
+                             : launch_mfma<64, 16, false>(a, grid, s);
+  return fp8 ? launch_mfma<64, 32, true>(a, grid, s) : launch_mfma<64, 32, false>(a, grid, s);
+}
+
+}  // namespace pkv

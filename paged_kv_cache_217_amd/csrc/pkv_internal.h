@@ -34,7 +34,10 @@ struct DecodeArgs {
   bool write_partials;        // true: (m, l, o) to workspace; false: out directly
 };
 
+// Partition kernels: matrix-core (default) and vector-ALU variants.
 hipError_t launch_decode_partition(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_partition_mfma(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_partition_valu(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_splitk_reduce(void* out, int out_dtype, const float* m, const float* l,
                                 const float* o, const int32_t* context_lens, int B, int n_q,
                                 int d, int P_max, int partition, hipStream_t stream);
