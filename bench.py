@@ -31,8 +31,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode attention: KV GB/s and % of HBM peak; decode tokens/s"
 COUNTERS = os.path.join(ROOT, "profiles", "decode_partition_counters.json")
-KERNEL_SOURCES = ["paged_kv_cache_217_amd/csrc/decode_attention.hip",
-                  "paged_kv_cache_217_amd/csrc/pkv_device.h"]
+KERNEL_SOURCES = ["paged_kv_cache_217_amd/csrc/decode_mfma.hip",
+                  "paged_kv_cache_217_amd/csrc/pkv_device.h",
+                  "paged_kv_cache_217_amd/csrc/pkv_internal.h"]
 
 
 def log(*a):
@@ -168,21 +169,29 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] warmup step {i + 1}/{args.warmup} done")
 
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(layers)]
-              for _ in range(args.steps)]
+    # timed region 1: exactly K steps, nothing but the work between the events
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for s in range(args.steps):
-        step(events[s])
+        step()
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(stop) / args.steps
     log(f"[bench] {args.steps} timed steps: {ms_step:.3f} ms/step (host wall {wall:.3f}s)")
 
+    # timed region 2: the same K steps with HIP events on the launch stream around
+    # every kernel (an event pair costs a few microseconds, so region 1 gives the
+    # step time and this one the per-kernel durations)
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(layers)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
     t_append, t_part, t_reduce = [], [], []
     for s in range(args.steps):
         for layer in range(layers):
@@ -235,7 +244,7 @@ def main():
         "decode_tokens_per_s": round(tok_s, 1),
         "kernels_ms": {"kv_append": round(avg(t_append), 5),
                        "decode_partition": round(ms_part, 5),
-                       "splitk_reduce": round(avg(t_reduce), 5)},
+                       "splitk_reduce": round(avg(t_reduce), 5) if split else None},
         "roofline": {"bound": "hbm", "kernel": "decode_partition",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -33,12 +33,17 @@ pkv_status check_desc(const pkv_cache_desc* d) {
 int head_tile(int G) { return G <= 16 ? G : 16; }
 
 int32_t pick_partition(const pkv_cache_desc* d, int32_t B, int32_t n_q, int32_t max_ctx) {
-  // Aim for >= 2048 workgroups (8 per CU on 256 CUs) without going below 256
-  // tokens per partition (each of 4 waves then still owns several blocks).
+  // The partition kernel holds two 4-wave workgroups per CU (its register
+  // budget allows two waves per SIMD), so 512 workgroups fill the 256 CUs
+  // once. Take the largest power-of-two partition (256 .. 8192 tokens) that
+  // still yields at least one full round; a batch whose longest sequence fits
+  // in one partition runs in a single pass with no reduce.
+  constexpr int64_t kOneRound = 256 * 2;
   const int G = n_q / d->n_kv;
-  const int64_t units = static_cast<int64_t>(B) * d->n_kv * ((G + head_tile(G) - 1) / head_tile(G));
-  int64_t P = 256;
-  while (P < max_ctx && P < 4096 && units * cdiv(max_ctx, 2 * P) >= 2048) P *= 2;
+  const int64_t units =
+      static_cast<int64_t>(B) * d->n_kv * ((G + head_tile(G) - 1) / head_tile(G));
+  int64_t P = 8192;
+  while (P > 256 && units * cdiv(max_ctx, P) < kOneRound) P /= 2;
   while (cdiv(max_ctx, P) > kMaxReducePartitions) P *= 2;
   return static_cast<int32_t>(P);
 }
