@@ -127,7 +127,8 @@ def main():
     bt = torch.from_numpy(w.block_tables).to(dev)
     cl = torch.from_numpy(w.context_lens).to(dev)
     pos = torch.from_numpy((w.context_lens - 1).astype(np.int32)).to(dev)
-    P = args.partition or pkv.default_partition_size(caches[0][0], B, n_q, max_ctx)
+    P = args.partition or w.partition_size or \
+        pkv.default_partition_size(caches[0][0], B, n_q, max_ctx)
     P_max = max(1, -(-max_ctx // P))
     ws, _ = pkv.make_workspace(caches[0][0], B, n_q, max_ctx, P)
     m_, l_, o_ = pkv.partial_views(ws, B, n_q, d, P_max)

@@ -62,6 +62,22 @@ struct Vec<4> {
   using T = uint32_t;
 };
 
+// Streaming (non-temporal) loads of KV bytes: every K/V byte is read once
+// per step, so the loads ask the caches not to keep the lines.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void ld_stream(uint4& out, const uint8_t* p) {
+  const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  out = make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void ld_stream(uint2& out, const uint8_t* p) {
+  const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  out = make_uint2(x[0], x[1]);
+}
+__device__ __forceinline__ void ld_stream(uint32_t& out, const uint8_t* p) {
+  out = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
@@ -201,7 +217,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_mfma(DecodeArgs a) {
         if (BPC == 2 && rg == 1 && !haveB)
           ch.k[rg][kk] = KT{};
         else
-          ch.k[rg][kk] = *reinterpret_cast<const KT*>(base + k_off(rg, kk));
+          ld_stream(ch.k[rg][kk], base + k_off(rg, kk));
       }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -209,7 +225,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_mfma(DecodeArgs a) {
       if (BPC == 2 && s >= 4 && !haveB)
         ch.v[s] = VT{};
       else
-        ch.v[s] = *reinterpret_cast<const VT*>(base + v_off(s));
+        ld_stream(ch.v[s], base + v_off(s));
     }
   };
 

@@ -47,7 +47,7 @@ class Workload:
     num_blocks: int
     scale: float
     layers: int = 1
-    partition_size: int = 512
+    partition_size: int = 0           # 0: the library's default; else fixed by the workload
     shared_prefix_blocks: int = 0
     notes: dict = field(default_factory=dict)
 
@@ -107,7 +107,7 @@ def make_structure(context_lens, bs, seed, pool_factor=1.2, extra_blocks=0,
 
 
 def custom(name, context_lens, n_q, n_kv, d, bs, kv_dtype=BF16, seed=0,
-           pool_factor=1.2, extra_blocks=0, scale=None, partition_size=512):
+           pool_factor=1.2, extra_blocks=0, scale=None, partition_size=0):
     ctx, bt, pool = make_structure(context_lens, bs, STRUCT_SEED + seed,
                                    pool_factor, extra_blocks)
     return Workload(name, len(ctx), n_q, n_kv, d, bs, kv_dtype, ctx, bt, pool,
@@ -123,7 +123,7 @@ def tiny():
     perm = torch.randperm(32, generator=_gen(STRUCT_SEED + 1)).numpy().astype(np.int32)
     bt = _tables_from_perm(ctx, 16, perm)
     return Workload("tiny_paged_decode", 2, 4, 2, 64, 16, BF16, ctx, bt, 32, 1.0 / 8.0,
-                    partition_size=512, notes={"seed": 1})
+                    notes={"seed": 1})
 
 
 def mha_7b():
@@ -135,7 +135,7 @@ def mha_7b():
     perm = torch.randperm(pool, generator=g).numpy().astype(np.int32)
     bt = _tables_from_perm(ctx, 16, perm)
     return Workload("mha_7b_single_layer", 32, 32, 32, 128, 16, BF16, ctx, bt, pool,
-                    1.0 / math.sqrt(128), partition_size=512, notes={"seed": 2})
+                    1.0 / math.sqrt(128), notes={"seed": 2})
 
 
 def gqa_70b(layers=80):
@@ -145,8 +145,7 @@ def gqa_70b(layers=80):
     perm = torch.randperm(pool, generator=_gen(STRUCT_SEED + 3)).numpy().astype(np.int32)
     bt = _tables_from_perm(ctx, 16, perm)
     return Workload("gqa_70b_80_layers", 64, 64, 8, 128, 16, BF16, ctx, bt, pool,
-                    1.0 / math.sqrt(128), layers=layers, partition_size=1024,
-                    notes={"seed": 3})
+                    1.0 / math.sqrt(128), layers=layers, notes={"seed": 3})
 
 
 def lognormal_lengths(n, median, sigma, cap, g):
@@ -164,8 +163,7 @@ def gqa_70b_fp8():
     perm = torch.randperm(pool, generator=g).numpy().astype(np.int32)
     bt = _tables_from_perm(ctx, 32, perm)
     return Workload("gqa_70b_fp8_single_layer", 256, 64, 8, 128, 32, FP8, ctx, bt, pool,
-                    1.0 / math.sqrt(128), partition_size=512,
-                    notes={"seed": 4, "lognormal_sigma": 1.0})
+                    1.0 / math.sqrt(128), notes={"seed": 4, "lognormal_sigma": 1.0})
 
 
 def long_shared_prefix():
