@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 
 #include "pkv.h"
 #include "pkv_internal.h"
@@ -35,17 +36,33 @@ int head_tile(int G) { return G <= 16 ? G : 16; }
 int32_t pick_partition(const pkv_cache_desc* d, int32_t B, int32_t n_q, int32_t max_ctx) {
   // The partition kernel holds two 4-wave workgroups per CU (its register
   // budget allows two waves per SIMD), so 512 workgroups fill the 256 CUs
-  // once. Take the largest power-of-two partition (256 .. 8192 tokens) that
-  // still yields at least one full round; a batch whose longest sequence fits
-  // in one partition runs in a single pass with no reduce.
+  // once. A batch whose (sequence, KV head) pairs alone fill that round and
+  // whose longest sequence is at most 8192 tokens runs in a single pass with
+  // no reduce. Otherwise partitions are at most 4096 tokens (a workgroup then
+  // streams <= 2 MiB of bf16 K+V, which bounds the tail of a launch over
+  // sequences of very different lengths) and shrink by halves while the grid
+  // would not fill one round.
   constexpr int64_t kOneRound = 256 * 2;
   const int G = n_q / d->n_kv;
   const int64_t units =
       static_cast<int64_t>(B) * d->n_kv * ((G + head_tile(G) - 1) / head_tile(G));
-  int64_t P = 8192;
+  if (max_ctx <= 8192 && units >= kOneRound) return 8192;
+  int64_t P = 4096;
   while (P > 256 && units * cdiv(max_ctx, P) < kOneRound) P /= 2;
   while (cdiv(max_ctx, P) > kMaxReducePartitions) P *= 2;
   return static_cast<int32_t>(P);
+}
+
+// Partials mode runs one wave per partition when partitions are short (each
+// wave then keeps a long load pipeline instead of a few chunks);
+// PKV_WAVE_PARTITIONS=0/1 overrides the choice (for measurement).
+bool use_wave_partitions(int32_t partition) {
+  static const int forced = [] {
+    const char* e = getenv("PKV_WAVE_PARTITIONS");
+    return e ? (e[0] == '1' ? 1 : 0) : -1;
+  }();
+  if (forced >= 0) return forced == 1;
+  return partition <= 1024;
 }
 
 struct Workspace {
@@ -209,6 +226,7 @@ pkv_status pkv_paged_decode_attention(const pkv_cache_desc* desc, void* out, int
   a.ws_l = w.l;
   a.ws_o = w.o;
   a.write_partials = true;
+  a.wave_partitions = use_wave_partitions(a.partition);
   hipError_t e = pkv::launch_decode_partition(a, as_stream(stream));
   if (e != hipSuccess) return PKV_ERR_HIP;
   return from_hip(pkv::launch_splitk_reduce(out, out_dtype, w.m, w.l, w.o, context_lens, B, n_q,
@@ -237,6 +255,7 @@ pkv_status pkv_paged_decode_partials(const pkv_cache_desc* desc, const void* q,
   a.ws_l = w.l;
   a.ws_o = w.o;
   a.write_partials = true;
+  a.wave_partitions = use_wave_partitions(a.partition);
   return from_hip(pkv::launch_decode_partition(a, as_stream(stream)));
 }
 

@@ -251,55 +251,143 @@ __global__ __launch_bounds__(256) void decode_partition_valu(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K reduce: one workgroup per (sequence, query head), one thread per
-// output element. Weights w_j = l_j 2^(m_j - M) are computed once into LDS.
+// Split-K reduce, two shapes chosen by the partition count:
+//   <= 32 partitions: one wave per (sequence, query head) (below);
+//   more: one 256-thread workgroup per (sequence, query head). Thread t owns
+//   output dims 4*(t % (D/4)) .. +4 for the partitions j = t / (D/4)
+//   (mod 256 / (D/4)), reading 16 bytes per partition row, so a long list of
+//   partitions is read many rows at a time; the weights
+//   w_j = l_j 2^(m_j - M) are computed once into LDS.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void splitk_reduce_kernel(
+constexpr int kWaveReduceMaxPartitions = 32;
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Few partitions per sequence: one wave per (sequence, query head), lanes own
+// output dims, weights broadcast by cross-lane reads (no LDS, no barrier).
+template <int D>
+__global__ __launch_bounds__(256) void splitk_reduce_wave_kernel(
     void* __restrict__ out, int out_dtype, const float* __restrict__ m,
     const float* __restrict__ l, const float* __restrict__ o,
-    const int32_t* __restrict__ context_lens, int n_q, int d, int P_max, int partition) {
-  __shared__ float w[kMaxReducePartitions];
-  __shared__ float red[128];
-  const int bh = blockIdx.x;
+    const int32_t* __restrict__ context_lens, int B, int n_q, int P_max, int partition) {
+  constexpr int DL = D / 64;                         // output dims per lane
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= B * n_q) return;                         // whole wave
   const int b = bh / n_q;
   const int ctx = context_lens[b];
-  const int np = min((ctx + partition - 1) / partition, P_max);
+  const int np = ctx > 0 ? min((ctx + partition - 1) / partition, P_max) : 0;
   const float* mb = m + static_cast<int64_t>(bh) * P_max;
   const float* lb = l + static_cast<int64_t>(bh) * P_max;
-  const float* ob = o + static_cast<int64_t>(bh) * P_max * d;
+  const float* ob = o + static_cast<int64_t>(bh) * P_max * D;
 
   float mx = -INFINITY;
-  for (int jj = threadIdx.x; jj < np; jj += blockDim.x) mx = fmaxf(mx, mb[jj]);
-  red[threadIdx.x] = mx;
-  __syncthreads();
-  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
+  for (int jj = lane; jj < np; jj += 64) mx = fmaxf(mx, mb[jj]);
+  const float M = wave_max(mx);
+  float acc[DL];
+#pragma unroll
+  for (int k = 0; k < DL; ++k) acc[k] = 0.0f;
   float lsum = 0.0f;
-  for (int jj = threadIdx.x; jj < np; jj += blockDim.x) {
-    const float wj = lb[jj] * fast_exp2(mb[jj] - M);
-    w[jj] = wj;
-    lsum += wj;
+  for (int j0 = 0; j0 < np; j0 += 64) {
+    const int jl = j0 + lane;
+    const float wl = jl < np ? lb[jl] * fast_exp2(mb[jl] - M) : 0.0f;
+    lsum += wl;
+    const int n = min(64, np - j0);
+    for (int jj = 0; jj < n; ++jj) {
+      const float wj = __shfl(wl, jj);
+      const float* row = ob + static_cast<int64_t>(j0 + jj) * D;
+#pragma unroll
+      for (int k = 0; k < DL; ++k) acc[k] = fmaf(wj, row[lane + 64 * k], acc[k]);
+    }
   }
-  red[threadIdx.x] = lsum;
-  __syncthreads();
-  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  const float L = red[0];
-  for (int e = threadIdx.x; e < d; e += blockDim.x) {
-    float acc = 0.0f;
-    for (int jj = 0; jj < np; ++jj) acc = fmaf(w[jj], ob[static_cast<int64_t>(jj) * d + e], acc);
-    const float v = np > 0 ? acc / L : 0.0f;
-    const int64_t oi = static_cast<int64_t>(bh) * d + e;
+  const float L = wave_sum(lsum);
+#pragma unroll
+  for (int k = 0; k < DL; ++k) {
+    const float v = np > 0 ? acc[k] / L : 0.0f;
+    const int64_t oi = static_cast<int64_t>(bh) * D + lane + 64 * k;
     if (out_dtype == PKV_FP32)
       static_cast<float*>(out)[oi] = v;
     else
       static_cast<uint16_t*>(out)[oi] = f32_to_bf16_rne(v);
+  }
+}
+
+// Many partitions per sequence: one 256-thread workgroup per (sequence, head).
+template <int D>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(
+    void* __restrict__ out, int out_dtype, const float* __restrict__ m,
+    const float* __restrict__ l, const float* __restrict__ o,
+    const int32_t* __restrict__ context_lens, int n_q, int P_max, int partition) {
+  constexpr int DG = D / 4;                           // 16-byte dim groups
+  constexpr int PG = 256 / DG;                        // partition groups
+  __shared__ float w[kMaxReducePartitions];
+  __shared__ float red[4];
+  __shared__ float4 part[PG][DG];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wv = t >> 6;
+  const int bh = blockIdx.x;
+  const int b = bh / n_q;
+  const int ctx = context_lens[b];
+  const int np = ctx > 0 ? min((ctx + partition - 1) / partition, P_max) : 0;
+  const float* mb = m + static_cast<int64_t>(bh) * P_max;
+  const float* lb = l + static_cast<int64_t>(bh) * P_max;
+  const float* ob = o + static_cast<int64_t>(bh) * P_max * D;
+
+  float mx = -INFINITY;
+  for (int jj = t; jj < np; jj += 256) mx = fmaxf(mx, mb[jj]);
+  mx = wave_max(mx);
+  if (lane == 0) red[wv] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float ls = 0.0f;
+  for (int jj = t; jj < np; jj += 256) {
+    const float wj = lb[jj] * fast_exp2(mb[jj] - M);
+    w[jj] = wj;
+    ls += wj;
+  }
+  ls = wave_sum(ls);
+  if (lane == 0) red[wv] = ls;
+  __syncthreads();
+  const float L = red[0] + red[1] + red[2] + red[3];
+
+  const int dg = t % DG;
+  const int pg = t / DG;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int jj = pg; jj < np; jj += PG) {
+    const float wj = w[jj];
+    const float4 v = *reinterpret_cast<const float4*>(ob + static_cast<int64_t>(jj) * D + 4 * dg);
+    acc.x = fmaf(wj, v.x, acc.x);
+    acc.y = fmaf(wj, v.y, acc.y);
+    acc.z = fmaf(wj, v.z, acc.z);
+    acc.w = fmaf(wj, v.w, acc.w);
+  }
+  part[pg][dg] = acc;
+  __syncthreads();
+  if (t < D) {
+    float s = 0.0f;
+    const int g4 = t / 4;
+    const int k = t % 4;
+#pragma unroll
+    for (int q = 0; q < PG; ++q) {
+      const float4 v = part[q][g4];
+      s += k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+    }
+    const float r = np > 0 ? s / L : 0.0f;
+    const int64_t oi = static_cast<int64_t>(bh) * D + t;
+    if (out_dtype == PKV_FP32)
+      static_cast<float*>(out)[oi] = r;
+    else
+      static_cast<uint16_t*>(out)[oi] = f32_to_bf16_rne(r);
   }
 }
 
@@ -359,9 +447,27 @@ hipError_t launch_decode_partition(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_splitk_reduce(void* out, int out_dtype, const float* m, const float* l,
                                 const float* o, const int32_t* context_lens, int B, int n_q,
                                 int d, int P_max, int partition, hipStream_t stream) {
-  if (P_max > kMaxReducePartitions) return hipErrorInvalidValue;
-  splitk_reduce_kernel<<<B * n_q, 128, 0, stream>>>(out, out_dtype, m, l, o, context_lens, n_q,
-                                                    d, P_max, partition);
+  if (P_max > kMaxReducePartitions || (d != 64 && d != 128)) return hipErrorInvalidValue;
+  const int64_t pairs = static_cast<int64_t>(B) * n_q;
+  if (P_max <= kWaveReduceMaxPartitions) {
+    const unsigned grid = static_cast<unsigned>((pairs + 3) / 4);
+    if (d == 128)
+      splitk_reduce_wave_kernel<128><<<grid, 256, 0, stream>>>(out, out_dtype, m, l, o,
+                                                               context_lens, B, n_q, P_max,
+                                                               partition);
+    else
+      splitk_reduce_wave_kernel<64><<<grid, 256, 0, stream>>>(out, out_dtype, m, l, o,
+                                                              context_lens, B, n_q, P_max,
+                                                              partition);
+    return hipGetLastError();
+  }
+  const unsigned grid = static_cast<unsigned>(pairs);
+  if (d == 128)
+    splitk_reduce_kernel<128><<<grid, 256, 0, stream>>>(out, out_dtype, m, l, o, context_lens,
+                                                        n_q, P_max, partition);
+  else
+    splitk_reduce_kernel<64><<<grid, 256, 0, stream>>>(out, out_dtype, m, l, o, context_lens,
+                                                       n_q, P_max, partition);
   return hipGetLastError();
 }
 

@@ -32,6 +32,22 @@
 // reference by more than 2^8 are the accumulators rescaled (weights stay
 // <= 256, far inside bf16 and fp32 range); the true max is tracked and the
 // partition's statistics are rebased on it at the end.
+//
+// A chunk is 32 tokens for bf16 and 64 for FP8 (16 KiB of K+V either way),
+// i.e. 2 or 4 row groups of 16 tokens. K loads are 16 B per lane: for bf16
+// lane (c, g4) reads dims 32kk + 8*g4 of token c (one MFMA step per load);
+// for FP8 it reads 16 dims at 64h + 16*g4 (two MFMA steps per load). Either
+// way a load instruction covers 64 contiguous bytes of 16 token rows; the
+// query operand uses the same dim assignment, so the dot products are
+// unchanged.
+//
+// Two work decompositions:
+//   interleaved (default): one workgroup per (partition, KV head, sequence);
+//     its 4 waves take the partition's chunks round-robin and merge their
+//     softmax states through LDS;
+//   wave-per-partition (short partitions): one workgroup per 4 consecutive
+//     partitions of a (KV head, sequence); each wave runs one partition end
+//     to end, so the load pipeline stays long, and writes its own partial.
 #include <float.h>
 
 #include "pkv_device.h"
@@ -106,41 +122,56 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c
 
 }  // namespace
 
+// Two waves per SIMD: the register budget is 256 per lane (arch + acc).
 template <int D, int BS, bool FP8, int NW, bool SPLIT_P>
-__global__ __launch_bounds__(NW * 64) void decode_partition_mfma(DecodeArgs a) {
-  constexpr int NKK = D / 32;                 // QK MFMAs per 16-token row group
-  constexpr int NJ = D / 16;                  // PV MFMAs (16 output dims each)
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_partition_mfma(DecodeArgs a) {
+  constexpr int CT = FP8 ? 64 : 32;           // tokens per chunk
+  constexpr int NRG = CT / 16;                // 16-token row groups per chunk
+  constexpr int NKS = CT / 32;                // 32-token PV k-steps per chunk
+  constexpr int NKK = D / 32;                 // QK MFMA steps over d
+  constexpr int NKL = FP8 ? NKK / 2 : NKK;    // 16-byte K loads per row group
+  constexpr int NJ = D / 16;                  // PV MFMAs per k-step (16 dims each)
   constexpr int DPL = D / 16;                 // dims per lane per V row
-  constexpr int BPC = 32 / BS;                // blocks per 32-token chunk
+  constexpr int BPC = CT / BS;                // blocks per chunk
   constexpr int EB = FP8 ? 1 : 2;             // bytes per element
-  constexpr int KB = 8 * EB;                  // bytes per K load (8 dims)
   constexpr int VB = DPL * EB;                // bytes per V load (DPL dims)
-  using KT = typename Vec<KB>::T;
+  constexpr int NVS = 8 * NKS;                // V token slots per chunk
   using VT = typename Vec<VB>::T;
   constexpr int VW = (DPL * 2) / 4;           // bf16 words per V row slice (after conversion)
+  static_assert(CT % BS == 0 && NKL >= 1, "chunk shape");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15;
   const int g4 = lane >> 4;
 
+  // grid: x = (KV head, head tile), y = sequence, z = partition group counted
+  // from the end, so the partitions that only long sequences have are
+  // dispatched first and the short tail of the launch is made of first
+  // partitions
   const int G = a.n_q / a.n_kv;
   const int tiles = (G + 15) / 16;
-  const int j = blockIdx.x;
-  const int g = blockIdx.y / tiles;
-  const int tile = blockIdx.y % tiles;
+  const int g = blockIdx.x / tiles;
+  const int tile = blockIdx.x % tiles;
   const int h0 = g * G + tile * 16;
   const int nh = min(16, G - tile * 16);
-  const int b = blockIdx.z;
+  const int b = blockIdx.y;
+  const int pz = gridDim.z - 1 - blockIdx.z;
   const int ctx = min(a.context_lens[b], a.max_blocks * BS);
+  const bool wave_parts = a.wave_partitions;
+  // interleaved: the workgroup's partition; wave-per-partition: this wave's
+  const int j = wave_parts ? pz * NW + wave : pz;
   const int t0 = j * a.partition;
 
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
   __shared__ float sm_acc[NW][16][D + 4];
 
-  if (t0 >= ctx) {
-    if (!a.write_partials && j == 0) {
+  const int first_t0 = (wave_parts ? pz * NW : pz) * a.partition;
+  if (first_t0 >= ctx) {
+    // nothing to read; an empty sequence still owes zeros in single-pass mode
+    if (!a.write_partials && pz == 0) {
       for (int i = threadIdx.x; i < nh * D; i += blockDim.x) {
         const int64_t o = (static_cast<int64_t>(b) * a.n_q + h0 + i / D) * D + i % D;
         if (a.out_dtype == PKV_FP32)
@@ -151,19 +182,24 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_mfma(DecodeArgs a) {
     }
     return;
   }
-  const int t1 = min(t0 + a.partition, ctx);
+  const int t1 = min(t0 + a.partition, ctx);         // may be <= t0 for an idle wave
   const int blk0 = t0 / BS;
-  const int blk1 = (t1 + BS - 1) / BS;
+  const int blk1 = t1 > t0 ? (t1 + BS - 1) / BS : blk0;
   const int n_ch = (blk1 - blk0 + BPC - 1) / BPC;
 
-  // Q^T operand: lane (c, g4) holds q[h0 + c][32kk + 8*g4 .. +8] for each kk
+  // dims of MFMA step kk used by lane (c, g4); K and Q follow the same map
+  auto dimbase = [&](int kk) -> int {
+    return FP8 ? 64 * (kk >> 1) + 16 * g4 + 8 * (kk & 1) : 32 * kk + 8 * g4;
+  };
+
+  // Q^T operand: lane (c, g4) holds q[h0 + c][dimbase(kk) .. +8] for each kk
   bf16x8_t qop[NKK];
   {
     const bool live = c < nh;
     const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * a.n_q + h0 + (live ? c : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      uint4 w = *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * g4);
+      uint4 w = *reinterpret_cast<const uint4*>(qrow + dimbase(kk));
       if (!live) w = make_uint4(0, 0, 0, 0);
       qop[kk] = __builtin_bit_cast(bf16x8_t, w);
     }
@@ -176,56 +212,51 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_mfma(DecodeArgs a) {
   const int64_t block_stride = static_cast<int64_t>(a.n_kv) * tile_bytes;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
 
-  // per-lane byte offsets inside a chunk's tiles
-  // K: row group rg, step kk -> token rg*16 + c, dims 32kk + 8*g4
-  // V: slot s -> token (s < 4 ? 4*g4 + s : 16 + 4*g4 + s - 4), dims DPL*c
-  auto k_off = [&](int rg, int kk) -> int {
-    const int tok = rg * 16 + c;                          // token within the chunk
-    return ((tok % BS) * D + 32 * kk + 8 * g4) * EB;
-  };
-  auto v_off = [&](int s) -> int {
-    const int tok = (s < 4 ? 4 * g4 + s : 16 + 4 * g4 + s - 4);
-    return ((tok % BS) * D + DPL * c) * EB;
+  // chunk token of V slot s: k-step s/8, row group 2*(s/8) + (s%8)/4, token 4*g4 + s%4
+  auto v_tok = [&](int s) -> int {
+    const int s8 = s & 7;
+    return 16 * (2 * (s >> 3) + (s8 >> 2)) + 4 * g4 + (s8 & 3);
   };
 
   struct Chunk {
-    KT k[2][NKK];
-    VT v[8];
+    uint4 k[NRG][NKL];
+    VT v[NVS];
   };
 
   auto load = [&](Chunk& ch, int ci) {
-    const int bA = blk0 + ci * BPC;
-    int pA = bt[bA];
-    if (pA < 0 || pA >= a.num_blocks) pA = 0;
-    const uint8_t* kA = a.k_cache + pA * block_stride + head_off;
-    const uint8_t* vA = a.v_cache + pA * block_stride + head_off;
-    const uint8_t* kB = kA;
-    const uint8_t* vB = vA;
-    bool haveB = true;
-    if constexpr (BPC == 2) {
-      haveB = bA + 1 < blk1;
-      int pB = haveB ? bt[bA + 1] : 0;
-      if (pB < 0 || pB >= a.num_blocks) pB = 0;
-      kB = a.k_cache + pB * block_stride + head_off;
-      vB = a.v_cache + pB * block_stride + head_off;
+    const uint8_t* kb[BPC];
+    const uint8_t* vb[BPC];
+    bool have[BPC];
+#pragma unroll
+    for (int i = 0; i < BPC; ++i) {
+      const int blk = blk0 + ci * BPC + i;
+      have[i] = blk < blk1;
+      int p = have[i] ? bt[blk] : 0;
+      if (p < 0 || p >= a.num_blocks) p = 0;
+      kb[i] = a.k_cache + p * block_stride + head_off;
+      vb[i] = a.v_cache + p * block_stride + head_off;
     }
 #pragma unroll
-    for (int rg = 0; rg < 2; ++rg)
+    for (int rg = 0; rg < NRG; ++rg) {
+      const int t = 16 * rg + c;                       // K: token c of row group rg
+      const int bi = t / BS;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const uint8_t* base = (BPC == 2 && rg == 1) ? kB : kA;
-        if (BPC == 2 && rg == 1 && !haveB)
-          ch.k[rg][kk] = KT{};
+      for (int kl = 0; kl < NKL; ++kl) {
+        const int dim = FP8 ? 64 * kl + 16 * g4 : 32 * kl + 8 * g4;
+        if (have[bi])
+          ld_stream(ch.k[rg][kl], kb[bi] + ((t % BS) * D + dim) * EB);
         else
-          ld_stream(ch.k[rg][kk], base + k_off(rg, kk));
+          ch.k[rg][kl] = make_uint4(0, 0, 0, 0);
       }
+    }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint8_t* base = (BPC == 2 && s >= 4) ? vB : vA;
-      if (BPC == 2 && s >= 4 && !haveB)
-        ch.v[s] = VT{};
+    for (int s = 0; s < NVS; ++s) {
+      const int t = v_tok(s);
+      const int bi = t / BS;
+      if (have[bi])
+        ld_stream(ch.v[s], vb[bi] + ((t % BS) * D + DPL * c) * EB);
       else
-        ld_stream(ch.v[s], base + v_off(s));
+        ch.v[s] = VT{};
     }
   };
 
@@ -237,48 +268,43 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_mfma(DecodeArgs a) {
   for (int jj = 0; jj < NJ; ++jj) acc[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   auto compute = [&](Chunk& ch, int ci) {
-    const int tok0 = (blk0 + ci * BPC) * BS;             // first token of the chunk
-    // ---- scores
-    f32x4_t sc[2];
+    const int tok0 = (blk0 + ci * BPC) * BS;           // first token of the chunk
+    // ---- scores: s[4*rg + i] is token 16*rg + 4*g4 + i for head c
+    float s[4 * NRG];
 #pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-      sc[rg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int rg = 0; rg < NRG; ++rg) {
+      f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         bf16x8_t kop;
         if constexpr (!FP8) {
           kop = __builtin_bit_cast(bf16x8_t, ch.k[rg][kk]);
         } else {
-          const uint2 w = ch.k[rg][kk];
-          kop = as_bf16x8(fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x),
-                          fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y));
+          const uint4 w = ch.k[rg][kk >> 1];
+          const uint32_t w0 = (kk & 1) ? w.z : w.x;
+          const uint32_t w1 = (kk & 1) ? w.w : w.y;
+          kop = as_bf16x8(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                          fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
         }
-        sc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sc[rg], 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sc, 0, 0, 0);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[4 * rg + i] = sc[i] * qscale;
     }
-    float s[8];
+    if (tok0 + CT > t1) {                              // only the partition's last chunk
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = sc[0][i] * qscale;
-      s[4 + i] = sc[1][i] * qscale;
-    }
-    const bool tail = tok0 + 32 > t1;
-    if (tail) {
+      for (int rg = 0; rg < NRG; ++rg)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tok = tok0 + (i < 4 ? 4 * g4 + i : 16 + 4 * g4 + i - 4);
-        s[i] = tok < t1 ? s[i] : -INFINITY;
-      }
+        for (int i = 0; i < 4; ++i)
+          if (tok0 + 16 * rg + 4 * g4 + i >= t1) s[4 * rg + i] = -INFINITY;
 #pragma unroll
-      for (int si = 0; si < 8; ++si) {
-        const int tok = tok0 + (si < 4 ? 4 * g4 + si : 16 + 4 * g4 + si - 4);
-        if (tok >= t1) ch.v[si] = VT{};
-      }
+      for (int si = 0; si < NVS; ++si)
+        if (tok0 + v_tok(si) >= t1) ch.v[si] = VT{};
     }
     // ---- online softmax for head c (shared by the 4 k-group lanes)
     float mx = s[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+    for (int i = 1; i < 4 * NRG; ++i) mx = fmaxf(mx, s[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     m_true = fmaxf(m_true, mx);
@@ -291,68 +317,74 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_mfma(DecodeArgs a) {
       for (int jj = 0; jj < NJ; ++jj) acc[jj] *= alpha;
       m_ref = m_new;
     }
-    float p[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = fast_exp2(s[i] - m_ref);
-      l += p[i];
-    }
-    uint32_t ph[4], pl[4];
+    for (int ks = 0; ks < NKS; ++ks) {
+      // P^T operand of k-step ks: slots 0-3 row group 2ks, 4-7 row group 2ks+1
+      float p[8];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      ph[t] = pack_bf16(p[2 * t], p[2 * t + 1]);
-      if constexpr (SPLIT_P) {
-        float h0f, h1f;
-        bf16x2_to_f32(ph[t], h0f, h1f);
-        pl[t] = pack_bf16(p[2 * t] - h0f, p[2 * t + 1] - h1f);
+      for (int i = 0; i < 8; ++i) {
+        p[i] = fast_exp2(s[8 * ks + i] - m_ref);
+        l += p[i];
       }
-    }
-    const bf16x8_t pop_hi = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
-    bf16x8_t pop_lo;
-    if constexpr (SPLIT_P) pop_lo = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
-
-    // ---- V^T operand: vb[s][w] = bf16 pair (dims DPL*c + 2w, +1) of token slot s
-    uint32_t vb[8][VW];
+      uint32_t ph[4], pl[4];
 #pragma unroll
-    for (int si = 0; si < 8; ++si) {
-      if constexpr (!FP8) {
-#pragma unroll
-        for (int w = 0; w < VW; ++w) vb[si][w] = word(ch.v[si], w);
-      } else {
-#pragma unroll
-        for (int w = 0; w < VW / 2; ++w) {
-          const uint32_t x = word(ch.v[si], w);
-          vb[si][2 * w] = fp8x2_to_bf16x2<false>(x);
-          vb[si][2 * w + 1] = fp8x2_to_bf16x2<true>(x);
+      for (int t = 0; t < 4; ++t) {
+        ph[t] = pack_bf16(p[2 * t], p[2 * t + 1]);
+        if constexpr (SPLIT_P) {
+          float h0f, h1f;
+          bf16x2_to_f32(ph[t], h0f, h1f);
+          pl[t] = pack_bf16(p[2 * t] - h0f, p[2 * t + 1] - h1f);
         }
       }
-    }
+      const bf16x8_t pop_hi = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
+      bf16x8_t pop_lo;
+      if constexpr (SPLIT_P) pop_lo = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
+
+      // ---- V^T operand: vb[s][w] = bf16 pair (dims DPL*c + 2w, +1) of slot 8ks + s
+      uint32_t vw[8][VW];
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const int w = jj >> 1;
-      const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t t4[4];
+      for (int si = 0; si < 8; ++si) {
+        if constexpr (!FP8) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        t4[t] = __builtin_amdgcn_perm(vb[2 * t + 1][w], vb[2 * t][w], sel);
-      const bf16x8_t vop = as_bf16x8(t4[0], t4[1], t4[2], t4[3]);
-      acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi, acc[jj], 0, 0, 0);
-      if constexpr (SPLIT_P)
-        acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo, acc[jj], 0, 0, 0);
+          for (int w = 0; w < VW; ++w) vw[si][w] = word(ch.v[8 * ks + si], w);
+        } else {
+#pragma unroll
+          for (int w = 0; w < VW / 2; ++w) {
+            const uint32_t x = word(ch.v[8 * ks + si], w);
+            vw[si][2 * w] = fp8x2_to_bf16x2<false>(x);
+            vw[si][2 * w + 1] = fp8x2_to_bf16x2<true>(x);
+          }
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        const int w = jj >> 1;
+        const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t t4[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          t4[t] = __builtin_amdgcn_perm(vw[2 * t + 1][w], vw[2 * t][w], sel);
+        const bf16x8_t vop = as_bf16x8(t4[0], t4[1], t4[2], t4[3]);
+        acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi, acc[jj], 0, 0, 0);
+        if constexpr (SPLIT_P)
+          acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo, acc[jj], 0, 0, 0);
+      }
     }
   };
 
-  // ---- main loop: this wave's chunks wave, wave + NW, ...; next chunk's loads in flight
+  // ---- main loop, next chunk's loads in flight while the current one is computed
   {
+    const int first = wave_parts ? 0 : wave;
+    const int stride = wave_parts ? 1 : NW;
     Chunk A, B;
-    int ci = wave;
+    int ci = first;
     if (ci < n_ch) load(A, ci);
-    for (; ci < n_ch; ci += 2 * NW) {
-      if (ci + NW < n_ch) load(B, ci + NW);
+    for (; ci < n_ch; ci += 2 * stride) {
+      if (ci + stride < n_ch) load(B, ci + stride);
       compute(A, ci);
-      if (ci + NW >= n_ch) break;
-      if (ci + 2 * NW < n_ch) load(A, ci + 2 * NW);
-      compute(B, ci + NW);
+      if (ci + stride >= n_ch) break;
+      if (ci + 2 * stride < n_ch) load(A, ci + 2 * stride);
+      compute(B, ci + stride);
     }
   }
 
@@ -371,8 +403,27 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_mfma(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) sm_acc[wave][c][DPL * (4 * g4 + i) + jj] = acc[jj][i] * f;
   __syncthreads();
 
-  // ---- merge the waves; write (m, l, o) or the final output
   const float vscale = FP8 ? a.v_scale[g] : 1.0f;
+  if (wave_parts) {
+    // every wave's partition is a partial of its own
+    for (int i = threadIdx.x; i < NW * nh * D; i += blockDim.x) {
+      const int w = i / (nh * D);
+      const int h = (i / D) % nh;
+      const int e = i % D;
+      const int jw = pz * NW + w;
+      if (jw >= a.P_max || jw * a.partition >= ctx) continue;
+      const float L = sm_l[w][h];
+      const int64_t mi = (static_cast<int64_t>(b) * a.n_q + h0 + h) * a.P_max + jw;
+      if (e == 0) {
+        a.ws_m[mi] = sm_m[w][h];
+        a.ws_l[mi] = L;
+      }
+      a.ws_o[mi * D + e] = sm_acc[w][h][e] / L * vscale;
+    }
+    return;
+  }
+
+  // ---- interleaved: merge the waves; write (m, l, o) or the final output
   for (int i = threadIdx.x; i < nh * D; i += blockDim.x) {
     const int h = i / D;
     const int e = i % D;
@@ -417,7 +468,8 @@ static hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
 
 hipError_t launch_decode_partition_mfma(const DecodeArgs& a, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
-  const dim3 grid(a.P_max, a.n_kv * ((G + 15) / 16), a.B);
+  const int gz = a.wave_partitions ? (a.P_max + kMfmaWaves - 1) / kMfmaWaves : a.P_max;
+  const dim3 grid(a.n_kv * ((G + 15) / 16), a.B, gz);
   const bool fp8 = a.kv_dtype == PKV_FP8_E4M3;
   if (a.d == 128) {
     if (a.bs == 16) return fp8 ? launch_mfma<128, 16, true>(a, grid, s)

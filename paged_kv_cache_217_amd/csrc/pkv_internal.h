@@ -32,6 +32,7 @@ struct DecodeArgs {
   int P_max;                  // partitions launched per sequence
   float scale;
   bool write_partials;        // true: (m, l, o) to workspace; false: out directly
+  bool wave_partitions;       // partials mode only: one wave per partition
 };
 
 // Partition kernels: matrix-core (default) and vector-ALU variants.
