@@ -56,6 +56,8 @@ def parse():
                     choices=["gqa_70b", "mha_7b", "gqa_70b_fp8", "long_prefix", "tiny"])
     ap.add_argument("--layers", type=int, default=0, help="override layer count (0: workload's)")
     ap.add_argument("--partition", type=int, default=0, help="split-K partition (0: library)")
+    ap.add_argument("--schedule", type=int, default=1,
+                    help="1: longest-first work list built once per step (pkv_decode_schedule)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the oracle CPU baseline (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -141,8 +143,14 @@ def main():
     stream = torch.cuda.current_stream()
     split = P_max > 1
 
+    sched_buf = None
+    if args.schedule:
+        sched_buf = torch.empty(max(32, pkv.lib().pkv_decode_schedule_bytes(B, max_ctx, P)) // 4,
+                                dtype=torch.int32, device=dev)
+
     def step(ev=None):
         pkv.slot_mapping(bt, pos, bs, out=slots)
+        sched = pkv.decode_schedule(cl, max_ctx, P, out=sched_buf) if args.schedule else None
         for layer in range(layers):
             kc, vc, ks, vs = caches[layer]
             if ev is not None:
@@ -152,14 +160,14 @@ def main():
                 ev[layer][1].record(stream)
             if split:
                 pkv.paged_decode_partials(q[layer], kc, vc, bt, cl, w.scale, max_ctx, P,
-                                          k_scale=ks, v_scale=vs, workspace=ws)
+                                          k_scale=ks, v_scale=vs, workspace=ws, schedule=sched)
                 if ev is not None:
                     ev[layer][2].record(stream)
                 pkv.splitk_reduce(m_, l_, o_, cl, P, out=out)
             else:
                 pkv.paged_decode_attention(q[layer], kc, vc, bt, cl, w.scale, max_ctx,
                                            k_scale=ks, v_scale=vs, partition_size=P, out=out,
-                                           workspace=ws)
+                                           workspace=ws, schedule=sched)
                 if ev is not None:
                     ev[layer][2].record(stream)
             if ev is not None:
@@ -240,7 +248,8 @@ def main():
         "config": {"workload": w.name, "B": B, "context": max_ctx if len(set(
             w.context_lens.tolist())) == 1 else "varied", "tokens_per_layer": tokens,
             "n_q": n_q, "n_kv": n_kv, "d_head": d, "block_size": bs, "layers": layers,
-            "kv_dtype": w.kv_dtype, "partition_size": P, "accumulate": "fp32"},
+            "kv_dtype": w.kv_dtype, "partition_size": P, "accumulate": "fp32",
+            "schedule": "longest-first" if args.schedule else "grid order"},
         "hbm_peak_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
         "decode_tokens_per_s": round(tok_s, 1),
         "kernels_ms": {"kv_append": round(avg(t_append), 5),

@@ -151,7 +151,8 @@ pkv_status pkv_paged_decode_attention(const pkv_cache_desc* desc, void* out, int
                                       int32_t max_context_len, float scale,
                                       const float* k_scale, const float* v_scale,
                                       int32_t partition_size, void* workspace,
-                                      size_t workspace_bytes, void* stream);
+                                      size_t workspace_bytes, const void* schedule,
+                                      void* stream);
 
 /* ---------------------------------------------------------------------------
  * The two halves of pkv_paged_decode_attention, callable on their own (for
@@ -177,12 +178,36 @@ pkv_status pkv_paged_decode_partials(const pkv_cache_desc* desc, const void* q,
                                      int32_t max_context_len, float scale,
                                      const float* k_scale, const float* v_scale,
                                      int32_t partition_size, void* workspace,
-                                     size_t workspace_bytes, void* stream);
+                                     size_t workspace_bytes, const void* schedule,
+                                     void* stream);
 
 pkv_status pkv_splitk_reduce(void* out, int32_t out_dtype, const float* m, const float* l,
                              const float* o, const int32_t* context_lens, int32_t B,
                              int32_t n_q, int32_t d_head, int32_t max_partitions,
                              int32_t partition_size, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Longest-first schedule (optional; a performance aid, not part of the
+ * method). Sequences of very different lengths leave a long tail when their
+ * partitions run in index order. pkv_decode_schedule writes, into a caller
+ * buffer of pkv_decode_schedule_bytes(B, max_context_len, partition_size)
+ * bytes (device memory), the list of (sequence, partition) work items in
+ * decreasing size: every full partition, then each sequence's last partition
+ * bucketed by size. It depends only on context_lens and the partition size,
+ * so one schedule serves every layer of a decode step.
+ *
+ * Passing it as `schedule` to pkv_paged_decode_attention / _partials makes
+ * the partition kernel take its work in that order. The call must use the
+ * same context_lens contents, B, max_context_len and resolved partition size
+ * the schedule was built with (results are unspecified otherwise); NULL keeps
+ * the static grid order. partition_size must be > 0 (resolve 0 with
+ * pkv_default_partition_size first). B above 65535 is unsupported.
+ * ------------------------------------------------------------------------- */
+size_t pkv_decode_schedule_bytes(int32_t B, int32_t max_context_len, int32_t partition_size);
+
+pkv_status pkv_decode_schedule(const int32_t* context_lens, int32_t B, int32_t max_context_len,
+                               int32_t partition_size, void* schedule, size_t schedule_bytes,
+                               void* stream);
 
 /* ---------------------------------------------------------------------------
  * Copy-on-write block copy ([SMTS] "Paged KV-Cache with Radix Tree Prefix

@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     PkvError,
     cache_desc,
     copy_blocks,
+    decode_schedule,
     decode_workspace_bytes,
     default_partition_size,
     gather_kv,

@@ -61,10 +61,12 @@ SIGNATURES = {
     "pkv_default_partition_size": (_i32, [ctypes.POINTER(CacheDesc), _i32, _i32, _i32]),
     "pkv_paged_decode_attention": (_i32, [ctypes.POINTER(CacheDesc), _vp, _i32, _vp, _vp, _vp,
                                           _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32,
-                                          _vp, _sz, _vp]),
+                                          _vp, _sz, _vp, _vp]),
     "pkv_paged_decode_partials": (_i32, [ctypes.POINTER(CacheDesc), _vp, _vp, _vp, _vp, _i32,
                                          _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _sz,
-                                         _vp]),
+                                         _vp, _vp]),
+    "pkv_decode_schedule_bytes": (_sz, [_i32, _i32, _i32]),
+    "pkv_decode_schedule": (_i32, [_vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "pkv_splitk_reduce": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                  _vp]),
     "pkv_copy_blocks": (_i32, [ctypes.POINTER(CacheDesc), _vp, _vp, _vp, _i32, _vp]),
@@ -89,7 +91,7 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"libpkv.so not found at {LIB_PATH}; run "
-                              "`python -m paged_kv_cache_217_amd.build` first")
+                              "`python paged_kv_cache_217_amd/build.py` first")
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)
@@ -227,9 +229,23 @@ def _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_s
     return desc, B, n_q, d
 
 
+def decode_schedule(context_lens, max_context_len, partition_size, out=None, stream=None):
+    """Longest-first (sequence, partition) work list for the partition kernel (pkv.h)."""
+    _need(context_lens, torch.int32, "context_lens")
+    B = context_lens.numel()
+    nbytes = int(lib().pkv_decode_schedule_bytes(B, int(max_context_len), int(partition_size)))
+    if out is None:
+        out = torch.empty(max(nbytes, 32) // 4, dtype=torch.int32, device=context_lens.device)
+    _check(lib().pkv_decode_schedule(_ptr(context_lens), B, int(max_context_len),
+                                     int(partition_size), _ptr(out), out.numel() * 4,
+                                     _stream(stream)), "pkv_decode_schedule")
+    return out
+
+
 def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale,
                            max_context_len, k_scale=None, v_scale=None, partition_size=0,
-                           out=None, out_dtype=torch.float32, workspace=None, stream=None):
+                           out=None, out_dtype=torch.float32, workspace=None, schedule=None,
+                           stream=None):
     """out[b, h] = softmax(scale q[b,h] . K_b) V_b over the paged cache (see pkv.h)."""
     desc, B, n_q, d = _decode_common(q, k_cache, v_cache, block_tables, context_lens,
                                      k_scale, v_scale)
@@ -242,7 +258,7 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
         ctypes.byref(desc), _ptr(out), _out_code(out.dtype), _ptr(q), _ptr(k_cache),
         _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, n_q,
         int(max_context_len), float(scale), _ptr(k_scale), _ptr(v_scale), P, _ptr(workspace),
-        workspace.numel(), _stream(stream)), "pkv_paged_decode_attention")
+        workspace.numel(), _ptr(schedule), _stream(stream)), "pkv_paged_decode_attention")
     return out
 
 
@@ -260,7 +276,7 @@ def partial_views(workspace, B, n_q, d, P_max):
 
 def paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale,
                           max_context_len, partition_size, k_scale=None, v_scale=None,
-                          workspace=None, stream=None):
+                          workspace=None, schedule=None, stream=None):
     """Per-partition (m, l, o) of the split-K pass; returns (m, l, o, workspace)."""
     desc, B, n_q, d = _decode_common(q, k_cache, v_cache, block_tables, context_lens,
                                      k_scale, v_scale)
@@ -270,8 +286,8 @@ def paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale
     _check(lib().pkv_paged_decode_partials(
         ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), B, n_q, int(max_context_len), float(scale),
-        _ptr(k_scale), _ptr(v_scale), P, _ptr(workspace), workspace.numel(), _stream(stream)),
-        "pkv_paged_decode_partials")
+        _ptr(k_scale), _ptr(v_scale), P, _ptr(workspace), workspace.numel(), _ptr(schedule),
+        _stream(stream)), "pkv_paged_decode_partials")
     P_max = max(1, -(-int(max_context_len) // P))
     m, l, o = partial_views(workspace, B, n_q, d, P_max)
     return m, l, o, workspace

@@ -1,6 +1,9 @@
 """Build libpkv.so in-tree with hipcc for gfx950.
 
-    python -m paged_kv_cache_217_amd.build        (or build() from Python)
+    python paged_kv_cache_217_amd/build.py        (or __graft_entry__.build())
+
+This file is run or loaded by path, never imported through the package (the
+package loads libpkv.so when imported).
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
 selection disabled (the plain float code still vectorises to scalar

@@ -65,6 +65,21 @@ bool use_wave_partitions(int32_t partition) {
   return partition <= 1024;
 }
 
+size_t schedule_bytes(int64_t B, int64_t P_max) {
+  return pkv::kScheduleHeader * sizeof(int32_t) + static_cast<size_t>(B * P_max) * 2 * sizeof(int32_t);
+}
+
+// A schedule orders the partition kernel's work (see pkv_decode_schedule).
+pkv_status attach_schedule(pkv::DecodeArgs* a, const void* schedule) {
+  a->schedule = static_cast<const int32_t*>(schedule);
+  if (!schedule) return PKV_OK;
+  if ((reinterpret_cast<uintptr_t>(schedule) & 7u) != 0) return PKV_ERR_INVALID_ARG;
+  const int G = a->n_q / a->n_kv;
+  const int64_t grid = static_cast<int64_t>(a->n_kv) * ((G + 15) / 16) * a->B * a->P_max;
+  if (grid > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
 struct Workspace {
   float* m;
   float* l;
@@ -203,7 +218,8 @@ pkv_status pkv_paged_decode_attention(const pkv_cache_desc* desc, void* out, int
                                       int32_t max_context_len, float scale,
                                       const float* k_scale, const float* v_scale,
                                       int32_t partition_size, void* workspace,
-                                      size_t workspace_bytes_, void* stream) {
+                                      size_t workspace_bytes_, const void* schedule,
+                                      void* stream) {
   pkv::DecodeArgs a;
   pkv_status st = prepare_decode(desc, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
                                  context_lens, B, n_q, max_context_len, scale, k_scale, v_scale,
@@ -212,6 +228,8 @@ pkv_status pkv_paged_decode_attention(const pkv_cache_desc* desc, void* out, int
   if (out_dtype != PKV_FP32 && out_dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
   if (B == 0) return PKV_OK;
   if (!out) return PKV_ERR_INVALID_ARG;
+  st = attach_schedule(&a, schedule);
+  if (st != PKV_OK) return st;
   a.out = out;
   a.out_dtype = out_dtype;
   if (a.P_max == 1) {
@@ -226,7 +244,7 @@ pkv_status pkv_paged_decode_attention(const pkv_cache_desc* desc, void* out, int
   a.ws_l = w.l;
   a.ws_o = w.o;
   a.write_partials = true;
-  a.wave_partitions = use_wave_partitions(a.partition);
+  a.wave_partitions = a.schedule == nullptr && use_wave_partitions(a.partition);
   hipError_t e = pkv::launch_decode_partition(a, as_stream(stream));
   if (e != hipSuccess) return PKV_ERR_HIP;
   return from_hip(pkv::launch_splitk_reduce(out, out_dtype, w.m, w.l, w.o, context_lens, B, n_q,
@@ -240,13 +258,16 @@ pkv_status pkv_paged_decode_partials(const pkv_cache_desc* desc, const void* q,
                                      int32_t max_context_len, float scale,
                                      const float* k_scale, const float* v_scale,
                                      int32_t partition_size, void* workspace,
-                                     size_t workspace_bytes_, void* stream) {
+                                     size_t workspace_bytes_, const void* schedule,
+                                     void* stream) {
   pkv::DecodeArgs a;
   pkv_status st = prepare_decode(desc, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
                                  context_lens, B, n_q, max_context_len, scale, k_scale, v_scale,
                                  partition_size, &a);
   if (st != PKV_OK) return st;
   if (B == 0) return PKV_OK;
+  st = attach_schedule(&a, schedule);
+  if (st != PKV_OK) return st;
   const size_t need = workspace_bytes(B, n_q, a.d, a.P_max);
   if (!workspace || workspace_bytes_ < need) return PKV_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(workspace)) return PKV_ERR_INVALID_ARG;
@@ -255,7 +276,7 @@ pkv_status pkv_paged_decode_partials(const pkv_cache_desc* desc, const void* q,
   a.ws_l = w.l;
   a.ws_o = w.o;
   a.write_partials = true;
-  a.wave_partitions = use_wave_partitions(a.partition);
+  a.wave_partitions = a.schedule == nullptr && use_wave_partitions(a.partition);
   return from_hip(pkv::launch_decode_partition(a, as_stream(stream)));
 }
 
@@ -272,6 +293,28 @@ pkv_status pkv_splitk_reduce(void* out, int32_t out_dtype, const float* m, const
   return from_hip(pkv::launch_splitk_reduce(out, out_dtype, m, l, o, context_lens, B, n_q,
                                             d_head, max_partitions, partition_size,
                                             as_stream(stream)));
+}
+
+size_t pkv_decode_schedule_bytes(int32_t B, int32_t max_context_len, int32_t partition_size) {
+  if (B <= 0 || max_context_len < 0 || partition_size <= 0) return 0;
+  const int64_t P_max = std::max<int64_t>(1, cdiv(max_context_len, partition_size));
+  return schedule_bytes(B, P_max);
+}
+
+pkv_status pkv_decode_schedule(const int32_t* context_lens, int32_t B, int32_t max_context_len,
+                               int32_t partition_size, void* schedule, size_t schedule_bytes_,
+                               void* stream) {
+  if (B < 0 || max_context_len < 0 || partition_size <= 0) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  if (B > 65535) return PKV_ERR_UNSUPPORTED;
+  if (!context_lens || !schedule) return PKV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(schedule) & 7u) != 0) return PKV_ERR_INVALID_ARG;
+  const int64_t P_max = std::max<int64_t>(1, cdiv(max_context_len, partition_size));
+  if (P_max > kMaxReducePartitions) return PKV_ERR_UNSUPPORTED;
+  if (schedule_bytes_ < schedule_bytes(B, P_max)) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(pkv::launch_decode_schedule(context_lens, B, partition_size,
+                                              static_cast<int>(P_max),
+                                              static_cast<int32_t*>(schedule), as_stream(stream)));
 }
 
 pkv_status pkv_copy_blocks(const pkv_cache_desc* desc, void* k_cache, void* v_cache,

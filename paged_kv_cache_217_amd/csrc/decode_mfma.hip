@@ -150,14 +150,28 @@ void decode_partition_mfma(DecodeArgs a) {
   // from the end, so the partitions that only long sequences have are
   // dispatched first and the short tail of the launch is made of first
   // partitions
+  // With a schedule, x = item * (KV heads x tiles) + head slot, and the item
+  // names (sequence, partition) in longest-first order.
   const int G = a.n_q / a.n_kv;
   const int tiles = (G + 15) / 16;
-  const int g = blockIdx.x / tiles;
-  const int tile = blockIdx.x % tiles;
+  int hx, b, pz;
+  if (a.schedule != nullptr) {
+    const int hxn = a.n_kv * tiles;
+    const int item = blockIdx.x / hxn;
+    if (item >= a.schedule[0]) return;                 // past the list: nothing to do
+    const int2 it = reinterpret_cast<const int2*>(a.schedule + kScheduleHeader)[item];
+    hx = blockIdx.x % hxn;
+    b = it.x;
+    pz = it.y;
+  } else {
+    hx = blockIdx.x;
+    b = blockIdx.y;
+    pz = gridDim.z - 1 - blockIdx.z;
+  }
+  const int g = hx / tiles;
+  const int tile = hx % tiles;
   const int h0 = g * G + tile * 16;
   const int nh = min(16, G - tile * 16);
-  const int b = blockIdx.y;
-  const int pz = gridDim.z - 1 - blockIdx.z;
   const int ctx = min(a.context_lens[b], a.max_blocks * BS);
   const bool wave_parts = a.wave_partitions;
   // interleaved: the workgroup's partition; wave-per-partition: this wave's
@@ -468,8 +482,11 @@ static hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
 
 hipError_t launch_decode_partition_mfma(const DecodeArgs& a, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
+  const int hxn = a.n_kv * ((G + 15) / 16);
   const int gz = a.wave_partitions ? (a.P_max + kMfmaWaves - 1) / kMfmaWaves : a.P_max;
-  const dim3 grid(a.n_kv * ((G + 15) / 16), a.B, gz);
+  const dim3 grid = a.schedule != nullptr
+                        ? dim3(static_cast<unsigned>(static_cast<int64_t>(hxn) * a.B * a.P_max), 1, 1)
+                        : dim3(hxn, a.B, gz);
   const bool fp8 = a.kv_dtype == PKV_FP8_E4M3;
   if (a.d == 128) {
     if (a.bs == 16) return fp8 ? launch_mfma<128, 16, true>(a, grid, s)

@@ -33,7 +33,13 @@ struct DecodeArgs {
   float scale;
   bool write_partials;        // true: (m, l, o) to workspace; false: out directly
   bool wave_partitions;       // partials mode only: one wave per partition
+  const int32_t* schedule;    // optional longest-first work list (see schedule.hip)
 };
+
+// Schedule buffer: int32 header of kScheduleHeader words, then int2 items.
+constexpr int kScheduleHeader = 8;
+hipError_t launch_decode_schedule(const int32_t* context_lens, int B, int P, int P_max,
+                                  int32_t* sched, hipStream_t stream);
 
 // Partition kernels: matrix-core (default) and vector-ALU variants.
 hipError_t launch_decode_partition(const DecodeArgs& a, hipStream_t stream);

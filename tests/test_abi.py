@@ -53,7 +53,8 @@ def _decode(desc, **kw):
     return _lib.lib().pkv_paged_decode_attention(
         ctypes.byref(desc), args["out"], args["out_dtype"], args["q"], args["k"], args["v"],
         args["bt"], args["mb"], args["cl"], args["B"], args["n_q"], args["max_ctx"],
-        args["scale"], args["ks"], args["vs"], args["P"], args["ws"], args["wsb"], None)
+        args["scale"], args["ks"], args["vs"], args["P"], args["ws"], args["wsb"],
+        args.get("sched"), None)
 
 
 @pytest.mark.parametrize("kw,desc_kw,status", [
@@ -74,6 +75,23 @@ def _decode(desc, **kw):
 ])
 def test_decode_argument_validation(kw, desc_kw, status):
     assert _decode(_desc(**desc_kw), **kw) == status
+
+
+def test_schedule_validation_and_sizing():
+    L = _lib.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.pkv_decode_schedule_bytes(256, 26411, 4096) == 32 + 8 * 256 * 7
+    assert L.pkv_decode_schedule_bytes(4, 100, 0) == 0
+    assert L.pkv_decode_schedule(fake, 4, 100, 0, fake, 1024, None) == _lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_decode_schedule(fake, 70000, 100, 64, fake, 1 << 30, None) == \
+        _lib.PKV_ERR_UNSUPPORTED
+    assert L.pkv_decode_schedule(fake, 4, 100, 64, fake, 16, None) == \
+        _lib.PKV_ERR_WORKSPACE_TOO_SMALL
+    assert L.pkv_decode_schedule(fake, 4, 100, 64, ctypes.c_void_p(0x1004), 1024, None) == \
+        _lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_decode_schedule(fake, 0, 100, 64, None, 0, None) == _lib.PKV_OK
+    # a misaligned schedule is refused before anything is launched
+    assert _decode(_desc(), sched=ctypes.c_void_p(0x1004)) == _lib.PKV_ERR_INVALID_ARG
 
 
 def test_zero_batch_is_a_no_op():

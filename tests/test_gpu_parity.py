@@ -330,3 +330,77 @@ def test_append_then_attend_step(pkv):
         expect = ref.decode_attention(W.bits(q), ke, ve, w.block_tables, w.context_lens,
                                       w.scale, dt, ksn, vsn)
         check_close(out, expect, dt, f"step {dt}")
+
+
+# ------------------------------------------------------------------ longest-first schedule
+
+def expected_items(lens, P, P_max, single):
+    items = set()
+    for b, c in enumerate(lens):
+        n = min(-(-c // P), P_max) if c > 0 else 0
+        for j in range(n):
+            items.add((b, j))
+        if single and n == 0:
+            items.add((b, 0))
+    return items
+
+
+@pytest.mark.parametrize("lens,P", [([0, 5, 4096, 4097, 100, 8191, 1, 0, 30000], 4096),
+                                    ([37, 100], 8192), ([0, 0, 3], 16),
+                                    (list(range(1, 700, 3)), 64)])
+def test_schedule_is_every_item_longest_first(pkv, lens, P):
+    cl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    max_ctx = max(lens)
+    P_max = max(1, -(-max_ctx // P))
+    sched = pkv.decode_schedule(cl, max_ctx, P).cpu().numpy()
+    count = int(sched[0])
+    assert list(sched[1:4]) == [P, len(lens), P_max]
+    items = [tuple(x) for x in sched[8:8 + 2 * count].reshape(-1, 2)]
+    want = expected_items(lens, P, P_max, P_max == 1)
+    assert len(items) == count == len(want) and set(items) == want
+    # full partitions first, then last partitions in non-increasing size class
+    size = [min(P, max(lens[b] - j * P, 0)) for b, j in items]
+    nfull = sum(1 for b, j in items if (j + 1) * P < lens[b])
+    assert all(size[i] == P for i in range(nfull))
+    klass = [min(63, (P - s) * 64 // P) if s > 0 else 64 for s in size[nfull:]]
+    assert klass == sorted(klass)
+
+
+@pytest.mark.parametrize("case", [SHAPES[i] for i in (2, 3, 4, 5, 7, 10)],
+                         ids=[str(i) for i in (2, 3, 4, 5, 7, 10)])
+def test_scheduled_decode_matches(pkv, case):
+    lens, n_q, n_kv, d, bs, dt, P = case
+    w = W.custom("sched", lens, n_q, n_kv, d, bs, dt, seed=40 + SHAPES.index(case))
+    kc, vc, ks, vs = W.make_cache(w)
+    q = W.make_query(w)
+    kd, vd, qd, bt, cl, ksd, vsd = to_dev(w, kc, vc, q, ks, vs)
+    max_ctx = int(w.context_lens.max())
+    P = P or pkv.default_partition_size(kd, w.B, n_q, max_ctx)
+    sched = pkv.decode_schedule(cl, max_ctx, P)
+    out = pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, max_ctx, k_scale=ksd,
+                                     v_scale=vsd, partition_size=P, schedule=sched)
+    torch.cuda.synchronize()
+    expect = ref.decode_attention(W.bits(q), W.bits(kc), W.bits(vc), w.block_tables,
+                                  w.context_lens, w.scale, dt,
+                                  None if ks is None else ks.numpy(),
+                                  None if vs is None else vs.numpy())
+    check_close(out, expect, dt, f"scheduled {case}")
+    if P > 1024:       # same per-partition code path as the static grid: identical bits
+        plain = pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, max_ctx, k_scale=ksd,
+                                           v_scale=vsd, partition_size=P)
+        assert torch.equal(out, plain)
+
+
+def test_scheduled_single_pass_writes_empty_sequences(pkv):
+    w = W.custom("sched1", [0, 200, 0, 77], 8, 2, 128, 16, W.BF16, seed=47, extra_blocks=2)
+    kc, vc, _, _ = W.make_cache(w)
+    q = W.make_query(w)
+    kd, vd, qd, bt, cl, _, _ = to_dev(w, kc, vc, q)
+    sched = pkv.decode_schedule(cl, 200, 8192)
+    out = torch.full((w.B, w.n_q, w.d), float("nan"), device=DEV)
+    pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, 200, partition_size=8192,
+                               out=out, schedule=sched)
+    torch.cuda.synchronize()
+    expect = ref.decode_attention(W.bits(q), W.bits(kc), W.bits(vc), w.block_tables,
+                                  w.context_lens, w.scale)
+    check_close(out, expect, W.BF16, "scheduled single pass")
