@@ -404,3 +404,71 @@ def test_scheduled_single_pass_writes_empty_sequences(pkv):
     expect = ref.decode_attention(W.bits(q), W.bits(kc), W.bits(vc), w.block_tables,
                                   w.context_lens, w.scale)
     check_close(out, expect, W.BF16, "scheduled single pass")
+
+
+# ------------------------------------------------------------------ limits
+
+def test_reduce_at_its_partition_limit(pkv):
+    """8192 partitions of one block each: the largest split the reduce accepts."""
+    bs, ctx = 16, 8192 * 16
+    w = W.custom("maxparts", [ctx, 1000], 2, 1, 128, bs, W.BF16, seed=50, pool_factor=1.0)
+    for use_sched in (False, True):
+        kc, vc, _, _ = W.make_cache(w, poison_unused=False)
+        q = W.make_query(w)
+        kd, vd, qd, bt, cl, _, _ = to_dev(w, kc, vc, q)
+        sched = pkv.decode_schedule(cl, ctx, bs) if use_sched else None
+        out = pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, ctx, partition_size=bs,
+                                         schedule=sched)
+        torch.cuda.synchronize()
+        expect = ref.decode_attention(W.bits(q), W.bits(kc), W.bits(vc), w.block_tables,
+                                      w.context_lens, w.scale)
+        check_close(out, expect, W.BF16, f"8192 partitions sched={use_sched}")
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, ctx + bs, partition_size=bs)
+
+
+def test_full_table_row_and_last_pool_block(pkv):
+    """A sequence exactly as long as its table row; the pool's last block in use."""
+    bs, mb = 32, 5
+    lens = [mb * bs, 3]
+    w = W.custom("edge", lens, 16, 2, 64, bs, W.FP8, seed=51, pool_factor=1.0)
+    bt = w.block_tables.copy()
+    last = w.num_blocks - 1
+    row = int(np.argwhere(bt == last)[0][0]) if (bt == last).any() else 0
+    assert (bt[:, :] == last).any() and bt.shape[1] == mb
+    kc, vc, ks, vs = W.make_cache(w)
+    q = W.make_query(w)
+    kd, vd, qd, btd, cl, ksd, vsd = to_dev(w, kc, vc, q, ks, vs)
+    for P in (0, 32, 64):
+        out = pkv.paged_decode_attention(qd, kd, vd, btd, cl, w.scale, mb * bs, k_scale=ksd,
+                                         v_scale=vsd, partition_size=P)
+        torch.cuda.synchronize()
+        expect = ref.decode_attention(W.bits(q), W.bits(kc), W.bits(vc), bt, w.context_lens,
+                                      w.scale, W.FP8, ks.numpy(), vs.numpy())
+        check_close(out, expect, W.FP8, f"edge P={P} row={row}")
+
+
+def test_many_short_sequences_scheduled(pkv):
+    """4096 sequences of 1..64 tokens through the schedule, split-K and single pass."""
+    rng = np.random.default_rng(52)
+    lens = rng.integers(0, 65, size=4096).tolist()
+    w = W.custom("many", lens, 8, 8, 64, 16, W.BF16, seed=52)
+    kc, vc, _, _ = W.make_cache(w)
+    q = W.make_query(w)
+    kd, vd, qd, bt, cl, _, _ = to_dev(w, kc, vc, q)
+    expect = ref.decode_attention(W.bits(q), W.bits(kc), W.bits(vc), w.block_tables,
+                                  w.context_lens, w.scale)
+    for P in (16, 32, 8192):
+        sched = pkv.decode_schedule(cl, 64, P)
+        out = pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, 64, partition_size=P,
+                                         schedule=sched)
+        torch.cuda.synchronize()
+        check_close(out, expect, W.BF16, f"many P={P}")
+
+
+def test_bf16_output_through_split_k(pkv):
+    w = W.custom("bf16split", [900, 2000, 5], 32, 4, 128, 16, W.BF16, seed=53)
+    out, expect = run_case(pkv, w, partition_size=256, out_dtype=torch.bfloat16)
+    got = out.float().cpu().double().numpy()
+    assert np.max(np.abs(got - expect)) <= MAX_ABS[W.BF16]
+    assert np.max(np.abs(got - expect) / np.maximum(np.abs(expect), 1e-3)) <= 2 ** -8 + 1e-4
