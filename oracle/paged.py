@@ -17,6 +17,8 @@ What the decode path computes, in the order the pages give it:
   5. Append-then-attend: the new token's K/V is written to the cache first and
      attended to in the same step ([LLMI] section "Why We Need the Key-Value
      (KV) Cache" and flow step 5).
+  6. Several new tokens at once (chunked prefill, draft verification): each
+     attends causally to the positions up to its own (`multi_query_attention`).
 
 The oracle computes the plain definition (4) with a two-pass softmax in
 float64. Online softmax and split-K partitions are exact reformulations; the
@@ -276,4 +278,44 @@ def copy_blocks(cache, pairs):
     out = cache.copy()
     for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
         out[dst] = cache[src]
+    return out
+
+
+# --------------------------------------------------------------------------
+# 5. several new query tokens per sequence (chunked prefill, draft verification)
+# --------------------------------------------------------------------------
+
+def multi_query_attention(q_bits, k_cache, v_cache, block_tables, context_lens, query_lens,
+                          scale, kv_dtype=BF16, k_scale=None, v_scale=None):
+    """Causal attention of the last query_lens[b] tokens of each sequence.
+
+    q_bits: uint16 [B, Q, n_q, d] bfloat16 patterns (query i of sequence b is
+    row i; rows i >= query_lens[b] are unused and left zero in the output).
+    The K/V of the new tokens are already in the cache (append-then-attend), so
+    sequence b holds context_lens[b] tokens and its query i sits at position
+    p = context_lens[b] - query_lens[b] + i. That query attends to tokens
+    0..p: causal self-attention over the new tokens ([LLMI] "4. Internal
+    workings", flow step 2) on top of the cached prefix. [LLMI] "9. Failure
+    modes and limitations" (chunked prefill) and "7. Practical applications"
+    (speculative decoding verifies several draft tokens in one pass) are the
+    two uses. Returns float64 [B, Q, n_q, d].
+    """
+    B, Q, n_q, d = q_bits.shape
+    n_kv = k_cache.shape[1]
+    G = n_q // n_kv
+    q = _bf16.to_f64(q_bits)
+    out = np.zeros((B, Q, n_q, d))
+    for b in range(B):
+        ctx = int(context_lens[b])
+        ql = int(query_lens[b])
+        if ql > ctx or ql > Q:
+            raise ValueError("query_lens must be <= context_lens and <= Q")
+        kd = dequantize(gather(k_cache, block_tables[b], ctx), kv_dtype, k_scale)
+        vd = dequantize(gather(v_cache, block_tables[b], ctx), kv_dtype, v_scale)
+        for i in range(ql):
+            p = ctx - ql + i
+            for h in range(n_q):
+                g = h // G
+                out[b, i, h], _ = attention_one(q[b, i, h], kd[:p + 1, g, :], vd[:p + 1, g, :],
+                                                scale)
     return out
