@@ -50,77 +50,13 @@
 //     to end, so the load pipeline stays long, and writes its own partial.
 #include <float.h>
 
+#include "mfma_common.h"
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-namespace {
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazyRescale = 8.0f;     // log2 of the largest weight allowed before rescaling
-
-template <int BYTES>
-struct Vec;
-template <>
-struct Vec<16> {
-  using T = uint4;
-};
-template <>
-struct Vec<8> {
-  using T = uint2;
-};
-template <>
-struct Vec<4> {
-  using T = uint32_t;
-};
-
-// Streaming (non-temporal) loads of KV bytes: every K/V byte is read once
-// per step, so the loads ask the caches not to keep the lines.
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void ld_stream(uint4& out, const uint8_t* p) {
-  const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  out = make_uint4(x[0], x[1], x[2], x[3]);
-}
-__device__ __forceinline__ void ld_stream(uint2& out, const uint8_t* p) {
-  const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
-  out = make_uint2(x[0], x[1]);
-}
-__device__ __forceinline__ void ld_stream(uint32_t& out, const uint8_t* p) {
-  out = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-}
-
-__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-__device__ __forceinline__ uint32_t word(const uint2& v, int i) { return i == 0 ? v.x : v.y; }
-__device__ __forceinline__ uint32_t word(const uint32_t& v, int) { return v; }
-
-// 2 FP8 E4M3FN codes (bytes 0,1 or 2,3 of w) -> 2 bf16 in one word, exact.
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  auto r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, HI);
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  bf16x2_t v;
-  v[0] = static_cast<__bf16>(lo);
-  v[1] = static_cast<__bf16>(hi);
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  uint4 u = make_uint4(a, b, c, d);
-  return __builtin_bit_cast(bf16x8_t, u);
-}
-
-}  // namespace
+using namespace mfma;
 
 // Two waves per SIMD: the register budget is 256 per lane (arch + acc).
 template <int D, int BS, bool FP8, int NW, bool SPLIT_P>
