@@ -187,6 +187,52 @@ pkv_status pkv_splitk_reduce(void* out, int32_t out_dtype, const float* m, const
                              int32_t partition_size, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Paged attention for several new query tokens per sequence (chunked
+ * prefill, verification of draft tokens): [LLMI] "4. Internal workings"
+ * (causal self-attention while a prompt is ingested), "9. Failure modes and
+ * limitations" (prompts taken in chunks) and "7. Practical applications"
+ * (speculative decoding checks several proposed tokens in one pass); the
+ * K/V reads go through the block table exactly as in decode ([MTKV]
+ * "High-Throughput Paged Attention Kernel Integration").
+ *
+ * The new tokens' K/V are already in the cache (append first, as in decode),
+ * so sequence b holds ctx_b = context_lens[b] tokens, its last
+ * q_b = query_lens[b] of them are the queries, and query i < q_b sits at
+ * position p = ctx_b - q_b + i and attends to tokens 0..p:
+ *   out[b, i, h, :] = sum_{t <= p} w_t V_b[t, h / G, :],
+ *   w = softmax_{t <= p}(scale * q[b, i, h, :] . K_b[t, h / G, :]),
+ * K_b/V_b, FP8 scales and G as in pkv_paged_decode_attention. Rows
+ * i >= q_b of out are written as zeros.
+ *
+ * q: bfloat16 [B, Q, n_q, d_head] (query-major within a sequence). out:
+ * [B, Q, n_q, d_head] of out_dtype. query_lens: int32 [B] on the device,
+ * 0 <= query_lens[b] <= min(Q, ctx_b); a value outside that range is clamped
+ * into it. Q >= 1. Every other argument is as for pkv_paged_decode_attention,
+ * and Q == 1 with query_lens[b] == 1 computes the same thing as it.
+ * Split-K runs as in decode; a query's partitions end at its own position.
+ * workspace_bytes must be at least pkv_multi_query_workspace_bytes(...) for
+ * the same arguments when more than one partition results (else
+ * PKV_ERR_WORKSPACE_TOO_SMALL); with one partition it may be NULL.
+ * ------------------------------------------------------------------------- */
+size_t pkv_multi_query_workspace_bytes(int32_t B, int32_t Q, int32_t n_q, int32_t d_head,
+                                       int32_t max_context_len, int32_t partition_size);
+
+/* The partition size partition_size == 0 resolves to for multi-query calls. */
+int32_t pkv_multi_query_partition_size(const pkv_cache_desc* desc, int32_t B, int32_t Q,
+                                       int32_t n_q, int32_t max_context_len);
+
+pkv_status pkv_paged_multi_query_attention(const pkv_cache_desc* desc, void* out,
+                                           int32_t out_dtype, const void* q, int32_t Q,
+                                           const int32_t* query_lens, const void* k_cache,
+                                           const void* v_cache, const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, int32_t B, int32_t n_q,
+                                           int32_t max_context_len, float scale,
+                                           const float* k_scale, const float* v_scale,
+                                           int32_t partition_size, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Longest-first schedule (optional; a performance aid, not part of the
  * method). Sequences of very different lengths leave a long tail when their
  * partitions run in index order. pkv_decode_schedule writes, into a caller

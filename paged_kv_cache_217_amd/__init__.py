@@ -1,4 +1,4 @@
-"""MI355X-native paged KV cache and single-token decode attention.
+"""MI355X-native paged KV cache with single-token and multi-query decode attention.
 
 The compute path is libpkv.so (hand-written HIP for gfx950 behind the C ABI
 in include/pkv.h); this package is its Python binding. Importing it loads the
@@ -19,8 +19,10 @@ from ._lib import (  # noqa: F401
     kv_append,
     lib,
     make_workspace,
+    multi_query_partition_size,
     paged_decode_attention,
     paged_decode_partials,
+    paged_multi_query_attention,
     partial_views,
     slot_mapping,
     splitk_reduce,

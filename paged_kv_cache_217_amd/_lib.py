@@ -65,6 +65,12 @@ SIGNATURES = {
     "pkv_paged_decode_partials": (_i32, [ctypes.POINTER(CacheDesc), _vp, _vp, _vp, _vp, _i32,
                                          _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _sz,
                                          _vp, _vp]),
+    "pkv_multi_query_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_multi_query_partition_size": (_i32, [ctypes.POINTER(CacheDesc), _i32, _i32, _i32,
+                                              _i32]),
+    "pkv_paged_multi_query_attention": (_i32, [ctypes.POINTER(CacheDesc), _vp, _i32, _vp, _i32,
+                                               _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                                               _f32, _vp, _vp, _i32, _vp, _sz, _vp]),
     "pkv_decode_schedule_bytes": (_sz, [_i32, _i32, _i32]),
     "pkv_decode_schedule": (_i32, [_vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "pkv_splitk_reduce": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -259,6 +265,43 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
         _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, n_q,
         int(max_context_len), float(scale), _ptr(k_scale), _ptr(v_scale), P, _ptr(workspace),
         workspace.numel(), _ptr(schedule), _stream(stream)), "pkv_paged_decode_attention")
+    return out
+
+
+def multi_query_partition_size(k_cache, B, Q, n_q, max_context_len):
+    desc = cache_desc(k_cache)
+    return int(lib().pkv_multi_query_partition_size(ctypes.byref(desc), B, Q, n_q,
+                                                    max_context_len))
+
+
+def paged_multi_query_attention(q, query_lens, k_cache, v_cache, block_tables, context_lens,
+                                scale, max_context_len, k_scale=None, v_scale=None,
+                                partition_size=0, out=None, out_dtype=torch.float32,
+                                workspace=None, stream=None):
+    """Causal attention of the last query_lens[b] tokens of each sequence (see pkv.h).
+
+    q: bfloat16 [B, Q, n_q, d]; returns [B, Q, n_q, d] (rows past query_lens zero).
+    """
+    _need(query_lens, torch.int32, "query_lens")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, Q, n_q, d]")
+    B, Q, n_q, d = q.shape
+    desc, _, _, _ = _decode_common(q.view(B, Q * n_q, d), k_cache, v_cache, block_tables,
+                                   context_lens, k_scale, v_scale)
+    if query_lens.numel() != B:
+        raise ValueError("query_lens must hold one length per sequence")
+    if out is None:
+        out = torch.empty((B, Q, n_q, d), dtype=out_dtype, device=q.device)
+    P = int(partition_size) or multi_query_partition_size(k_cache, B, Q, n_q, max_context_len)
+    if workspace is None:
+        nbytes = int(lib().pkv_multi_query_workspace_bytes(B, Q, n_q, d, int(max_context_len), P))
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().pkv_paged_multi_query_attention(
+        ctypes.byref(desc), _ptr(out), _out_code(out.dtype), _ptr(q), Q, _ptr(query_lens),
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), B, n_q, int(max_context_len), float(scale), _ptr(k_scale),
+        _ptr(v_scale), P, _ptr(workspace), workspace.numel(), _stream(stream)),
+        "pkv_paged_multi_query_attention")
     return out
 
 

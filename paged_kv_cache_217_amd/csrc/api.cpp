@@ -33,7 +33,22 @@ pkv_status check_desc(const pkv_cache_desc* d) {
 // (the matrix-core kernel's head tile is 16 wide).
 int head_tile(int G) { return G <= 16 ? G : 16; }
 
+int32_t pick_partition_units(int64_t units, int32_t max_ctx);
+
 int32_t pick_partition(const pkv_cache_desc* d, int32_t B, int32_t n_q, int32_t max_ctx) {
+  const int G = n_q / d->n_kv;
+  return pick_partition_units(
+      static_cast<int64_t>(B) * d->n_kv * ((G + head_tile(G) - 1) / head_tile(G)), max_ctx);
+}
+
+// Multi-query workgroups each own 16 (query, head) rows of one KV head.
+int32_t pick_partition_mq(const pkv_cache_desc* d, int32_t B, int32_t Q, int32_t n_q,
+                          int32_t max_ctx) {
+  const int64_t rows = static_cast<int64_t>(Q) * (n_q / d->n_kv);
+  return pick_partition_units(static_cast<int64_t>(B) * d->n_kv * cdiv(rows, 16), max_ctx);
+}
+
+int32_t pick_partition_units(int64_t units, int32_t max_ctx) {
   // The partition kernel holds two 4-wave workgroups per CU (its register
   // budget allows two waves per SIMD), so 512 workgroups fill the 256 CUs
   // once. A batch whose (sequence, KV head) pairs alone fill that round and
@@ -43,9 +58,6 @@ int32_t pick_partition(const pkv_cache_desc* d, int32_t B, int32_t n_q, int32_t 
   // sequences of very different lengths) and shrink by halves while the grid
   // would not fill one round.
   constexpr int64_t kOneRound = 256 * 2;
-  const int G = n_q / d->n_kv;
-  const int64_t units =
-      static_cast<int64_t>(B) * d->n_kv * ((G + head_tile(G) - 1) / head_tile(G));
   if (max_ctx <= 8192 && units >= kOneRound) return 8192;
   int64_t P = 4096;
   while (P > 256 && units * cdiv(max_ctx, P) < kOneRound) P /= 2;
@@ -293,6 +305,73 @@ pkv_status pkv_splitk_reduce(void* out, int32_t out_dtype, const float* m, const
   return from_hip(pkv::launch_splitk_reduce(out, out_dtype, m, l, o, context_lens, B, n_q,
                                             d_head, max_partitions, partition_size,
                                             as_stream(stream)));
+}
+
+size_t pkv_multi_query_workspace_bytes(int32_t B, int32_t Q, int32_t n_q, int32_t d_head,
+                                       int32_t max_context_len, int32_t partition_size) {
+  if (B <= 0 || Q <= 0 || n_q <= 0 || d_head <= 0 || max_context_len < 0 ||
+      partition_size <= 0)
+    return 0;
+  const int64_t P_max = std::max<int64_t>(1, cdiv(max_context_len, partition_size));
+  return workspace_bytes(static_cast<int64_t>(B) * Q, n_q, d_head, P_max);
+}
+
+int32_t pkv_multi_query_partition_size(const pkv_cache_desc* desc, int32_t B, int32_t Q,
+                                       int32_t n_q, int32_t max_context_len) {
+  if (check_desc(desc) != PKV_OK || B < 0 || Q <= 0 || n_q <= 0 || n_q % desc->n_kv != 0 ||
+      max_context_len < 0)
+    return 0;
+  return pick_partition_mq(desc, B, Q, n_q, max_context_len);
+}
+
+pkv_status pkv_paged_multi_query_attention(const pkv_cache_desc* desc, void* out,
+                                           int32_t out_dtype, const void* q, int32_t Q,
+                                           const int32_t* query_lens, const void* k_cache,
+                                           const void* v_cache, const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, int32_t B, int32_t n_q,
+                                           int32_t max_context_len, float scale,
+                                           const float* k_scale, const float* v_scale,
+                                           int32_t partition_size, void* workspace,
+                                           size_t workspace_bytes_, void* stream) {
+  if (Q <= 0) return PKV_ERR_INVALID_ARG;
+  if (desc && check_desc(desc) == PKV_OK && n_q > 0 && n_q % desc->n_kv == 0 &&
+      partition_size == 0 && B >= 0 && max_context_len >= 0)
+    partition_size = pick_partition_mq(desc, B, Q, n_q, max_context_len);
+  pkv::DecodeArgs a;
+  pkv_status st = prepare_decode(desc, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                                 context_lens, B, n_q, max_context_len, scale, k_scale, v_scale,
+                                 partition_size, &a);
+  if (st != PKV_OK) return st;
+  if (out_dtype != PKV_FP32 && out_dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  if (!out || !query_lens) return PKV_ERR_INVALID_ARG;
+  const int64_t rows = static_cast<int64_t>(Q) * (n_q / desc->n_kv);
+  if (static_cast<int64_t>(desc->n_kv) * cdiv(rows, 16) > 0x7fffffff / 256)
+    return PKV_ERR_UNSUPPORTED;
+  a.Q = Q;
+  a.query_lens = query_lens;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  const hipStream_t s = as_stream(stream);
+  if (a.P_max == 1) {
+    a.write_partials = false;
+    return from_hip(pkv::launch_multi_query_partition(a, s));
+  }
+  const int64_t BQ = static_cast<int64_t>(B) * Q;
+  const size_t need = workspace_bytes(BQ, n_q, a.d, a.P_max);
+  if (!workspace || workspace_bytes_ < need) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(workspace)) return PKV_ERR_INVALID_ARG;
+  const Workspace w = carve(workspace, BQ, n_q, a.P_max);
+  a.ws_m = w.m;
+  a.ws_l = w.l;
+  a.ws_o = w.o;
+  a.write_partials = true;
+  hipError_t e = pkv::launch_multi_query_partition(a, s);
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  return from_hip(pkv::launch_splitk_reduce(out, out_dtype, w.m, w.l, w.o, context_lens, B, n_q,
+                                            a.d, a.P_max, a.partition, s, Q, query_lens,
+                                            max_blocks_per_seq * desc->block_size));
 }
 
 size_t pkv_decode_schedule_bytes(int32_t B, int32_t max_context_len, int32_t partition_size) {

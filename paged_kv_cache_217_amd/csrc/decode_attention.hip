@@ -271,20 +271,42 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Which partials an output row merges. Rows are (sequence, query, head),
+// query-major within a sequence; with one query per sequence (query_lens null)
+// a row reads every partition of its context, otherwise query i of q_len sits
+// at position ctx - q_len + i and reads only the partitions up to it; rows past
+// q_len read none and are written as zeros.
+struct ReduceRows {
+  const int32_t* context_lens;
+  const int32_t* query_lens;
+  int Q, n_q, P_max, partition, ctx_cap;
+};
+
+__device__ __forceinline__ int row_partitions(const ReduceRows& r, int64_t row) {
+  const int b = static_cast<int>(row / (static_cast<int64_t>(r.Q) * r.n_q));
+  const int ctx = min(r.context_lens[b], r.ctx_cap);
+  int last = ctx;                                    // tokens this row sees
+  if (r.query_lens) {
+    const int i = static_cast<int>((row / r.n_q) % r.Q);
+    const int ql = max(0, min(min(r.query_lens[b], r.Q), ctx));
+    last = i < ql ? ctx - ql + i + 1 : 0;
+  }
+  return last > 0 ? min((last + r.partition - 1) / r.partition, r.P_max) : 0;
+}
+
 // Few partitions per sequence: one wave per (sequence, query head), lanes own
 // output dims, weights broadcast by cross-lane reads (no LDS, no barrier).
 template <int D>
 __global__ __launch_bounds__(256) void splitk_reduce_wave_kernel(
     void* __restrict__ out, int out_dtype, const float* __restrict__ m,
     const float* __restrict__ l, const float* __restrict__ o,
-    const int32_t* __restrict__ context_lens, int B, int n_q, int P_max, int partition) {
+    ReduceRows rows, int64_t n_rows) {
   constexpr int DL = D / 64;                         // output dims per lane
   const int lane = threadIdx.x & 63;
-  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (bh >= B * n_q) return;                         // whole wave
-  const int b = bh / n_q;
-  const int ctx = context_lens[b];
-  const int np = ctx > 0 ? min((ctx + partition - 1) / partition, P_max) : 0;
+  const int64_t bh = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (bh >= n_rows) return;                          // whole wave
+  const int P_max = rows.P_max;
+  const int np = row_partitions(rows, bh);
   const float* mb = m + static_cast<int64_t>(bh) * P_max;
   const float* lb = l + static_cast<int64_t>(bh) * P_max;
   const float* ob = o + static_cast<int64_t>(bh) * P_max * D;
@@ -325,7 +347,7 @@ template <int D>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(
     void* __restrict__ out, int out_dtype, const float* __restrict__ m,
     const float* __restrict__ l, const float* __restrict__ o,
-    const int32_t* __restrict__ context_lens, int n_q, int P_max, int partition) {
+    ReduceRows rows) {
   constexpr int DG = D / 4;                           // 16-byte dim groups
   constexpr int PG = 256 / DG;                        // partition groups
   __shared__ float w[kMaxReducePartitions];
@@ -334,10 +356,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wv = t >> 6;
-  const int bh = blockIdx.x;
-  const int b = bh / n_q;
-  const int ctx = context_lens[b];
-  const int np = ctx > 0 ? min((ctx + partition - 1) / partition, P_max) : 0;
+  const int64_t bh = blockIdx.x;
+  const int P_max = rows.P_max;
+  const int np = row_partitions(rows, bh);
   const float* mb = m + static_cast<int64_t>(bh) * P_max;
   const float* lb = l + static_cast<int64_t>(bh) * P_max;
   const float* ob = o + static_cast<int64_t>(bh) * P_max * D;
@@ -446,28 +467,26 @@ hipError_t launch_decode_partition(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_splitk_reduce(void* out, int out_dtype, const float* m, const float* l,
                                 const float* o, const int32_t* context_lens, int B, int n_q,
-                                int d, int P_max, int partition, hipStream_t stream) {
+                                int d, int P_max, int partition, hipStream_t stream, int Q,
+                                const int32_t* query_lens, int ctx_cap) {
   if (P_max > kMaxReducePartitions || (d != 64 && d != 128)) return hipErrorInvalidValue;
-  const int64_t pairs = static_cast<int64_t>(B) * n_q;
+  const ReduceRows rows{context_lens, query_lens, Q, n_q, P_max, partition, ctx_cap};
+  const int64_t n_rows = static_cast<int64_t>(B) * Q * n_q;
   if (P_max <= kWaveReduceMaxPartitions) {
-    const unsigned grid = static_cast<unsigned>((pairs + 3) / 4);
+    const unsigned grid = static_cast<unsigned>((n_rows + 3) / 4);
     if (d == 128)
-      splitk_reduce_wave_kernel<128><<<grid, 256, 0, stream>>>(out, out_dtype, m, l, o,
-                                                               context_lens, B, n_q, P_max,
-                                                               partition);
+      splitk_reduce_wave_kernel<128><<<grid, 256, 0, stream>>>(out, out_dtype, m, l, o, rows,
+                                                               n_rows);
     else
-      splitk_reduce_wave_kernel<64><<<grid, 256, 0, stream>>>(out, out_dtype, m, l, o,
-                                                              context_lens, B, n_q, P_max,
-                                                              partition);
+      splitk_reduce_wave_kernel<64><<<grid, 256, 0, stream>>>(out, out_dtype, m, l, o, rows,
+                                                              n_rows);
     return hipGetLastError();
   }
-  const unsigned grid = static_cast<unsigned>(pairs);
+  const unsigned grid = static_cast<unsigned>(n_rows);
   if (d == 128)
-    splitk_reduce_kernel<128><<<grid, 256, 0, stream>>>(out, out_dtype, m, l, o, context_lens,
-                                                        n_q, P_max, partition);
+    splitk_reduce_kernel<128><<<grid, 256, 0, stream>>>(out, out_dtype, m, l, o, rows);
   else
-    splitk_reduce_kernel<64><<<grid, 256, 0, stream>>>(out, out_dtype, m, l, o, context_lens,
-                                                       n_q, P_max, partition);
+    splitk_reduce_kernel<64><<<grid, 256, 0, stream>>>(out, out_dtype, m, l, o, rows);
   return hipGetLastError();
 }
 

@@ -34,6 +34,10 @@ struct DecodeArgs {
   bool write_partials;        // true: (m, l, o) to workspace; false: out directly
   bool wave_partitions;       // partials mode only: one wave per partition
   const int32_t* schedule;    // optional longest-first work list (see schedule.hip)
+  // several query tokens per sequence (multi-query kernel and reduce only):
+  // q is [B, Q, n_q, d], out and partial rows are (sequence, query, head)
+  int Q;                      // 1 for single-token decode
+  const int32_t* query_lens;  // [B]; nullptr for single-token decode
 };
 
 // Schedule buffer: int32 header of kScheduleHeader words, then int2 items.
@@ -47,7 +51,10 @@ hipError_t launch_decode_partition_mfma(const DecodeArgs& a, hipStream_t stream)
 hipError_t launch_decode_partition_valu(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_splitk_reduce(void* out, int out_dtype, const float* m, const float* l,
                                 const float* o, const int32_t* context_lens, int B, int n_q,
-                                int d, int P_max, int partition, hipStream_t stream);
+                                int d, int P_max, int partition, hipStream_t stream,
+                                int Q = 1, const int32_t* query_lens = nullptr,
+                                int ctx_cap = INT32_MAX);
+hipError_t launch_multi_query_partition(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, int max_blocks,
                                const int32_t* positions, int B, int bs, int64_t* slots,

@@ -7,8 +7,8 @@ the HIP library's tests and the oracle receive the same tensors from it.
 
 Seeds: the structure of workload k = 1..5 (lengths, permutations, prefix
 layout) comes from a CPU torch generator seeded 217000 + k, its values from
-generators seeded 217100 + k (+50 for queries, +90 for new tokens) on the
-device where they are created. Test-only shapes use their own small k.
+generators seeded 217100 + k (+50 for queries, +70 for multi-token
+queries, +90 for new tokens) on the device where they are created. Test-only shapes use their own small k.
 
 FP8 caches are produced from N(0,1) data with one float32 scale per
 (K or V, KV head) equal to absmax / 448; the quotient is clamped to +-448 and
@@ -253,6 +253,12 @@ def make_query(w, device="cpu", seed_offset=0, layers=1):
     g = _gen(VALUE_SEED + 50 + w.notes.get("seed", 0) + seed_offset, device)
     shape = (w.B, w.n_q, w.d) if layers == 1 else (layers, w.B, w.n_q, w.d)
     return _bf16_randn(shape, g, device)
+
+
+def make_multi_query(w, Q, device="cpu", seed_offset=0):
+    """bf16 [B, Q, n_q, d] queries for several new tokens per sequence."""
+    g = _gen(VALUE_SEED + 70 + w.notes.get("seed", 0) + seed_offset, device)
+    return _bf16_randn((w.B, Q, w.n_q, w.d), g, device)
 
 
 def make_new_tokens(w, T=None, device="cpu", seed_offset=0):
