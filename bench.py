@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0          # dense bf16
 METRIC = "paged decode attention: KV GB/s and % of HBM peak; decode tokens/s"
 COUNTERS = os.path.join(ROOT, "profiles", "decode_partition_counters.json")
 KERNEL_SOURCES = ["paged_kv_cache_217_amd/csrc/decode_mfma.hip",
@@ -53,7 +54,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gqa_70b",
-                    choices=["gqa_70b", "mha_7b", "gqa_70b_fp8", "long_prefix", "tiny"])
+                    choices=["gqa_70b", "mha_7b", "gqa_70b_fp8", "long_prefix", "tiny",
+                             "spec_verify_70b", "chunked_prefill_70b"])
     ap.add_argument("--layers", type=int, default=0, help="override layer count (0: workload's)")
     ap.add_argument("--partition", type=int, default=0, help="split-K partition (0: library)")
     ap.add_argument("--schedule", type=int, default=1,
@@ -105,6 +107,9 @@ def main():
         return
 
     w = W.ALL[args.workload]()
+    if w.Q > 1:
+        bench_multi_query(args, w, pkv, W, np, torch, dev)
+        return
     layers = args.layers or w.layers
     B, n_q, n_kv, d, bs = w.B, w.n_q, w.n_kv, w.d, w.bs
     max_ctx = int(w.context_lens.max())
@@ -265,6 +270,124 @@ def main():
     # ---------------------------------------------------------------- oracle on the CPU
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, caches[0], q[0], args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def bench_multi_query(args, w, pkv, W, np, torch, dev):
+    """Several query tokens per sequence: per layer, kv_append of the Q new
+    tokens of every sequence, then causal multi-query paged attention."""
+    layers = args.layers or w.layers
+    B, Q, n_q, n_kv, d, bs = w.B, w.Q, w.n_q, w.n_kv, w.d, w.bs
+    ql = w.query_lens
+    max_ctx = int(w.context_lens.max())
+    log(f"[bench] workload {w.name}: B={B} Q={Q} n_q={n_q} n_kv={n_kv} d={d} bs={bs} "
+        f"layers={layers} tokens={w.total_tokens}")
+    caches = [W.make_cache(w, device=dev, seed_offset=1000 * layer, poison_unused=False)
+              for layer in range(layers)]
+    q = torch.stack([W.make_multi_query(w, Q, device=dev, seed_offset=1000 * layer)
+                     for layer in range(layers)])
+    k_new, v_new = W.make_new_tokens(w, T=layers * B * Q, device=dev)
+    k_new = k_new.view(layers, B * Q, n_kv, d)
+    v_new = v_new.view(layers, B * Q, n_kv, d)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    cl = torch.from_numpy(w.context_lens).to(dev)
+    qld = torch.from_numpy(ql).to(dev)
+    # one table row and one position per new token (padding rows: position -1)
+    pos_np = np.full((B, Q), -1, dtype=np.int32)
+    for b in range(B):
+        pos_np[b, :ql[b]] = w.context_lens[b] - ql[b] + np.arange(ql[b])
+    bt_tok = bt.repeat_interleave(Q, dim=0).contiguous()
+    pos = torch.from_numpy(pos_np.reshape(-1)).to(dev)
+    slots = torch.empty(B * Q, dtype=torch.int64, device=dev)
+    P = args.partition or pkv.multi_query_partition_size(caches[0][0], B, Q, n_q, max_ctx)
+    P_max = max(1, -(-max_ctx // P))
+    nbytes = pkv.lib().pkv_multi_query_workspace_bytes(B, Q, n_q, d, max_ctx, P)
+    ws = torch.empty(max(16, nbytes), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Q, n_q, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"[bench] partition {P} tokens, {P_max} partitions/seq")
+
+    def step(ev=None):
+        pkv.slot_mapping(bt_tok, pos, bs, out=slots)
+        for layer in range(layers):
+            kc, vc, ks, vs = caches[layer]
+            if ev is not None:
+                ev[layer][0].record(stream)
+            pkv.kv_append(kc, vc, k_new[layer], v_new[layer], slots, ks, vs)
+            if ev is not None:
+                ev[layer][1].record(stream)
+            pkv.paged_multi_query_attention(q[layer], qld, kc, vc, bt, cl, w.scale, max_ctx,
+                                            k_scale=ks, v_scale=vs, partition_size=P, out=out,
+                                            workspace=ws)
+            if ev is not None:
+                ev[layer][2].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    log(f"[bench] {args.steps} timed steps: {ms_step:.3f} ms/step")
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(layers)]
+              for _ in range(args.steps)]
+    for s_ in range(args.steps):
+        step(events[s_])
+    torch.cuda.synchronize()
+    t_app = [e[0].elapsed_time(e[1]) for st in events for e in st]
+    t_att = [e[1].elapsed_time(e[2]) for st in events for e in st]
+    avg = lambda x: sum(x) / len(x)
+    ms_att = avg(t_att)
+
+    # algorithmic work of one attention call: every (sequence, KV head) reads its
+    # context's K and V once; each live query row costs 4 d flops per visible token
+    kv_bytes_layer = w.total_tokens * n_kv * d * w.p * 2
+    visible = sum(int(w.context_lens[b]) * int(ql[b]) - int(ql[b]) * (int(ql[b]) - 1) // 2
+                  for b in range(B))
+    flops = 4.0 * d * n_q * visible
+    att_bytes = (kv_bytes_layer + B * Q * n_q * d * (2 + 4)
+                 + sum(-(-int(c) // bs) for c in w.context_lens) * 4)
+    if P_max > 1:
+        att_bytes += 2 * B * Q * n_q * P_max * (d + 2) * 4
+    intensity = flops / att_bytes
+    mfma_bound = intensity > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        achieved = flops / (ms_att * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "multi_query_attention", "achieved": round(achieved, 2),
+                "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "flops_per_launch": flops,
+                "traffic": None}
+    else:
+        achieved = att_bytes / (ms_att * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "multi_query_attention", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "bytes_per_launch": att_bytes, "traffic": None}
+    new_tokens = int(ql.sum())
+    result = {
+        "metric": "multi-query paged attention: query tokens/s, KV GB/s",
+        "value": round(new_tokens / (ms_step * 1e-3), 1),
+        "unit": "query tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "Q": Q, "query_tokens": new_tokens,
+                   "tokens_per_layer": w.total_tokens, "n_q": n_q, "n_kv": n_kv, "d_head": d,
+                   "block_size": bs, "layers": layers, "kv_dtype": w.kv_dtype,
+                   "partition_size": P, "accumulate": "fp32"},
+        "kv_gbs": round(kv_bytes_layer * layers / (ms_step * 1e-3) / 1e9, 2),
+        "attention_tflops": round(flops / (ms_att * 1e-3) / 1e12, 2),
+        "kernels_ms": {"kv_append": round(avg(t_app), 5),
+                       "multi_query_attention": round(ms_att, 5)},
+        "roofline": roof,
+    }
     print(json.dumps(result), flush=True)
 
 

@@ -41,11 +41,16 @@ int32_t pick_partition(const pkv_cache_desc* d, int32_t B, int32_t n_q, int32_t 
       static_cast<int64_t>(B) * d->n_kv * ((G + head_tile(G) - 1) / head_tile(G)), max_ctx);
 }
 
-// Multi-query workgroups each own 16 (query, head) rows of one KV head.
+// Multi-query workgroups each own 16 (query, head) rows of one KV head. A
+// launch whose row tiles alone fill four rounds of the chip runs in a single
+// pass: splitting it would only add partials (fp32, d_head + 2 words per row
+// and partition) that outweigh the K/V a prompt chunk reads.
 int32_t pick_partition_mq(const pkv_cache_desc* d, int32_t B, int32_t Q, int32_t n_q,
                           int32_t max_ctx) {
   const int64_t rows = static_cast<int64_t>(Q) * (n_q / d->n_kv);
-  return pick_partition_units(static_cast<int64_t>(B) * d->n_kv * cdiv(rows, 16), max_ctx);
+  const int64_t units = static_cast<int64_t>(B) * d->n_kv * cdiv(rows, 16);
+  if (units >= 4 * 512) return static_cast<int32_t>(std::max<int64_t>(32, cdiv(max_ctx, 32) * 32));
+  return pick_partition_units(units, max_ctx);
 }
 
 int32_t pick_partition_units(int64_t units, int32_t max_ctx) {

@@ -21,6 +21,7 @@ are never read.
 """
 
 from dataclasses import dataclass, field
+from typing import Optional
 import math
 
 import numpy as np
@@ -50,6 +51,8 @@ class Workload:
     partition_size: int = 0           # 0: the library's default; else fixed by the workload
     shared_prefix_blocks: int = 0
     notes: dict = field(default_factory=dict)
+    Q: int = 1                        # query tokens per sequence (1: single-token decode)
+    query_lens: Optional[np.ndarray] = None   # int32 [B] when Q > 1
 
     @property
     def G(self):
@@ -183,8 +186,34 @@ def long_shared_prefix():
                     notes={"seed": 5, "ref_count": B})
 
 
+def spec_verify_70b(layers=80):
+    """The 70B decode batch verifying 4 draft tokens per sequence: B=64, each
+    context 8192 tokens including the 4 candidates, 64/8 heads, d=128, bs=16."""
+    ctx = np.full(64, 8192, dtype=np.int32)
+    pool = 64 * 512
+    perm = torch.randperm(pool, generator=_gen(STRUCT_SEED + 6)).numpy().astype(np.int32)
+    bt = _tables_from_perm(ctx, 16, perm)
+    return Workload("spec_verify_70b_80_layers", 64, 64, 8, 128, 16, BF16, ctx, bt, pool,
+                    1.0 / math.sqrt(128), layers=layers, notes={"seed": 6}, Q=4,
+                    query_lens=np.full(64, 4, dtype=np.int32))
+
+
+def chunked_prefill_70b(layers=4):
+    """One 512-token prompt chunk per sequence at four depths of a 64K-token
+    prompt (contexts 4096, 16384, 32768, 65536 including the chunk), 64/8
+    heads, d=128, bs=16."""
+    ctx = np.array([4096, 16384, 32768, 65536], dtype=np.int32)
+    need = int(sum(int(c) // 16 for c in ctx))
+    perm = torch.randperm(need, generator=_gen(STRUCT_SEED + 7)).numpy().astype(np.int32)
+    bt = _tables_from_perm(ctx, 16, perm)
+    return Workload("chunked_prefill_70b", 4, 64, 8, 128, 16, BF16, ctx, bt, need,
+                    1.0 / math.sqrt(128), layers=layers, notes={"seed": 7}, Q=512,
+                    query_lens=np.full(4, 512, dtype=np.int32))
+
+
 ALL = {"tiny": tiny, "mha_7b": mha_7b, "gqa_70b": gqa_70b, "gqa_70b_fp8": gqa_70b_fp8,
-       "long_prefix": long_shared_prefix}
+       "long_prefix": long_shared_prefix, "spec_verify_70b": spec_verify_70b,
+       "chunked_prefill_70b": chunked_prefill_70b}
 
 
 # ---------------------------------------------------------------- values
