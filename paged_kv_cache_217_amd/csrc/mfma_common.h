@@ -45,6 +45,34 @@ __device__ __forceinline__ void ld_stream(uint32_t& out, const uint8_t* p) {
   out = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
 }
 
+// Buffer-resource form of the same streaming loads: the (block, head) tile's
+// base and size sit in four scalar registers and each lane adds a 32-bit
+// offset. A resource of size 0 (an absent block) makes every load return
+// zeros without touching memory, so the tail of a chunk needs no branches.
+// Word 3 is the raw (untyped, unswizzled) buffer configuration of CDNA.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kLoadNonTemporal = 2;            // cache-policy bit of the load
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), static_cast<short>(0),
+                                           bytes, kRawBufferWord3);
+}
+// `off` is the per-lane part of the byte offset (one register shared by many
+// loads), `soff` a wave-uniform part (a compile-time constant at every call).
+__device__ __forceinline__ void ld_stream(uint4& out, __amdgpu_buffer_rsrc_t r, uint32_t off,
+                                          int soff) {
+  const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kLoadNonTemporal);
+  out = make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void ld_stream(uint2& out, __amdgpu_buffer_rsrc_t r, uint32_t off,
+                                          int soff) {
+  const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, kLoadNonTemporal);
+  out = make_uint2(x[0], x[1]);
+}
+__device__ __forceinline__ void ld_stream(uint32_t& out, __amdgpu_buffer_rsrc_t r, uint32_t off,
+                                          int soff) {
+  out = __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, kLoadNonTemporal);
+}
+
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }

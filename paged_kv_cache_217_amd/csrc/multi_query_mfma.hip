@@ -23,6 +23,7 @@
 // position are not read at all. Rows that see no token of a partition emit
 // an empty partial (l = 0, o = 0) and the reduce skips them.
 #include <float.h>
+#include <stdlib.h>
 
 #include "mfma_common.h"
 #include "pkv_device.h"
@@ -32,9 +33,16 @@ namespace pkv {
 
 using namespace mfma;
 
-template <int D, int BS, bool FP8, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+// Each wave owns TPW row tiles and applies every K operand and transposed V
+// operand it loads to all of them; R such waves share a workgroup, S waves
+// (chunk streams) per tile set. The R waves of one stream read the same K/V
+// chunk at the same time, so a KV head's context crosses HBM once for all of
+// the group's tiles.
+template <int D, int BS, bool FP8, int TPW, int R, int S>
+__global__ __launch_bounds__(R * S * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void multi_query_partition_mfma(DecodeArgs a) {
+  constexpr int NW = R * S;
+  constexpr int GR = 16 * TPW * R;            // rows per workgroup
   constexpr int CT = FP8 ? 64 : 32;           // tokens per chunk
   constexpr int NRG = CT / 16;                // 16-token row groups per chunk
   constexpr int NKS = CT / 32;                // 32-token PV k-steps per chunk
@@ -54,39 +62,34 @@ void multi_query_partition_mfma(DecodeArgs a) {
   const int c = lane & 15;
   const int g4 = lane >> 4;
 
-  // grid: x = (KV head, row tile), y = sequence, z = partition from the end
+  // grid: x = (KV head, group of GR rows), y = sequence, z = partition from
+  // the end
   const int G = a.n_q / a.n_kv;
   const int rows = a.Q * G;                           // query rows of one KV head
-  const int tiles = (rows + 15) / 16;
-  const int g = blockIdx.x / tiles;
-  const int tile = blockIdx.x % tiles;
+  const int groups = (rows + GR - 1) / GR;
+  const int g = blockIdx.x / groups;
+  const int row0 = (blockIdx.x % groups) * GR;        // first row of the group
   const int b = blockIdx.y;
   const int j = gridDim.z - 1 - blockIdx.z;
   const int ctx = min(a.context_lens[b], a.max_blocks * BS);
   const int ql = max(0, min(min(a.query_lens[b], a.Q), ctx));
-
-  // this lane's row and its position; the tile's position range
-  const int row = tile * 16 + c;
-  const int qi = row / G;
-  const int hq = g * G + row % G;
-  const bool live_row = row < rows && qi < ql;
-  const int pos = ctx - ql + qi;                      // last token this row may see
-  const int i_lo = (tile * 16) / G;
-  const int i_hi = min((tile * 16 + 15) / G, ql - 1);
-  const int p_lo = ctx - ql + i_lo;
-  const int p_hi = ctx - ql + i_hi;
   const int t0 = j * a.partition;
 
-  __shared__ float sm_m[NW][16];
-  __shared__ float sm_l[NW][16];
-  __shared__ float sm_acc[NW][16][D + 4];
+  __shared__ float sm_m[NW][TPW * 16];
+  __shared__ float sm_l[NW][TPW * 16];
+  __shared__ float sm_acc[NW][TPW * 16][D + 4];
 
-  if (i_lo >= ql || t0 > p_hi) {
-    // no row of this tile reads this partition; a single pass still owes the
-    // tile's rows their zeros (rows past q_len, or a sequence with none)
+  // last position of the query among rows [r0, r1) (r1 > r0), or -1 if none
+  auto last_pos = [&](int r0, int r1) -> int {
+    const int i_hi = min((min(r1, rows) - 1) / G, ql - 1);
+    return r0 / G < ql && r0 < rows ? ctx - ql + i_hi : -1;
+  };
+  if (t0 > last_pos(row0, row0 + GR)) {
+    // no row of this group reads this partition; a single pass still owes the
+    // group's rows their zeros (rows past q_len, or a sequence with none)
     if (!a.write_partials && j == 0) {
-      for (int e = threadIdx.x; e < 16 * D; e += blockDim.x) {
-        const int r = tile * 16 + e / D;
+      for (int e = threadIdx.x; e < GR * D; e += blockDim.x) {
+        const int r = row0 + e / D;
         if (r >= rows) continue;
         const int64_t oi =
             ((static_cast<int64_t>(b) * a.Q + r / G) * a.n_q + g * G + r % G) * D + e % D;
@@ -98,23 +101,36 @@ void multi_query_partition_mfma(DecodeArgs a) {
     }
     return;
   }
+
+  // this wave's tiles and chunk stream; this lane's rows and their positions
+  const int tl = wave % R;
+  const int st = wave / R;
+  const int wrow0 = row0 + tl * TPW * 16;             // first row of the wave
+  const int p_lo = ctx - ql + wrow0 / G;              // smallest position of the wave
+  const int p_hi = last_pos(wrow0, wrow0 + TPW * 16); // largest (-1: none)
   const int t1 = min(t0 + a.partition, p_hi + 1);    // tokens past p_hi are never read
   const int blk0 = t0 / BS;
   const int blk1 = (t1 + BS - 1) / BS;
-  const int n_ch = (blk1 - blk0 + BPC - 1) / BPC;
+  const int n_ch = t0 < t1 ? (blk1 - blk0 + BPC - 1) / BPC : 0;
 
   auto dimbase = [&](int kk) -> int {
     return FP8 ? 64 * (kk >> 1) + 16 * g4 + 8 * (kk & 1) : 32 * kk + 8 * g4;
   };
-  bf16x8_t qop[NKK];
-  {
-    const int64_t qrow = live_row ? (static_cast<int64_t>(b) * a.Q + qi) * a.n_q + hq : 0;
-    const uint16_t* qp = a.q + qrow * D;
+  bf16x8_t qop[TPW][NKK];
+  int pos[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int row = wrow0 + 16 * t + c;
+    const int qi = row / G;
+    const bool live_row = row < rows && qi < ql;
+    pos[t] = ctx - ql + qi;                           // last token this row may see
+    const int64_t qrow =
+        live_row ? (static_cast<int64_t>(b) * a.Q + qi) * a.n_q + g * G + row % G : 0;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      uint4 w = *reinterpret_cast<const uint4*>(qp + dimbase(kk));
+      uint4 w = *reinterpret_cast<const uint4*>(a.q + qrow * D + dimbase(kk));
       if (!live_row) w = make_uint4(0, 0, 0, 0);
-      qop[kk] = __builtin_bit_cast(bf16x8_t, w);
+      qop[t][kk] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
   float qscale = a.scale * kLog2e;
@@ -130,137 +146,166 @@ void multi_query_partition_mfma(DecodeArgs a) {
     return 16 * (2 * (s >> 3) + (s8 >> 2)) + 4 * g4 + (s8 & 3);
   };
 
-  struct Chunk {
+  // K and V of a chunk are separate buffers: the next chunk's V is requested
+  // only once this chunk's K has been consumed, so at most three of the four
+  // buffers hold data at any time.
+  struct KChunk {
     uint4 k[NRG][NKL];
+  };
+  struct VChunk {
     VT v[NVS];
   };
 
-  auto load = [&](Chunk& ch, int ci) {
-    const uint8_t* kb[BPC];
-    const uint8_t* vb[BPC];
-    bool have[BPC];
+  // block i of chunk ci as a buffer resource (size 0 when absent: loads give 0)
+  auto rsrc = [&](const uint8_t* cache, int ci, int i) -> __amdgpu_buffer_rsrc_t {
+    const int blk = blk0 + ci * BPC + i;
+    const bool have = blk < blk1;
+    int p = __builtin_amdgcn_readfirstlane(have ? bt[blk] : 0);
+    if (p < 0 || p >= a.num_blocks) p = 0;
+    return tile_rsrc(cache + p * block_stride + head_off, have ? static_cast<int>(tile_bytes) : 0);
+  };
+  const uint32_t k_lane = static_cast<uint32_t>((c * D + (FP8 ? 16 : 8) * g4) * EB);
+  const uint32_t v_lane = static_cast<uint32_t>((4 * g4 * D + DPL * c) * EB);
+  auto load_k = [&](KChunk& kc, int ci) {
+    __amdgpu_buffer_rsrc_t r[BPC];
 #pragma unroll
-    for (int i = 0; i < BPC; ++i) {
-      const int blk = blk0 + ci * BPC + i;
-      have[i] = blk < blk1;
-      int p = have[i] ? bt[blk] : 0;
-      if (p < 0 || p >= a.num_blocks) p = 0;
-      kb[i] = a.k_cache + p * block_stride + head_off;
-      vb[i] = a.v_cache + p * block_stride + head_off;
-    }
+    for (int i = 0; i < BPC; ++i) r[i] = rsrc(a.k_cache, ci, i);
+    // token 16 rg + c of the chunk is row (16 rg) % BS + c of block 16 rg / BS
 #pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) {
-      const int t = 16 * rg + c;
-      const int bi = t / BS;
+    for (int rg = 0; rg < NRG; ++rg)
 #pragma unroll
-      for (int kl = 0; kl < NKL; ++kl) {
-        const int dim = FP8 ? 64 * kl + 16 * g4 : 32 * kl + 8 * g4;
-        if (have[bi])
-          ld_stream(ch.k[rg][kl], kb[bi] + ((t % BS) * D + dim) * EB);
-        else
-          ch.k[rg][kl] = make_uint4(0, 0, 0, 0);
-      }
-    }
+      for (int kl = 0; kl < NKL; ++kl)
+        ld_stream(kc.k[rg][kl], r[16 * rg / BS], k_lane,
+                  (((16 * rg) % BS) * D + (FP8 ? 64 : 32) * kl) * EB);
+  };
+  auto load_v = [&](VChunk& vc, int ci) {
+    __amdgpu_buffer_rsrc_t r[BPC];
+#pragma unroll
+    for (int i = 0; i < BPC; ++i) r[i] = rsrc(a.v_cache, ci, i);
+    // token v_tok(s) = 16 X + 4 g4 + (s & 3), X = 2 (s / 8) + (s % 8) / 4
 #pragma unroll
     for (int s = 0; s < NVS; ++s) {
-      const int t = v_tok(s);
-      const int bi = t / BS;
-      if (have[bi])
-        ld_stream(ch.v[s], vb[bi] + ((t % BS) * D + DPL * c) * EB);
-      else
-        ch.v[s] = VT{};
+      const int X = 2 * (s >> 3) + ((s & 7) >> 2);
+      ld_stream(vc.v[s], r[16 * X / BS], v_lane, (((16 * X) % BS + (s & 3)) * D) * EB);
     }
   };
 
-  float m_ref = -INFINITY;
-  float m_true = -INFINITY;
-  float l = 0.0f;
-  f32x4_t acc[NJ];
+  float m_ref[TPW], m_true[TPW], l[TPW];
+  f32x4_t acc[TPW][NJ];
 #pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) acc[jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < TPW; ++t) {
+    m_ref[t] = -INFINITY;
+    m_true[t] = -INFINITY;
+    l[t] = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) acc[t][jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
-  auto compute = [&](Chunk& ch, int ci) {
+  using Scores = float[TPW][4 * NRG];
+  // scores of chunk ci (base-2 units), masked causally and at the partition end
+  auto qk = [&](const KChunk& kc, int ci, Scores& s) {
     const int tok0 = (blk0 + ci * BPC) * BS;
-    float s[4 * NRG];
 #pragma unroll
     for (int rg = 0; rg < NRG; ++rg) {
-      f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4_t sc[TPW];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) sc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         bf16x8_t kop;
         if constexpr (!FP8) {
-          kop = __builtin_bit_cast(bf16x8_t, ch.k[rg][kk]);
+          kop = __builtin_bit_cast(bf16x8_t, kc.k[rg][kk]);
         } else {
-          const uint4 w = ch.k[rg][kk >> 1];
+          const uint4 w = kc.k[rg][kk >> 1];
           const uint32_t w0 = (kk & 1) ? w.z : w.x;
           const uint32_t w1 = (kk & 1) ? w.w : w.y;
           kop = as_bf16x8(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
                           fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
         }
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sc, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[t][kk], sc[t], 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[4 * rg + i] = sc[i] * qscale;
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[t][4 * rg + i] = sc[t][i] * qscale;
     }
     if (tok0 + CT > min(p_lo + 1, t1)) {
       // causal: each row sees tokens up to its own position, and nothing past
       // the partition's end (such slots were not loaded)
-      const int lim = min(pos + 1, t1);
 #pragma unroll
-      for (int rg = 0; rg < NRG; ++rg)
+      for (int t = 0; t < TPW; ++t) {
+        const int lim = min(pos[t] + 1, t1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (tok0 + 16 * rg + 4 * g4 + i >= lim) s[4 * rg + i] = -INFINITY;
+        for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (tok0 + 16 * rg + 4 * g4 + i >= lim) s[t][4 * rg + i] = -INFINITY;
+      }
     }
+  };
+
+  // online softmax update with the scores of chunk ci, then O += P V
+  auto pv = [&](VChunk& vc, int ci, Scores& s) {
+    const int tok0 = (blk0 + ci * BPC) * BS;
     if (tok0 + CT > t1) {
 #pragma unroll
       for (int si = 0; si < NVS; ++si)
-        if (tok0 + v_tok(si) >= t1) ch.v[si] = VT{};
+        if (tok0 + v_tok(si) >= t1) vc.v[si] = VT{};
     }
-    float mx = s[0];
+    float m_use[TPW];
 #pragma unroll
-    for (int i = 1; i < 4 * NRG; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    m_true = fmaxf(m_true, mx);
-    // a row may see none of a chunk's tokens (all -inf): it keeps its state
-    const bool need = mx > m_ref + kLazyRescale;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float alpha = need ? fast_exp2(m_ref - mx) : 1.0f;
-      if (need) m_ref = mx;
-      l *= alpha;
+    for (int t = 0; t < TPW; ++t) {
+      float mx = s[t][0];
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) acc[jj] *= alpha;
+      for (int i = 1; i < 4 * NRG; ++i) mx = fmaxf(mx, s[t][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      m_true[t] = fmaxf(m_true[t], mx);
+      // a row may see none of a chunk's tokens (all -inf): it keeps its state
+      const bool need = mx > m_ref[t] + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float alpha = need ? fast_exp2(m_ref[t] - mx) : 1.0f;
+        if (need) m_ref[t] = mx;
+        l[t] *= alpha;
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) acc[t][jj] *= alpha;
+      }
+      m_use[t] = m_ref[t] == -INFINITY ? 0.0f : m_ref[t];
     }
-    const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      float p[8];
+      bf16x8_t pop_hi[TPW], pop_lo[TPW];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = fast_exp2(s[8 * ks + i] - m_use);
-        l += p[i];
-      }
-      uint32_t ph[4], pl[4];
+      for (int t = 0; t < TPW; ++t) {
+        float p[8];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        ph[t] = pack_bf16(p[2 * t], p[2 * t + 1]);
-        float h0f, h1f;
-        bf16x2_to_f32(ph[t], h0f, h1f);
-        pl[t] = pack_bf16(p[2 * t] - h0f, p[2 * t + 1] - h1f);
+        for (int i = 0; i < 8; ++i) {
+          p[i] = fast_exp2(s[t][8 * ks + i] - m_use[t]);
+          l[t] += p[i];
+        }
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          ph[u] = pack_bf16(p[2 * u], p[2 * u + 1]);
+          float h0f, h1f;
+          bf16x2_to_f32(ph[u], h0f, h1f);
+          pl[u] = pack_bf16(p[2 * u] - h0f, p[2 * u + 1] - h1f);
+        }
+        pop_hi[t] = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
+        pop_lo[t] = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
       }
-      const bf16x8_t pop_hi = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
-      const bf16x8_t pop_lo = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
       uint32_t vw[8][VW];
 #pragma unroll
       for (int si = 0; si < 8; ++si) {
         if constexpr (!FP8) {
 #pragma unroll
-          for (int w = 0; w < VW; ++w) vw[si][w] = word(ch.v[8 * ks + si], w);
+          for (int w = 0; w < VW; ++w) vw[si][w] = word(vc.v[8 * ks + si], w);
         } else {
 #pragma unroll
           for (int w = 0; w < VW / 2; ++w) {
-            const uint32_t x = word(ch.v[8 * ks + si], w);
+            const uint32_t x = word(vc.v[8 * ks + si], w);
             vw[si][2 * w] = fp8x2_to_bf16x2<false>(x);
             vw[si][2 * w + 1] = fp8x2_to_bf16x2<true>(x);
           }
@@ -272,59 +317,80 @@ void multi_query_partition_mfma(DecodeArgs a) {
         const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
         uint32_t t4[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          t4[t] = __builtin_amdgcn_perm(vw[2 * t + 1][w], vw[2 * t][w], sel);
+        for (int u = 0; u < 4; ++u)
+          t4[u] = __builtin_amdgcn_perm(vw[2 * u + 1][w], vw[2 * u][w], sel);
         const bf16x8_t vop = as_bf16x8(t4[0], t4[1], t4[2], t4[3]);
-        acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi, acc[jj], 0, 0, 0);
-        acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo, acc[jj], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          acc[t][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi[t], acc[t][jj], 0, 0, 0);
+          acc[t][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[t], acc[t][jj], 0, 0, 0);
+        }
       }
     }
   };
 
   {
-    Chunk A, B;
-    int ci = wave;
-    if (ci < n_ch) load(A, ci);
-    for (; ci < n_ch; ci += 2 * NW) {
-      if (ci + NW < n_ch) load(B, ci + NW);
-      compute(A, ci);
-      if (ci + NW >= n_ch) break;
-      if (ci + 2 * NW < n_ch) load(A, ci + 2 * NW);
-      compute(B, ci + NW);
+    KChunk kA, kB;
+    VChunk vA, vB;
+    Scores sc;
+    int ci = st;
+    if (ci < n_ch) {
+      load_k(kA, ci);
+      load_v(vA, ci);
+    }
+    for (; ci < n_ch; ci += 2 * S) {
+      const bool nb = ci + S < n_ch;
+      if (nb) load_k(kB, ci + S);
+      qk(kA, ci, sc);
+      if (nb) load_v(vB, ci + S);
+      pv(vA, ci, sc);
+      if (!nb) break;
+      const bool na = ci + 2 * S < n_ch;
+      if (na) load_k(kA, ci + 2 * S);
+      qk(kB, ci + S, sc);
+      if (na) load_v(vA, ci + 2 * S);
+      pv(vB, ci + S, sc);
     }
   }
 
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  const float f = m_true == -INFINITY ? 0.0f : fast_exp2(m_ref - m_true);
-  l *= f;
-  if (g4 == 0) {
-    sm_m[wave][c] = m_true;
-    sm_l[wave][c] = l;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    float lt = l[t];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const float f = m_true[t] == -INFINITY ? 0.0f : fast_exp2(m_ref[t] - m_true[t]);
+    if (g4 == 0) {
+      sm_m[wave][16 * t + c] = m_true[t];
+      sm_l[wave][16 * t + c] = lt * f;
+    }
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sm_acc[wave][16 * t + c][DPL * (4 * g4 + i) + jj] = acc[t][jj][i] * f;
   }
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm_acc[wave][c][DPL * (4 * g4 + i) + jj] = acc[jj][i] * f;
   __syncthreads();
 
   const float vscale = FP8 ? a.v_scale[g] : 1.0f;
-  for (int e = threadIdx.x; e < 16 * D; e += blockDim.x) {
-    const int r = e / D;                               // tile row
+  for (int e = threadIdx.x; e < GR * D; e += blockDim.x) {
+    const int r = e / D;                               // group row
     const int dd = e % D;
-    const int rr = tile * 16 + r;
+    const int rr = row0 + r;
     if (rr >= rows) continue;
     const int ri = rr / G;
     const int64_t orow = (static_cast<int64_t>(b) * a.Q + ri) * a.n_q + g * G + rr % G;
+    const int rt = r / (16 * TPW);                     // its waves: rt + R * s
+    const int rc = r % (16 * TPW);
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][r]);
+    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, sm_m[rt + R * s2][rc]);
     float L = 0.0f, O = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float fw = sm_m[w][r] == -INFINITY ? 0.0f : fast_exp2(sm_m[w][r] - M);
-      L = fmaf(sm_l[w][r], fw, L);
-      O = fmaf(sm_acc[w][r][dd], fw, O);
+    for (int s2 = 0; s2 < S; ++s2) {
+      const int w = rt + R * s2;
+      const float fw = sm_m[w][rc] == -INFINITY ? 0.0f : fast_exp2(sm_m[w][rc] - M);
+      L = fmaf(sm_l[w][rc], fw, L);
+      O = fmaf(sm_acc[w][rc][dd], fw, O);
     }
     const bool live = ri < ql;
     const float o = live && L > 0.0f ? O / L * vscale : 0.0f;
@@ -345,27 +411,51 @@ void multi_query_partition_mfma(DecodeArgs a) {
   }
 }
 
-constexpr int kMqWaves = 4;
+// Row tiles per wave, waves per tile set and waves per set, for a launch of
+// `tiles` row tiles per KV head; PKV_MQ_GROUP="TRS" (e.g. "214") overrides it
+// (for measurement).
+struct Group {
+  int TPW, R, S;
+};
+
+static Group pick_group(int tiles) {
+  static const int forced = [] {
+    const char* e = getenv("PKV_MQ_GROUP");
+    return e && e[0] && e[1] && e[2] ? (e[0] - '0') * 100 + (e[1] - '0') * 10 + (e[2] - '0')
+                                     : 0;
+  }();
+  if (forced == 114 || forced == 124 || forced == 214) return {forced / 100, forced / 10 % 10, forced % 10};
+  return tiles >= 2 ? Group{2, 1, 4} : Group{1, 1, 4};
+}
+
+template <int D, int BS, bool FP8, int TPW, int R, int S>
+static hipError_t launch_g(const DecodeArgs& a, int tiles, hipStream_t s) {
+  constexpr int tpg = TPW * R;
+  const dim3 grid(a.n_kv * ((tiles + tpg - 1) / tpg), a.B, a.P_max);
+  multi_query_partition_mfma<D, BS, FP8, TPW, R, S><<<grid, R * S * 64, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 template <int D, int BS, bool FP8>
-static hipError_t launch_mq(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  multi_query_partition_mfma<D, BS, FP8, kMqWaves><<<grid, kMqWaves * 64, 0, s>>>(a);
-  return hipGetLastError();
+static hipError_t launch_mq(const DecodeArgs& a, int tiles, hipStream_t s) {
+  const Group gr = pick_group(tiles);
+  if (gr.TPW == 2) return launch_g<D, BS, FP8, 2, 1, 4>(a, tiles, s);
+  if (gr.R == 2) return launch_g<D, BS, FP8, 1, 2, 4>(a, tiles, s);
+  return launch_g<D, BS, FP8, 1, 1, 4>(a, tiles, s);
 }
 
 hipError_t launch_multi_query_partition(const DecodeArgs& a, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
   const int tiles = (a.Q * G + 15) / 16;
-  const dim3 grid(a.n_kv * tiles, a.B, a.P_max);
   const bool fp8 = a.kv_dtype == PKV_FP8_E4M3;
   if (a.d == 128) {
-    if (a.bs == 16) return fp8 ? launch_mq<128, 16, true>(a, grid, s)
-                               : launch_mq<128, 16, false>(a, grid, s);
-    return fp8 ? launch_mq<128, 32, true>(a, grid, s) : launch_mq<128, 32, false>(a, grid, s);
+    if (a.bs == 16) return fp8 ? launch_mq<128, 16, true>(a, tiles, s)
+                               : launch_mq<128, 16, false>(a, tiles, s);
+    return fp8 ? launch_mq<128, 32, true>(a, tiles, s) : launch_mq<128, 32, false>(a, tiles, s);
   }
-  if (a.bs == 16) return fp8 ? launch_mq<64, 16, true>(a, grid, s)
-                             : launch_mq<64, 16, false>(a, grid, s);
-  return fp8 ? launch_mq<64, 32, true>(a, grid, s) : launch_mq<64, 32, false>(a, grid, s);
+  if (a.bs == 16) return fp8 ? launch_mq<64, 16, true>(a, tiles, s)
+                             : launch_mq<64, 16, false>(a, tiles, s);
+  return fp8 ? launch_mq<64, 32, true>(a, tiles, s) : launch_mq<64, 32, false>(a, tiles, s);
 }
 
 }  // namespace pkv
