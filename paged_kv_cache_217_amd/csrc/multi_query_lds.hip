@@ -1,0 +1,390 @@
+// Paged multi-query attention for many query rows per KV head (a prompt
+// chunk: [LLMI] "LLM inference: prefill, decode, KV cache"
+// (systemcraft.online), "4. Internal workings" and "9. Failure modes and
+// limitations"), on the gfx950 matrix cores with the K/V chunk shared
+// through LDS.
+//
+// Same arithmetic and outputs as multi_query_mfma.hip (query i of sequence b
+// at position ctx - q_len + i attends causally to tokens 0..p through the
+// block table; [MTKV] "Architecting Multi-Tier Disaggregated KV-Cache
+// Hierarchies for Terabyte-Scale LLM Inference", "High-Throughput Paged
+// Attention Kernel Integration"). There a wave streams K/V from HBM into its
+// own registers, which suits a few rows per KV head. A 512-token chunk with
+// 8 query heads per KV head has 4096 rows per KV head; each K/V byte then
+// feeds thousands of rows and the work is a dense contraction, so here:
+//  - a workgroup owns 128 rows (4 waves x 2 tiles of 16) of one KV head and
+//    walks the context in chunks; each chunk is fetched once by the whole
+//    workgroup (a wave fetches one 1 KiB slice of one (block, head) tile per
+//    load) into an LDS double buffer and every wave reads it from there;
+//  - LDS rows are XOR-swizzled in 16-byte columns so that the 16 lanes that
+//    read one K column of 16 different tokens hit 16 different banks;
+//  - each wave keeps its rows' softmax state and output in registers for the
+//    whole context, so there is no merge between waves;
+//  - the row groups of one (sequence, KV head) run on one XCD (blocks are
+//    handed to the 8 XCDs round-robin), so the K/V they all read is fetched
+//    into that XCD's L2 once.
+#include <float.h>
+
+#include "mfma_common.h"
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+using namespace mfma;
+
+template <int D, int BS, bool FP8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void multi_query_lds_mfma(DecodeArgs a) {
+  constexpr int NW = 4;                       // waves
+  constexpr int TPW = 2;                      // 16-row tiles per wave
+  constexpr int GR = NW * TPW * 16;           // rows per workgroup
+  constexpr int CT = FP8 ? 64 : 32;           // tokens per chunk
+  constexpr int NRG = CT / 16;                // 16-token row groups per chunk
+  constexpr int NKS = CT / 32;                // 32-token PV k-steps per chunk
+  constexpr int NKK = D / 32;                 // QK MFMA steps over d
+  constexpr int NJ = D / 16;                  // PV MFMAs per k-step
+  constexpr int DPL = D / 16;                 // dims per lane per V row
+  constexpr int EB = FP8 ? 1 : 2;             // bytes per element
+  constexpr int VB = DPL * EB;                // bytes of one lane's V slice
+  using VT = typename Vec<VB>::T;
+  constexpr int VW = (DPL * 2) / 4;           // bf16 words per V slice
+  constexpr int RB = D * EB;                  // bytes per token row
+  constexpr int NCOL = RB / 16;               // 16-byte columns per row
+  constexpr int CB = CT * RB;                 // bytes of K (or V) per chunk
+  constexpr int TB = BS * RB;                 // bytes of one (block, head) tile
+  constexpr int PIECES = CB / (16 * 256);     // 16-byte pieces per thread
+  static_assert(PIECES >= 1 && CB % (16 * 256) == 0, "chunk must split into thread pieces");
+  static_assert(TB % 1024 == 0, "a wave's 1 KiB slice must lie in one tile");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15;
+  const int g4 = lane >> 4;
+
+  // grid: x = (KV head, group of GR rows), y = sequence, z = partition from
+  // the end. Consecutive blocks go to different XCDs; when the x extent is a
+  // multiple of 8 the index is permuted so that an XCD receives consecutive
+  // work items, i.e. the row groups of one KV head.
+  const int G = a.n_q / a.n_kv;
+  const int rows = a.Q * G;
+  const int groups = (rows + GR - 1) / GR;
+  int wid = blockIdx.x;
+  if (gridDim.x % 8 == 0) wid = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  const int g = wid / groups;
+  const int row0 = (wid % groups) * GR;
+  const int b = blockIdx.y;
+  const int j = gridDim.z - 1 - blockIdx.z;
+  const int ctx = min(a.context_lens[b], a.max_blocks * BS);
+  const int ql = max(0, min(min(a.query_lens[b], a.Q), ctx));
+  const int t0 = j * a.partition;
+
+  // last position among rows [r0, r1), or -1 if none of them has a query
+  auto last_pos = [&](int r0, int r1) -> int {
+    const int i_hi = min((min(r1, rows) - 1) / G, ql - 1);
+    return r0 / G < ql && r0 < rows ? ctx - ql + i_hi : -1;
+  };
+  const int p_grp = last_pos(row0, row0 + GR);
+  if (t0 > p_grp) {
+    // no row of this group reads this partition; a single pass still owes the
+    // group's rows their zeros
+    if (!a.write_partials && j == 0) {
+      for (int e = threadIdx.x; e < GR * D; e += blockDim.x) {
+        const int r = row0 + e / D;
+        if (r >= rows) continue;
+        const int64_t oi =
+            ((static_cast<int64_t>(b) * a.Q + r / G) * a.n_q + g * G + r % G) * D + e % D;
+        if (a.out_dtype == PKV_FP32)
+          static_cast<float*>(a.out)[oi] = 0.0f;
+        else
+          static_cast<uint16_t*>(a.out)[oi] = 0;
+      }
+    }
+    return;
+  }
+  const int t1 = min(t0 + a.partition, p_grp + 1);   // tokens past the group's last are not read
+  const int blk0 = t0 / BS;
+  const int blk1 = (t1 + BS - 1) / BS;
+  const int n_ch = (t1 - t0 + CT - 1) / CT;
+
+  // this wave's rows
+  const int wrow0 = row0 + wave * TPW * 16;
+  const int p_lo = ctx - ql + wrow0 / G;
+  auto dimbase = [&](int kk) -> int {
+    return FP8 ? 64 * (kk >> 1) + 16 * g4 + 8 * (kk & 1) : 32 * kk + 8 * g4;
+  };
+  bf16x8_t qop[TPW][NKK];
+  int pos[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int row = wrow0 + 16 * t + c;
+    const int qi = row / G;
+    const bool live_row = row < rows && qi < ql;
+    pos[t] = ctx - ql + qi;
+    const int64_t qrow =
+        live_row ? (static_cast<int64_t>(b) * a.Q + qi) * a.n_q + g * G + row % G : 0;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      uint4 w = *reinterpret_cast<const uint4*>(a.q + qrow * D + dimbase(kk));
+      if (!live_row) w = make_uint4(0, 0, 0, 0);
+      qop[t][kk] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+  float qscale = a.scale * kLog2e;
+  if constexpr (FP8) qscale *= a.k_scale[g];
+
+  __shared__ __align__(16) uint8_t sk[2][CB];
+  __shared__ __align__(16) uint8_t sv[2][CB];
+
+  // byte of (token t, byte x of its row) in a swizzled LDS chunk
+  auto lds_at = [](int t, int x) -> int {
+    return t * RB + (((x >> 4) ^ (t % NCOL)) << 4) + (x & 15);
+  };
+
+  // chunk ci into registers: piece e = threadIdx + 256 k is bytes
+  // [16 e, 16 e + 16) of the chunk; a wave's 64 pieces lie in one tile
+  const int64_t tile_bytes = TB;
+  const int64_t head_off = static_cast<int64_t>(g) * tile_bytes;
+  const int64_t block_stride = static_cast<int64_t>(a.n_kv) * tile_bytes;
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
+  uint4 stage_k[PIECES], stage_v[PIECES];
+  auto fetch = [&](int ci) {
+#pragma unroll
+    for (int k = 0; k < PIECES; ++k) {
+      const int wbyte = (256 * k + 64 * wave) * 16;   // first byte of the wave's slice
+      const int blk = blk0 + ci * (CT / BS) + wbyte / TB;
+      const bool have = blk < blk1;
+      int p = __builtin_amdgcn_readfirstlane(have ? bt[blk] : 0);
+      if (p < 0 || p >= a.num_blocks) p = 0;
+      const int bytes = have ? TB : 0;                // absent: loads give 0
+      const uint32_t off = static_cast<uint32_t>(wbyte % TB + 16 * lane);
+      ld_stream(stage_k[k], tile_rsrc(a.k_cache + p * block_stride + head_off, bytes), off, 0);
+      ld_stream(stage_v[k], tile_rsrc(a.v_cache + p * block_stride + head_off, bytes), off, 0);
+    }
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < PIECES; ++k) {
+      const int e = threadIdx.x + 256 * k;
+      const int t = (16 * e) / RB;
+      const int at = lds_at(t, (16 * e) % RB);
+      *reinterpret_cast<uint4*>(&sk[buf][at]) = stage_k[k];
+      *reinterpret_cast<uint4*>(&sv[buf][at]) = stage_v[k];
+    }
+  };
+
+  auto v_tok = [&](int s) -> int {
+    const int s8 = s & 7;
+    return 16 * (2 * (s >> 3) + (s8 >> 2)) + 4 * g4 + (s8 & 3);
+  };
+
+  float m_ref[TPW], m_true[TPW], l[TPW];
+  f32x4_t acc[TPW][NJ];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    m_ref[t] = -INFINITY;
+    m_true[t] = -INFINITY;
+    l[t] = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) acc[t][jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  auto compute = [&](int buf, int ci) {
+    const uint8_t* kl_ = sk[buf];
+    const uint8_t* vl_ = sv[buf];
+    const int tok0 = t0 + ci * CT;
+    float s[TPW][4 * NRG];
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg) {
+      f32x4_t sc[TPW];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) sc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      const int tk = 16 * rg + c;                    // this lane's K token
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        bf16x8_t kop;
+        if constexpr (!FP8) {
+          kop = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const uint4*>(kl_ + lds_at(tk, 2 * dimbase(kk))));
+        } else {
+          // 16 FP8 codes at dims 64 (kk / 2) + 16 g4, of which this step uses 8
+          const uint4 w = *reinterpret_cast<const uint4*>(
+              kl_ + lds_at(tk, 64 * (kk >> 1) + 16 * g4));
+          const uint32_t w0 = (kk & 1) ? w.z : w.x;
+          const uint32_t w1 = (kk & 1) ? w.w : w.y;
+          kop = as_bf16x8(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                          fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
+        }
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[t][kk], sc[t], 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[t][4 * rg + i] = sc[t][i] * qscale;
+    }
+    if (tok0 + CT > min(p_lo + 1, t1)) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int lim = min(pos[t] + 1, t1);
+#pragma unroll
+        for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (tok0 + 16 * rg + 4 * g4 + i >= lim) s[t][4 * rg + i] = -INFINITY;
+      }
+    }
+    float m_use[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      float mx = s[t][0];
+#pragma unroll
+      for (int i = 1; i < 4 * NRG; ++i) mx = fmaxf(mx, s[t][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      m_true[t] = fmaxf(m_true[t], mx);
+      const bool need = mx > m_ref[t] + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float alpha = need ? fast_exp2(m_ref[t] - mx) : 1.0f;
+        if (need) m_ref[t] = mx;
+        l[t] *= alpha;
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) acc[t][jj] *= alpha;
+      }
+      m_use[t] = m_ref[t] == -INFINITY ? 0.0f : m_ref[t];
+    }
+    const bool tail = tok0 + CT > t1;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8_t pop_hi[TPW], pop_lo[TPW];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p[i] = fast_exp2(s[t][8 * ks + i] - m_use[t]);
+          l[t] += p[i];
+        }
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          ph[u] = pack_bf16(p[2 * u], p[2 * u + 1]);
+          float h0f, h1f;
+          bf16x2_to_f32(ph[u], h0f, h1f);
+          pl[u] = pack_bf16(p[2 * u] - h0f, p[2 * u + 1] - h1f);
+        }
+        pop_hi[t] = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
+        pop_lo[t] = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
+      }
+      uint32_t vw[8][VW];
+#pragma unroll
+      for (int si = 0; si < 8; ++si) {
+        const int tv = v_tok(8 * ks + si);
+        VT v = *reinterpret_cast<const VT*>(vl_ + lds_at(tv, VB * c));
+        if (tail && tok0 + tv >= t1) v = VT{};        // slots past the end may hold NaN
+        if constexpr (!FP8) {
+#pragma unroll
+          for (int w = 0; w < VW; ++w) vw[si][w] = word(v, w);
+        } else {
+#pragma unroll
+          for (int w = 0; w < VW / 2; ++w) {
+            const uint32_t x = word(v, w);
+            vw[si][2 * w] = fp8x2_to_bf16x2<false>(x);
+            vw[si][2 * w + 1] = fp8x2_to_bf16x2<true>(x);
+          }
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        const int w = jj >> 1;
+        const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t t4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          t4[u] = __builtin_amdgcn_perm(vw[2 * u + 1][w], vw[2 * u][w], sel);
+        const bf16x8_t vop = as_bf16x8(t4[0], t4[1], t4[2], t4[3]);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          acc[t][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi[t], acc[t][jj], 0, 0, 0);
+          acc[t][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[t], acc[t][jj], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // double-buffered walk: chunk ci + 1 is in flight while chunk ci is used
+  fetch(0);
+  commit(0);
+  __syncthreads();
+  for (int ci = 0; ci < n_ch; ++ci) {
+    const int buf = ci & 1;
+    if (ci + 1 < n_ch) fetch(ci + 1);
+    compute(buf, ci);
+    if (ci + 1 < n_ch) commit(buf ^ 1);              // the other buffer was last read at ci - 1
+    __syncthreads();
+  }
+
+  // outputs: lane (c, g4) holds dims DPL (4 g4 + i) + jj of row 16 t + c
+  const float vscale = FP8 ? a.v_scale[g] : 1.0f;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    float lt = l[t];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const float f = m_true[t] == -INFINITY ? 0.0f : fast_exp2(m_ref[t] - m_true[t]);
+    const float L = lt * f;
+    const int rr = wrow0 + 16 * t + c;
+    if (rr >= rows) continue;
+    const int ri = rr / G;
+    const bool live = ri < ql;
+    const int64_t orow = (static_cast<int64_t>(b) * a.Q + ri) * a.n_q + g * G + rr % G;
+    const float inv = live && L > 0.0f ? f * vscale / L : 0.0f;
+    if (a.write_partials) {
+      const int64_t mi = orow * a.P_max + j;
+      if (g4 == 0) {
+        a.ws_m[mi] = m_true[t];
+        a.ws_l[mi] = live ? L : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+          a.ws_o[mi * D + DPL * (4 * g4 + i) + jj] = acc[t][jj][i] * inv;
+    } else if (a.out_dtype == PKV_FP32) {
+      float* o = static_cast<float*>(a.out) + orow * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) o[DPL * (4 * g4 + i) + jj] = acc[t][jj][i] * inv;
+    } else {
+      uint16_t* o = static_cast<uint16_t*>(a.out) + orow * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+          o[DPL * (4 * g4 + i) + jj] = f32_to_bf16_rne(acc[t][jj][i] * inv);
+    }
+  }
+}
+
+template <int D, int BS, bool FP8>
+static hipError_t launch_lds(const DecodeArgs& a, hipStream_t s) {
+  const int G = a.n_q / a.n_kv;
+  const int groups = (a.Q * G + 127) / 128;
+  const dim3 grid(a.n_kv * groups, a.B, a.P_max);
+  multi_query_lds_mfma<D, BS, FP8><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_multi_query_lds(const DecodeArgs& a, hipStream_t s) {
+  const bool fp8 = a.kv_dtype == PKV_FP8_E4M3;
+  if (a.d == 128) {
+    if (a.bs == 16) return fp8 ? launch_lds<128, 16, true>(a, s) : launch_lds<128, 16, false>(a, s);
+    return fp8 ? launch_lds<128, 32, true>(a, s) : launch_lds<128, 32, false>(a, s);
+  }
+  if (a.bs == 16) return fp8 ? launch_lds<64, 16, true>(a, s) : launch_lds<64, 16, false>(a, s);
+  return fp8 ? launch_lds<64, 32, true>(a, s) : launch_lds<64, 32, false>(a, s);
+}
+
+}  // namespace pkv

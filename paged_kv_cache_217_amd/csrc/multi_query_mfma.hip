@@ -444,9 +444,22 @@ static hipError_t launch_mq(const DecodeArgs& a, int tiles, hipStream_t s) {
   return launch_g<D, BS, FP8, 1, 1, 4>(a, tiles, s);
 }
 
+// Many rows per KV head (128 or more) share each K/V chunk through LDS
+// (multi_query_lds.hip); fewer stream it into registers here.
+// PKV_MQ_KERNEL=reg / lds forces one of the two (for measurement).
+static int forced_mq_kernel() {
+  static const int v = [] {
+    const char* e = getenv("PKV_MQ_KERNEL");
+    return e ? (e[0] == 'l' ? 2 : e[0] == 'r' ? 1 : 0) : 0;
+  }();
+  return v;
+}
+
 hipError_t launch_multi_query_partition(const DecodeArgs& a, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
   const int tiles = (a.Q * G + 15) / 16;
+  const int forced = forced_mq_kernel();
+  if (forced == 2 || (forced == 0 && tiles >= 8)) return launch_multi_query_lds(a, s);
   const bool fp8 = a.kv_dtype == PKV_FP8_E4M3;
   if (a.d == 128) {
     if (a.bs == 16) return fp8 ? launch_mq<128, 16, true>(a, tiles, s)

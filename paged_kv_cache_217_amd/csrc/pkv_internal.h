@@ -55,6 +55,7 @@ hipError_t launch_splitk_reduce(void* out, int out_dtype, const float* m, const 
                                 int Q = 1, const int32_t* query_lens = nullptr,
                                 int ctx_cap = INT32_MAX);
 hipError_t launch_multi_query_partition(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_multi_query_lds(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, int max_blocks,
                                const int32_t* positions, int B, int bs, int64_t* slots,

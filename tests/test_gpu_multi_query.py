@@ -73,6 +73,11 @@ CASES = [
     ([40, 97, 600], [3, 4, 5], 5, 64, 8, 128, 32, W.FP8, 64),
     ([1, 2, 31, 32, 33], [1, 2, 9, 16, 33], 33, 8, 4, 64, 16, W.FP8, 32),
     ([513, 66], [2, 66], 66, 16, 16, 128, 16, W.FP8, 512),
+    # 128 or more rows per KV head: the LDS-shared kernel
+    ([300, 1025], [40, 200], 200, 16, 2, 128, 32, W.FP8, 0),
+    ([300, 1025], [40, 200], 200, 16, 2, 128, 32, W.FP8, 256),
+    ([77, 640, 5], [77, 130, 5], 130, 8, 2, 64, 16, W.BF16, 0),
+    ([77, 640, 5], [77, 130, 5], 130, 8, 2, 64, 16, W.FP8, 96),
 ]
 
 
