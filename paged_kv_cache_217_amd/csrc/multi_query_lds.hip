@@ -16,8 +16,9 @@
 //    walks the context in chunks; each chunk is fetched once by the whole
 //    workgroup (a wave fetches one 1 KiB slice of one (block, head) tile per
 //    load) into an LDS double buffer and every wave reads it from there;
-//  - LDS rows are XOR-swizzled in 16-byte columns so that the 16 lanes that
-//    read one K column of 16 different tokens hit 16 different banks;
+//  - LDS rows are padded by 16 bytes, so the 16 lanes that read the same
+//    16-byte column of 16 consecutive tokens hit 16 different 4-bank groups,
+//    and every LDS address is one per-lane register plus an immediate;
 //  - each wave keeps its rows' softmax state and output in registers for the
 //    whole context, so there is no merge between waves;
 //  - the row groups of one (sequence, KV head) run on one XCD (blocks are
@@ -50,8 +51,9 @@ void multi_query_lds_mfma(DecodeArgs a) {
   using VT = typename Vec<VB>::T;
   constexpr int VW = (DPL * 2) / 4;           // bf16 words per V slice
   constexpr int RB = D * EB;                  // bytes per token row
-  constexpr int NCOL = RB / 16;               // 16-byte columns per row
+  constexpr int LR = RB + 16;                 // padded LDS row
   constexpr int CB = CT * RB;                 // bytes of K (or V) per chunk
+  constexpr int LB = CT * LR;                 // LDS bytes of K (or V) per chunk
   constexpr int TB = BS * RB;                 // bytes of one (block, head) tile
   constexpr int PIECES = CB / (16 * 256);     // 16-byte pieces per thread
   static_assert(PIECES >= 1 && CB % (16 * 256) == 0, "chunk must split into thread pieces");
@@ -133,13 +135,8 @@ void multi_query_lds_mfma(DecodeArgs a) {
   float qscale = a.scale * kLog2e;
   if constexpr (FP8) qscale *= a.k_scale[g];
 
-  __shared__ __align__(16) uint8_t sk[2][CB];
-  __shared__ __align__(16) uint8_t sv[2][CB];
-
-  // byte of (token t, byte x of its row) in a swizzled LDS chunk
-  auto lds_at = [](int t, int x) -> int {
-    return t * RB + (((x >> 4) ^ (t % NCOL)) << 4) + (x & 15);
-  };
+  __shared__ __align__(16) uint8_t sk[4][LB];
+  __shared__ __align__(16) uint8_t sv[4][LB];
 
   // chunk ci into registers: piece e = threadIdx + 256 k is bytes
   // [16 e, 16 e + 16) of the chunk; a wave's 64 pieces lie in one tile
@@ -147,8 +144,12 @@ void multi_query_lds_mfma(DecodeArgs a) {
   const int64_t head_off = static_cast<int64_t>(g) * tile_bytes;
   const int64_t block_stride = static_cast<int64_t>(a.n_kv) * tile_bytes;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
-  uint4 stage_k[PIECES], stage_v[PIECES];
-  auto fetch = [&](int ci) {
+  // two register stage sets, filled together at the top of a step that
+  // computes two chunks: a load has two chunks of compute to land
+  struct Stage {
+    uint4 k[PIECES], v[PIECES];
+  };
+  auto fetch = [&](Stage& st, int ci) {
 #pragma unroll
     for (int k = 0; k < PIECES; ++k) {
       const int wbyte = (256 * k + 64 * wave) * 16;   // first byte of the wave's slice
@@ -158,18 +159,17 @@ void multi_query_lds_mfma(DecodeArgs a) {
       if (p < 0 || p >= a.num_blocks) p = 0;
       const int bytes = have ? TB : 0;                // absent: loads give 0
       const uint32_t off = static_cast<uint32_t>(wbyte % TB + 16 * lane);
-      ld_stream(stage_k[k], tile_rsrc(a.k_cache + p * block_stride + head_off, bytes), off, 0);
-      ld_stream(stage_v[k], tile_rsrc(a.v_cache + p * block_stride + head_off, bytes), off, 0);
+      ld_stream(st.k[k], tile_rsrc(a.k_cache + p * block_stride + head_off, bytes), off, 0);
+      ld_stream(st.v[k], tile_rsrc(a.v_cache + p * block_stride + head_off, bytes), off, 0);
     }
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int k = 0; k < PIECES; ++k) {
       const int e = threadIdx.x + 256 * k;
-      const int t = (16 * e) / RB;
-      const int at = lds_at(t, (16 * e) % RB);
-      *reinterpret_cast<uint4*>(&sk[buf][at]) = stage_k[k];
-      *reinterpret_cast<uint4*>(&sv[buf][at]) = stage_v[k];
+      const int at = (16 * e) / RB * LR + (16 * e) % RB;
+      *reinterpret_cast<uint4*>(&sk[buf][at]) = st.k[k];
+      *reinterpret_cast<uint4*>(&sv[buf][at]) = st.v[k];
     }
   };
 
@@ -189,27 +189,33 @@ void multi_query_lds_mfma(DecodeArgs a) {
     for (int jj = 0; jj < NJ; ++jj) acc[t][jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
+  // per-lane LDS offsets: K token c at dims of lane group g4; V token 4 g4 at
+  // dims VB c / EB
+  const int k_lane = c * LR + 16 * g4;
+  const int v_lane = 4 * g4 * LR + VB * c;
   auto compute = [&](int buf, int ci) {
     const uint8_t* kl_ = sk[buf];
     const uint8_t* vl_ = sv[buf];
     const int tok0 = t0 + ci * CT;
     float s[TPW][4 * NRG];
+    // K Q^T for every (row group, tile): kk outermost so that the NRG x TPW
+    // accumulation chains interleave
+    f32x4_t sc[NRG][TPW];
 #pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) {
-      f32x4_t sc[TPW];
+    for (int rg = 0; rg < NRG; ++rg)
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) sc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      const int tk = 16 * rg + c;                    // this lane's K token
+      for (int t = 0; t < TPW; ++t) sc[rg][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
+    for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+      for (int rg = 0; rg < NRG; ++rg) {
+        const uint8_t* kt = kl_ + k_lane + 16 * rg * LR;   // this lane's K token 16 rg + c
         bf16x8_t kop;
         if constexpr (!FP8) {
-          kop = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const uint4*>(kl_ + lds_at(tk, 2 * dimbase(kk))));
+          kop = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kt + 64 * kk));
         } else {
           // 16 FP8 codes at dims 64 (kk / 2) + 16 g4, of which this step uses 8
-          const uint4 w = *reinterpret_cast<const uint4*>(
-              kl_ + lds_at(tk, 64 * (kk >> 1) + 16 * g4));
+          const uint4 w = *reinterpret_cast<const uint4*>(kt + 64 * (kk >> 1));
           const uint32_t w0 = (kk & 1) ? w.z : w.x;
           const uint32_t w1 = (kk & 1) ? w.w : w.y;
           kop = as_bf16x8(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
@@ -217,13 +223,15 @@ void multi_query_lds_mfma(DecodeArgs a) {
         }
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
-          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[t][kk], sc[t], 0, 0, 0);
+          sc[rg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[t][kk], sc[rg][t], 0, 0, 0);
       }
+    }
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg)
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[t][4 * rg + i] = sc[t][i] * qscale;
-    }
+        for (int i = 0; i < 4; ++i) s[t][4 * rg + i] = sc[rg][t][i] * qscale;
     if (tok0 + CT > min(p_lo + 1, t1)) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
@@ -281,7 +289,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
 #pragma unroll
       for (int si = 0; si < 8; ++si) {
         const int tv = v_tok(8 * ks + si);
-        VT v = *reinterpret_cast<const VT*>(vl_ + lds_at(tv, VB * c));
+        VT v = *reinterpret_cast<const VT*>(vl_ + v_lane + (tv - 4 * g4) * LR);
         if (tail && tok0 + tv >= t1) v = VT{};        // slots past the end may hold NaN
         if constexpr (!FP8) {
 #pragma unroll
@@ -313,16 +321,27 @@ void multi_query_lds_mfma(DecodeArgs a) {
     }
   };
 
-  // double-buffered walk: chunk ci + 1 is in flight while chunk ci is used
-  fetch(0);
-  commit(0);
-  __syncthreads();
-  for (int ci = 0; ci < n_ch; ++ci) {
-    const int buf = ci & 1;
-    if (ci + 1 < n_ch) fetch(ci + 1);
-    compute(buf, ci);
-    if (ci + 1 < n_ch) commit(buf ^ 1);              // the other buffer was last read at ci - 1
+  // walk in steps of two chunks: LDS buffers 2h, 2h + 1 (h = step % 2) hold
+  // chunks ci, ci + 1 while ci + 2, ci + 3 arrive in the stage registers and
+  // are then written to the other pair, which was last read in the previous
+  // step, before the barrier that ended it
+  {
+    Stage sa, sb;
+    fetch(sa, 0);
+    if (n_ch > 1) fetch(sb, 1);
+    commit(sa, 0);
+    if (n_ch > 1) commit(sb, 1);
     __syncthreads();
+    for (int ci = 0, h = 0; ci < n_ch; ci += 2, h ^= 1) {
+      const bool more = ci + 2 < n_ch;
+      if (more) fetch(sa, ci + 2);
+      if (ci + 3 < n_ch) fetch(sb, ci + 3);
+      compute(2 * h, ci);
+      if (ci + 1 < n_ch) compute(2 * h + 1, ci + 1);
+      if (more) commit(sa, 2 * (h ^ 1));
+      if (ci + 3 < n_ch) commit(sb, 2 * (h ^ 1) + 1);
+      __syncthreads();
+    }
   }
 
   // outputs: lane (c, g4) holds dims DPL (4 g4 + i) + jj of row 16 t + c
