@@ -21,6 +21,21 @@ Readings where the page is silent:
   * free(seq) decrements each of the sequence's blocks and returns those that
     reach zero to the pool;
   * on exhaustion nothing changes and OutOfBlocks is raised.
+
+Swap ([LLMI] "9. Failure modes and limitations": a preempted request's KV
+blocks are evicted to host memory and brought back later; [MTKV] "C++ Block
+Scheduler and Asynchronous Fetch Kernel": blocks are demoted to pinned host
+memory and promoted back to HBM with asynchronous copies). Readings:
+  * swap_out(seq) returns the sequence's blocks in logical order (the caller
+    copies them out before anything reuses them), then releases its
+    references exactly as free() does; the sequence keeps its length and is
+    marked swapped; shared blocks stay resident for the other sharers;
+  * swap_in(seq) allocates cdiv(len, block_size) fresh blocks, popping them
+    in logical order, and makes them the sequence's table; sharing is not
+    restored (the copies are private); too few free blocks raise OutOfBlocks
+    and change nothing;
+  * a swapped sequence cannot append, fork or export its table; free() drops
+    it.
 """
 
 
@@ -35,6 +50,7 @@ class BlockManagerModel:
         self.ref = [0] * num_blocks
         self.tables = {}
         self.lens = {}
+        self.swapped = set()
 
     def _pop(self):
         if not self.free_pool:
@@ -45,6 +61,8 @@ class BlockManagerModel:
 
     def append_slot(self, seq):
         """Reserve the next token slot of `seq`; returns (slot, cow_src, cow_dst)."""
+        if seq in self.swapped:
+            raise ValueError("sequence is swapped out")
         table = self.tables.setdefault(seq, [])
         pos = self.lens.get(seq, 0)
         bs = self.block_size
@@ -62,7 +80,7 @@ class BlockManagerModel:
         return table[-1] * bs + pos % bs, cow[0], cow[1]
 
     def fork(self, parent, child):
-        if child in self.tables or parent not in self.tables:
+        if child in self.tables or child in self.swapped or parent not in self.tables:
             raise KeyError("fork needs an existing parent and a new child")
         self.tables[child] = list(self.tables[parent])
         self.lens[child] = self.lens[parent]
@@ -70,15 +88,45 @@ class BlockManagerModel:
             self.ref[blk] += 1
 
     def free(self, seq):
+        if seq in self.swapped:
+            self.swapped.discard(seq)
+            del self.lens[seq]
+            return
         for blk in self.tables.pop(seq):
             self.ref[blk] -= 1
             if self.ref[blk] == 0:
                 self.free_pool.append(blk)
         del self.lens[seq]
 
+    def swap_out(self, seq):
+        """Release a resident sequence's blocks; returns them in logical order."""
+        if seq not in self.tables:
+            raise KeyError("swap_out needs a resident sequence")
+        blocks = self.tables.pop(seq)
+        for blk in blocks:
+            self.ref[blk] -= 1
+            if self.ref[blk] == 0:
+                self.free_pool.append(blk)
+        self.swapped.add(seq)
+        return blocks
+
+    def swap_in(self, seq):
+        """Give a swapped sequence fresh blocks; returns them in logical order."""
+        if seq not in self.swapped:
+            raise KeyError("swap_in needs a swapped sequence")
+        n = -(-self.lens[seq] // self.block_size)
+        if len(self.free_pool) < n:
+            raise OutOfBlocks("not enough free blocks to swap in")
+        blocks = [self._pop() for _ in range(n)]
+        self.tables[seq] = blocks
+        self.swapped.discard(seq)
+        return blocks
+
     def export_table(self, seqs, max_blocks, pad=0):
         rows = []
         for s in seqs:
+            if s in self.swapped:
+                raise ValueError("sequence is swapped out")
             t = self.tables.get(s, [])
             if len(t) > max_blocks:
                 raise ValueError("table wider than max_blocks")

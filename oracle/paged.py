@@ -319,3 +319,38 @@ def multi_query_attention(q_bits, k_cache, v_cache, block_tables, context_lens, 
                 out[b, i, h], _ = attention_one(q[b, i, h], kd[:p + 1, g, :], vd[:p + 1, g, :],
                                                 scale)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Swap to host memory ([LLMI] "9. Failure modes and limitations": preemption
+# evicts a request's KV blocks to host RAM over PCIe; [MTKV] "C++ Block
+# Scheduler and Asynchronous Fetch Kernel": demotion of a block to pinned host
+# memory and promotion back to HBM are plain asynchronous copies of the
+# block's bytes). A swap moves bytes and nothing else, so the oracle is the
+# copy written out.
+
+def swap_out(k_cache, v_cache, block_ids):
+    """Host image of the listed blocks: raw patterns [2, n, n_kv, bs, d]
+    (K blocks, then V blocks, in list order). An id outside the pool gives
+    a block of zero bytes."""
+    nb = k_cache.shape[0]
+    n = len(block_ids)
+    out = np.zeros((2, n) + k_cache.shape[1:], dtype=k_cache.dtype)
+    for i, blk in enumerate(block_ids):
+        if 0 <= blk < nb:
+            out[0, i] = k_cache[blk]
+            out[1, i] = v_cache[blk]
+    return out
+
+
+def swap_in(k_cache, v_cache, block_ids, host):
+    """Caches with the listed blocks overwritten from a host image laid out
+    as swap_out() returns it; an id outside the pool is skipped."""
+    k = k_cache.copy()
+    v = v_cache.copy()
+    nb = k.shape[0]
+    for i, blk in enumerate(block_ids):
+        if 0 <= blk < nb:
+            k[blk] = host[0, i]
+            v[blk] = host[1, i]
+    return k, v
