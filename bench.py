@@ -69,6 +69,8 @@ def parse():
                     help="1: longest-first work list built once per step (pkv_decode_schedule)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the oracle CPU baseline (0 disables it)")
+    ap.add_argument("--swap", type=int, default=0, metavar="N",
+                    help="measure swapping N sequences of the 70B layer to host memory and back")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB block copy (for scaling HBM counters) and exit")
     return ap.parse_args()
@@ -111,6 +113,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         copy_calibration(pkv, torch)
+        return
+    if args.swap:
+        bench_swap(args, pkv, W, np, torch, dev)
         return
 
     w = W.ALL[args.workload]()
@@ -277,6 +282,69 @@ def main():
     # ---------------------------------------------------------------- oracle on the CPU
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, caches[0], q[0], args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def bench_swap(args, pkv, W, np, torch, dev):
+    """Swap args.swap sequences of one 70B-GQA layer pool (8192 tokens each,
+    512 blocks of 8 heads x 16 tokens x 128 dims) to pinned host memory and
+    back into other blocks, timed with HIP events on the stream the calls run
+    on (pkv_swap_out = pack kernel + device-to-host copy, pkv_swap_in =
+    host-to-device copy + unpack kernel; the kernels' share is in the
+    rocprofv3 trace)."""
+    w = W.gqa_70b(layers=1)
+    kc, vc, _, _ = W.make_cache(w, device=dev, poison_unused=False)
+    n_seq = min(args.swap, w.B)
+    ids = np.concatenate([w.block_tables[b, :512] for b in range(n_seq)]).astype(np.int32)
+    n = len(ids)
+    ids_d = torch.from_numpy(ids).to(dev)
+    back = torch.from_numpy(ids[::-1].copy()).to(dev)      # other blocks on the way back
+    nbytes = pkv.swap_bytes(kc, n)
+    staging = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    desc = pkv.cache_desc(kc)
+    L = pkv.lib()
+    import ctypes
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def phases(ev):                  # events: 0 start, 2 after swap-out, 4 after swap-in
+        ev[0].record(stream)
+        assert L.pkv_swap_out(ctypes.byref(desc), ctypes.c_void_p(kc.data_ptr()),
+                              ctypes.c_void_p(vc.data_ptr()), ctypes.c_void_p(ids_d.data_ptr()),
+                              n, ctypes.c_void_p(staging.data_ptr()),
+                              ctypes.c_void_p(host.data_ptr()), sp) == 0
+        ev[2].record(stream)
+        assert L.pkv_swap_in(ctypes.byref(desc), ctypes.c_void_p(kc.data_ptr()),
+                             ctypes.c_void_p(vc.data_ptr()), ctypes.c_void_p(back.data_ptr()),
+                             n, ctypes.c_void_p(staging.data_ptr()),
+                             ctypes.c_void_p(host.data_ptr()), sp) == 0
+        ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        phases([torch.cuda.Event(enable_timing=True) for _ in range(5)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for e in evs:
+        phases(e)
+    torch.cuda.synchronize()
+    t_out = sum(e[0].elapsed_time(e[2]) for e in evs) / len(evs)
+    t_in = sum(e[2].elapsed_time(e[4]) for e in evs) / len(evs)
+    gb = nbytes / 1e9
+    result = {
+        "metric": "KV swap to host memory and back: GB/s of KV image per direction",
+        "value": round(2 * gb / ((t_out + t_in) * 1e-3), 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t_out + t_in, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "swap of 70B-GQA sequences (one layer pool)", "sequences": n_seq,
+                   "blocks": n, "image_bytes": nbytes},
+        "swap_out_ms": round(t_out, 4), "swap_in_ms": round(t_in, 4),
+        "swap_out_gbs": round(gb / (t_out * 1e-3), 2), "swap_in_gbs": round(gb / (t_in * 1e-3), 2),
+        "roofline": {"bound": "host link", "achieved": round(gb / (t_out * 1e-3), 2),
+                     "peak": 64.0, "unit": "GB/s", "frac": round(gb / (t_out * 1e-3) / 64.0, 4),
+                     "note": "peak = PCIe 5.0 x16 nominal per direction", "traffic": None},
+    }
     print(json.dumps(result), flush=True)
 
 

@@ -279,6 +279,36 @@ pkv_status pkv_gather_kv(const pkv_cache_desc* desc, void* k_out, void* v_out,
                          const int32_t* block_table_row, int32_t context_len, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Swap of KV blocks to host memory and back ([LLMI] "9. Failure modes and
+ * limitations": under memory pressure a request is preempted by evicting its
+ * KV blocks to host RAM over PCIe and restoring them later; [MTKV] "C++ Block
+ * Scheduler and Asynchronous Fetch Kernel": demotion to pinned host memory and
+ * promotion back to HBM are asynchronous copies on a stream of their own).
+ *
+ * Host image of n blocks: raw cache bytes [2][n][n_kv][block_size][d_head]
+ * (K blocks, then V blocks, in block_ids order), pkv_swap_bytes(desc, n)
+ * bytes. pkv_swap_out packs the listed blocks into `staging` (device, at
+ * least that size) and copies the image to `host`; pkv_swap_in copies `host`
+ * into `staging` and unpacks it into the listed blocks. block_ids: int32 [n]
+ * on the device. An id outside the pool packs as zero bytes and is skipped on
+ * unpacking. `host` should be pinned (hipHostMalloc) for the copies to be
+ * asynchronous; both calls are stream-ordered on `stream` (use a second
+ * stream to overlap them with attention), the host image is complete once
+ * the stream reaches the end of pkv_swap_out, and `staging` must not be
+ * reused before then. Blocks released by pkv_bm_swap_out may be reallocated
+ * only by work ordered after the pkv_swap_out that reads them.
+ * ------------------------------------------------------------------------- */
+size_t pkv_swap_bytes(const pkv_cache_desc* desc, int32_t n_blocks);
+
+pkv_status pkv_swap_out(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                        const int32_t* block_ids, int32_t n_blocks, void* staging, void* host,
+                        void* stream);
+
+pkv_status pkv_swap_in(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
+                       const int32_t* block_ids, int32_t n_blocks, void* staging,
+                       const void* host, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Host block manager ([SMTS] "Paged KV-Cache with Radix Tree Prefix Cache":
  * physical blocks with reference counts, slot allocation popping the free
  * pool, exhaustion asking the scheduler to preempt; copy-on-write sharing).
@@ -299,6 +329,18 @@ pkv_status pkv_gather_kv(const pkv_cache_desc* desc, void* k_out, void* v_out,
  * export_table: rows of block ids for `seqs`, padded with 0 (never read),
  * into host int32 [B, max_blocks]; a sequence wider than max_blocks is an
  * invalid argument.
+ * swap_out(seq): writes the resident sequence's blocks in logical order to
+ * blocks_out (the blocks to pass to pkv_swap_out), then releases its
+ * references as free() does; shared blocks stay resident for their other
+ * sharers. The sequence keeps its length and is marked swapped: it cannot
+ * append, fork or be exported until swapped in; free() drops it.
+ * swap_in(seq): allocates cdiv(len, block_size) fresh blocks, popped in
+ * logical order, makes them the sequence's table and writes them to
+ * blocks_out (the blocks to pass to pkv_swap_in); sharing is not restored.
+ * Too few free blocks return PKV_ERR_OUT_OF_BLOCKS and change nothing.
+ * For both, *n_blocks receives the block count; blocks_out == NULL only
+ * queries it; capacity below it is an invalid argument (no change).
+ * is_swapped: 1 swapped, 0 resident, -1 unknown sequence.
  * ------------------------------------------------------------------------- */
 typedef struct pkv_bm pkv_bm;
 
@@ -312,6 +354,11 @@ pkv_status pkv_bm_export_table(const pkv_bm* bm, const int64_t* seqs, int32_t B,
                                int32_t max_blocks, int32_t* host_table);
 /* Token count of a sequence (-1 if unknown), free-pool size, a block's count. */
 int64_t pkv_bm_seq_len(const pkv_bm* bm, int64_t seq);
+pkv_status pkv_bm_swap_out(pkv_bm* bm, int64_t seq, int32_t* blocks_out, int32_t capacity,
+                           int32_t* n_blocks);
+pkv_status pkv_bm_swap_in(pkv_bm* bm, int64_t seq, int32_t* blocks_out, int32_t capacity,
+                          int32_t* n_blocks);
+int32_t pkv_bm_is_swapped(const pkv_bm* bm, int64_t seq);
 int32_t pkv_bm_num_free(const pkv_bm* bm);
 int32_t pkv_bm_ref_count(const pkv_bm* bm, int32_t block);
 

@@ -27,6 +27,9 @@ from ._lib import (  # noqa: F401
     slot_mapping,
     splitk_reduce,
     status_string,
+    swap_bytes,
+    swap_in,
+    swap_out,
     version,
 )
 

@@ -76,6 +76,12 @@ SIGNATURES = {
     "pkv_splitk_reduce": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                  _vp]),
     "pkv_copy_blocks": (_i32, [ctypes.POINTER(CacheDesc), _vp, _vp, _vp, _i32, _vp]),
+    "pkv_swap_bytes": (_sz, [ctypes.POINTER(CacheDesc), _i32]),
+    "pkv_swap_out": (_i32, [ctypes.POINTER(CacheDesc), _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "pkv_swap_in": (_i32, [ctypes.POINTER(CacheDesc), _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "pkv_bm_swap_out": (_i32, [_vp, ctypes.c_int64, _c_int32_p, _i32, _c_int32_p]),
+    "pkv_bm_swap_in": (_i32, [_vp, ctypes.c_int64, _c_int32_p, _i32, _c_int32_p]),
+    "pkv_bm_is_swapped": (_i32, [_vp, ctypes.c_int64]),
     "pkv_gather_kv": (_i32, [ctypes.POINTER(CacheDesc), _vp, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pkv_bm_create": (_i32, [_i32, _i32, ctypes.POINTER(_vp)]),
     "pkv_bm_destroy": (None, [_vp]),
@@ -360,6 +366,42 @@ def copy_blocks(k_cache, v_cache, pairs, stream=None):
                                  n, _stream(stream)), "pkv_copy_blocks")
 
 
+def swap_bytes(k_cache, n_blocks):
+    desc = cache_desc(k_cache)
+    return int(lib().pkv_swap_bytes(ctypes.byref(desc), int(n_blocks)))
+
+
+def swap_out(k_cache, v_cache, block_ids, staging, host, stream=None):
+    """Pack the listed blocks (int32 on the GPU) into `staging` (GPU) and copy the
+    image to `host` (pinned CPU uint8 tensor of swap_bytes(n) bytes)."""
+    desc = cache_desc(k_cache)
+    _need(block_ids, torch.int32, "block_ids")
+    n = block_ids.numel()
+    need = swap_bytes(k_cache, n)
+    if staging.numel() * staging.element_size() < need or host.numel() * host.element_size() < need:
+        raise ValueError("staging and host must hold swap_bytes(n) bytes")
+    if host.is_cuda or not host.is_contiguous():
+        raise ValueError("host must be a contiguous CPU tensor (pinned for an async copy)")
+    _check(lib().pkv_swap_out(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(block_ids),
+                              n, _ptr(staging), ctypes.c_void_p(host.data_ptr()),
+                              _stream(stream)), "pkv_swap_out")
+
+
+def swap_in(k_cache, v_cache, block_ids, staging, host, stream=None):
+    """Copy a host image into `staging` and unpack it into the listed blocks."""
+    desc = cache_desc(k_cache)
+    _need(block_ids, torch.int32, "block_ids")
+    n = block_ids.numel()
+    need = swap_bytes(k_cache, n)
+    if staging.numel() * staging.element_size() < need or host.numel() * host.element_size() < need:
+        raise ValueError("staging and host must hold swap_bytes(n) bytes")
+    if host.is_cuda or not host.is_contiguous():
+        raise ValueError("host must be a contiguous CPU tensor (pinned for an async copy)")
+    _check(lib().pkv_swap_in(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(block_ids),
+                             n, _ptr(staging), ctypes.c_void_p(host.data_ptr()),
+                             _stream(stream)), "pkv_swap_in")
+
+
 def gather_kv(k_cache, v_cache, block_table_row, context_len, stream=None):
     """Dense [ctx, n_kv, d] copies of one sequence's raw K/V rows."""
     desc = cache_desc(k_cache)
@@ -416,6 +458,24 @@ class BlockManager:
                "pkv_bm_export_table")
         flat = list(buf)[:n * max_blocks]
         return [flat[i * max_blocks:(i + 1) * max_blocks] for i in range(n)]
+
+    def _swap(self, fn, name, seq):
+        n = ctypes.c_int32()
+        _check(fn(self._h, seq, None, 0, ctypes.byref(n)), name)
+        buf = (ctypes.c_int32 * max(n.value, 1))()
+        _check(fn(self._h, seq, buf, n.value, ctypes.byref(n)), name)
+        return list(buf)[:n.value]
+
+    def swap_out(self, seq):
+        """Release a resident sequence's blocks; returns them (logical order) for pkv_swap_out."""
+        return self._swap(lib().pkv_bm_swap_out, "pkv_bm_swap_out", seq)
+
+    def swap_in(self, seq):
+        """Fresh blocks (logical order) for a swapped sequence, to fill with pkv_swap_in."""
+        return self._swap(lib().pkv_bm_swap_in, "pkv_bm_swap_in", seq)
+
+    def is_swapped(self, seq):
+        return int(lib().pkv_bm_is_swapped(self._h, seq))
 
     def seq_len(self, seq):
         return int(lib().pkv_bm_seq_len(self._h, seq))

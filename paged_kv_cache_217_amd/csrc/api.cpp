@@ -379,6 +379,51 @@ pkv_status pkv_paged_multi_query_attention(const pkv_cache_desc* desc, void* out
                                             max_blocks_per_seq * desc->block_size));
 }
 
+size_t pkv_swap_bytes(const pkv_cache_desc* desc, int32_t n_blocks) {
+  if (check_desc(desc) != PKV_OK || n_blocks < 0) return 0;
+  return static_cast<size_t>(2 * static_cast<int64_t>(n_blocks) * pkv::swap_block_bytes(*desc));
+}
+
+static pkv_status check_swap(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                             const int32_t* block_ids, int32_t n_blocks, const void* staging,
+                             const void* host) {
+  pkv_status st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (n_blocks < 0) return PKV_ERR_INVALID_ARG;
+  if (n_blocks == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_ids || !staging || !host) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(staging))
+    return PKV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(n_blocks) * pkv::swap_block_bytes(*desc) / 16384 > 0x3fffffff)
+    return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+pkv_status pkv_swap_out(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                        const int32_t* block_ids, int32_t n_blocks, void* staging, void* host,
+                        void* stream) {
+  pkv_status st = check_swap(desc, k_cache, v_cache, block_ids, n_blocks, staging, host);
+  if (st != PKV_OK || n_blocks == 0) return st;
+  const hipStream_t s = as_stream(stream);
+  hipError_t e = pkv::launch_swap_pack(*desc, k_cache, v_cache, block_ids, n_blocks, staging, s);
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  return from_hip(hipMemcpyAsync(host, staging, pkv_swap_bytes(desc, n_blocks),
+                                 hipMemcpyDeviceToHost, s));
+}
+
+pkv_status pkv_swap_in(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
+                       const int32_t* block_ids, int32_t n_blocks, void* staging,
+                       const void* host, void* stream) {
+  pkv_status st = check_swap(desc, k_cache, v_cache, block_ids, n_blocks, staging, host);
+  if (st != PKV_OK || n_blocks == 0) return st;
+  const hipStream_t s = as_stream(stream);
+  hipError_t e = hipMemcpyAsync(staging, host, pkv_swap_bytes(desc, n_blocks),
+                                hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  return from_hip(
+      pkv::launch_swap_unpack(*desc, k_cache, v_cache, block_ids, n_blocks, staging, s));
+}
+
 size_t pkv_decode_schedule_bytes(int32_t B, int32_t max_context_len, int32_t partition_size) {
   if (B <= 0 || max_context_len < 0 || partition_size <= 0) return 0;
   const int64_t P_max = std::max<int64_t>(1, cdiv(max_context_len, partition_size));

@@ -22,6 +22,7 @@ struct pkv_bm {
   struct Seq {
     std::vector<int32_t> blocks;
     int64_t len = 0;
+    bool swapped = false;                               // blocks live on the host
   };
   std::unordered_map<int64_t, Seq> seqs;
 
@@ -53,6 +54,8 @@ void pkv_bm_destroy(pkv_bm* bm) { delete bm; }
 pkv_status pkv_bm_append_slot(pkv_bm* bm, int64_t seq, int64_t* slot, int32_t* cow_src,
                               int32_t* cow_dst) {
   if (!bm || !slot || !cow_src || !cow_dst) return PKV_ERR_INVALID_ARG;
+  auto found = bm->seqs.find(seq);
+  if (found != bm->seqs.end() && found->second.swapped) return PKV_ERR_INVALID_ARG;
   auto& s = bm->seqs[seq];
   const int64_t pos = s.len;
   const int32_t bs = bm->block_size;
@@ -85,7 +88,8 @@ pkv_status pkv_bm_append_slot(pkv_bm* bm, int64_t seq, int64_t* slot, int32_t* c
 pkv_status pkv_bm_fork(pkv_bm* bm, int64_t parent, int64_t child) {
   if (!bm) return PKV_ERR_INVALID_ARG;
   auto p = bm->seqs.find(parent);
-  if (p == bm->seqs.end() || bm->seqs.count(child)) return PKV_ERR_INVALID_ARG;
+  if (p == bm->seqs.end() || p->second.swapped || bm->seqs.count(child))
+    return PKV_ERR_INVALID_ARG;
   pkv_bm::Seq copy = p->second;
   for (int32_t blk : copy.blocks) bm->ref[blk] += 1;
   bm->seqs.emplace(child, std::move(copy));
@@ -113,6 +117,7 @@ pkv_status pkv_bm_export_table(const pkv_bm* bm, const int64_t* seqs, int32_t B,
     const std::vector<int32_t>* blocks = it == bm->seqs.end() ? nullptr : &it->second.blocks;
     const int32_t n = blocks ? static_cast<int32_t>(blocks->size()) : 0;
     if (n > max_blocks) return PKV_ERR_INVALID_ARG;
+    if (it != bm->seqs.end() && it->second.swapped) return PKV_ERR_INVALID_ARG;
   }
   for (int32_t b = 0; b < B; ++b) {
     auto it = bm->seqs.find(seqs[b]);
@@ -124,6 +129,54 @@ pkv_status pkv_bm_export_table(const pkv_bm* bm, const int64_t* seqs, int32_t B,
     for (; n < max_blocks; ++n) row[n] = 0;
   }
   return PKV_OK;
+}
+
+pkv_status pkv_bm_swap_out(pkv_bm* bm, int64_t seq, int32_t* blocks_out, int32_t capacity,
+                           int32_t* n_blocks) {
+  if (!bm || !n_blocks) return PKV_ERR_INVALID_ARG;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end() || it->second.swapped) return PKV_ERR_INVALID_ARG;
+  auto& s = it->second;
+  const int32_t n = static_cast<int32_t>(s.blocks.size());
+  *n_blocks = n;
+  if (!blocks_out) return PKV_OK;                       // size query, no change
+  if (capacity < n) return PKV_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t blk = s.blocks[i];
+    blocks_out[i] = blk;
+    bm->ref[blk] -= 1;
+    if (bm->ref[blk] == 0) bm->free_pool.push_back(blk);
+  }
+  s.blocks.clear();
+  s.swapped = true;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_swap_in(pkv_bm* bm, int64_t seq, int32_t* blocks_out, int32_t capacity,
+                          int32_t* n_blocks) {
+  if (!bm || !n_blocks) return PKV_ERR_INVALID_ARG;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end() || !it->second.swapped) return PKV_ERR_INVALID_ARG;
+  auto& s = it->second;
+  const int64_t need = (s.len + bm->block_size - 1) / bm->block_size;
+  *n_blocks = static_cast<int32_t>(need);
+  if (!blocks_out) return PKV_OK;                       // size query, no change
+  if (capacity < need) return PKV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(bm->free_pool.size()) < need) return PKV_ERR_OUT_OF_BLOCKS;
+  for (int64_t i = 0; i < need; ++i) {
+    int32_t blk;
+    bm->pop(&blk);
+    s.blocks.push_back(blk);
+    blocks_out[i] = blk;
+  }
+  s.swapped = false;
+  return PKV_OK;
+}
+
+int32_t pkv_bm_is_swapped(const pkv_bm* bm, int64_t seq) {
+  if (!bm) return -1;
+  auto it = bm->seqs.find(seq);
+  return it == bm->seqs.end() ? -1 : (it->second.swapped ? 1 : 0);
 }
 
 int64_t pkv_bm_seq_len(const pkv_bm* bm, int64_t seq) {

@@ -114,6 +114,43 @@ __global__ void gather_kernel(uint8_t* __restrict__ k_out, uint8_t* __restrict__
   *reinterpret_cast<uint4*>(v_out + dst) = *reinterpret_cast<const uint4*>(v_cache + src);
 }
 
+// Swap to host: the listed blocks (every head's tile, K then V) are packed
+// into a contiguous device staging image before one DMA copy to host memory,
+// and unpacked from it after the copy back ([MTKV] "C++ Block Scheduler and
+// Asynchronous Fetch Kernel" copies block by block; one batched copy keeps the
+// DMA engine at the link's rate). grid: (n blocks x slices of 16 KiB, K/V).
+constexpr int kSwapSlice = 16384;
+typedef uint32_t swap_u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool PACK>
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    const int32_t* __restrict__ block_ids, int n_blocks, int64_t block_bytes, int num_blocks,
+    uint8_t* __restrict__ staging) {
+  const int slices = static_cast<int>((block_bytes + kSwapSlice - 1) / kSwapSlice);
+  const int i = blockIdx.x / slices;
+  const int64_t off0 = static_cast<int64_t>(blockIdx.x % slices) * kSwapSlice;
+  const int blk = block_ids[i];
+  const bool valid = blk >= 0 && blk < num_blocks;
+  uint8_t* cache = blockIdx.y == 0 ? k_cache : v_cache;
+  uint8_t* img = staging + (static_cast<int64_t>(blockIdx.y) * n_blocks + i) * block_bytes;
+  const int64_t end = min(off0 + kSwapSlice, block_bytes);
+  if (PACK) {
+    for (int64_t o = off0 + 16 * threadIdx.x; o < end; o += 16 * blockDim.x) {
+      swap_u32x4 w = {0u, 0u, 0u, 0u};                 // an absent block packs as zeros
+      if (valid)
+        w = __builtin_nontemporal_load(
+            reinterpret_cast<const swap_u32x4*>(cache + blk * block_bytes + o));
+      *reinterpret_cast<swap_u32x4*>(img + o) = w;
+    }
+  } else {
+    if (!valid) return;                               // an absent block is skipped
+    for (int64_t o = off0 + 16 * threadIdx.x; o < end; o += 16 * blockDim.x)
+      *reinterpret_cast<swap_u32x4*>(cache + blk * block_bytes + o) =
+          __builtin_nontemporal_load(reinterpret_cast<const swap_u32x4*>(img + o));
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, int max_blocks,
@@ -166,6 +203,33 @@ hipError_t launch_gather(const pkv_cache_desc& d, void* k_out, void* v_out, cons
       static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out),
       static_cast<const uint8_t*>(k_cache), static_cast<const uint8_t*>(v_cache), table, ctx,
       d.n_kv, row_bytes, d.block_size, d.num_blocks);
+  return hipGetLastError();
+}
+
+int64_t swap_block_bytes(const pkv_cache_desc& d) {
+  return static_cast<int64_t>(d.n_kv) * d.block_size * d.d_head *
+         (d.kv_dtype == PKV_FP8_E4M3 ? 1 : 2);
+}
+
+hipError_t launch_swap_pack(const pkv_cache_desc& d, const void* k_cache, const void* v_cache,
+                            const int32_t* block_ids, int n, void* staging, hipStream_t stream) {
+  const int64_t bb = swap_block_bytes(d);
+  const int slices = static_cast<int>((bb + kSwapSlice - 1) / kSwapSlice);
+  swap_blocks_kernel<true><<<dim3(n * slices, 2), 256, 0, stream>>>(
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(k_cache)),
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(v_cache)), block_ids, n, bb, d.num_blocks,
+      static_cast<uint8_t*>(staging));
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_unpack(const pkv_cache_desc& d, void* k_cache, void* v_cache,
+                              const int32_t* block_ids, int n, const void* staging,
+                              hipStream_t stream) {
+  const int64_t bb = swap_block_bytes(d);
+  const int slices = static_cast<int>((bb + kSwapSlice - 1) / kSwapSlice);
+  swap_blocks_kernel<false><<<dim3(n * slices, 2), 256, 0, stream>>>(
+      static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), block_ids, n, bb,
+      d.num_blocks, const_cast<uint8_t*>(static_cast<const uint8_t*>(staging)));
   return hipGetLastError();
 }
 

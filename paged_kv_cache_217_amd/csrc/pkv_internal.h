@@ -68,6 +68,15 @@ hipError_t launch_copy_blocks(const pkv_cache_desc& d, void* k_cache, void* v_ca
 hipError_t launch_gather(const pkv_cache_desc& d, void* k_out, void* v_out, const void* k_cache,
                          const void* v_cache, const int32_t* table, int ctx, hipStream_t stream);
 
+// Swap to host memory: bytes of one block's K (or V) for every head, and the
+// pack / unpack kernels around the DMA copy.
+int64_t swap_block_bytes(const pkv_cache_desc& d);
+hipError_t launch_swap_pack(const pkv_cache_desc& d, const void* k_cache, const void* v_cache,
+                            const int32_t* block_ids, int n, void* staging, hipStream_t stream);
+hipError_t launch_swap_unpack(const pkv_cache_desc& d, void* k_cache, void* v_cache,
+                              const int32_t* block_ids, int n, const void* staging,
+                              hipStream_t stream);
+
 // Whether the decode kernels were built for this (d, bs, G, dtype) combination.
 bool decode_supported(int d, int bs, int G, int kv_dtype);
 

@@ -183,6 +183,104 @@ def test_block_manager_matches_the_model_on_random_operations():
         lib_bm.close()
 
 
+def test_block_manager_with_swaps_matches_the_model():
+    rng = random.Random(2171)
+    for trial in range(30):
+        nb, bs = rng.choice([(6, 4), (12, 4), (40, 16), (9, 2)])
+        lib_bm = pkv.BlockManager(nb, bs)
+        model = BlockManagerModel(nb, bs)
+        resident, swapped = [], []
+        next_id = 0
+        for step in range(300):
+            op = rng.random()
+            if op < 0.5 or not resident:
+                seq = rng.choice(resident) if resident and rng.random() < 0.8 else next_id
+                if seq == next_id:
+                    next_id += 1
+                try:
+                    expect = model.append_slot(seq)
+                except ModelOutOfBlocks:
+                    if not model.tables.get(seq):
+                        model.tables.pop(seq, None)
+                        model.lens.pop(seq, None)
+                    with pytest.raises(pkv.OutOfBlocks):
+                        lib_bm.append_slot(seq)
+                    continue
+                assert lib_bm.append_slot(seq) == expect
+                if seq not in resident:
+                    resident.append(seq)
+            elif op < 0.6:
+                parent = rng.choice(resident)
+                model.fork(parent, next_id)
+                lib_bm.fork(parent, next_id)
+                resident.append(next_id)
+                next_id += 1
+            elif op < 0.75:
+                seq = resident.pop(rng.randrange(len(resident)))
+                assert lib_bm.swap_out(seq) == model.swap_out(seq)
+                assert lib_bm.is_swapped(seq) == 1
+                swapped.append(seq)
+            elif op < 0.9 and swapped:
+                seq = rng.choice(swapped)
+                try:
+                    expect = model.swap_in(seq)
+                except ModelOutOfBlocks:
+                    with pytest.raises(pkv.OutOfBlocks):
+                        lib_bm.swap_in(seq)
+                    continue
+                assert lib_bm.swap_in(seq) == expect
+                swapped.remove(seq)
+                resident.append(seq)
+            else:
+                pool = resident + swapped
+                seq = pool[rng.randrange(len(pool))]
+                (resident if seq in resident else swapped).remove(seq)
+                model.free(seq)
+                lib_bm.free(seq)
+            assert lib_bm.num_free() == len(model.free_pool)
+        for blk in range(nb):
+            assert lib_bm.ref_count(blk) == model.ref[blk]
+        for s in resident + swapped:
+            assert lib_bm.seq_len(s) == model.lens[s]
+        mb = max([len(t) for t in model.tables.values()] + [1])
+        assert lib_bm.export_table(resident, mb) == model.export_table(resident, mb)
+        lib_bm.close()
+
+
+def test_swapped_sequences_refuse_table_operations():
+    bm = pkv.BlockManager(4, 2)
+    for _ in range(3):
+        bm.append_slot(7)
+    assert bm.swap_out(7) == [3, 2] and bm.num_free() == 4
+    for call in (lambda: bm.append_slot(7), lambda: bm.fork(7, 8),
+                 lambda: bm.export_table([7], 4), lambda: bm.swap_out(7)):
+        with pytest.raises(pkv.PkvError):
+            call()
+    assert bm.seq_len(7) == 3 and bm.is_swapped(7) == 1 and bm.is_swapped(99) == -1
+    assert bm.swap_in(7) == [2, 3] and bm.is_swapped(7) == 0   # pool [0, 1, 3, 2] pops 2, 3
+    with pytest.raises(pkv.PkvError):
+        bm.swap_in(7)
+
+
+def test_swap_entry_points_validate():
+    L = _lib.lib()
+    fake = ctypes.c_void_p(0x1000)
+    d = _desc()
+    block = 2 * 16 * 128 * 2                  # n_kv x bs x d x 2 bytes
+    assert L.pkv_swap_bytes(ctypes.byref(d), 3) == 2 * 3 * block
+    assert L.pkv_swap_bytes(ctypes.byref(d), -1) == 0
+    for fn in (L.pkv_swap_out, L.pkv_swap_in):
+        assert fn(ctypes.byref(d), fake, fake, fake, -1, fake, fake, None) == \
+            _lib.PKV_ERR_INVALID_ARG
+        assert fn(ctypes.byref(d), fake, fake, fake, 0, None, None, None) == _lib.PKV_OK
+        assert fn(ctypes.byref(d), fake, fake, fake, 2, None, fake, None) == \
+            _lib.PKV_ERR_INVALID_ARG
+        assert fn(ctypes.byref(d), fake, fake, fake, 2, ctypes.c_void_p(0x1008), fake, None) == \
+            _lib.PKV_ERR_INVALID_ARG
+        assert fn(ctypes.byref(_desc(bs=8)), fake, fake, fake, 2, fake, fake, None) == \
+            _lib.PKV_ERR_UNSUPPORTED
+
+
 def test_block_manager_errors():
     bm = pkv.BlockManager(2, 4)
     with pytest.raises(pkv.PkvError):
