@@ -279,6 +279,41 @@ pkv_status pkv_gather_kv(const pkv_cache_desc* desc, void* k_out, void* v_out,
                          const int32_t* block_table_row, int32_t context_len, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Decode attention for a batch that shares a prompt prefix ([SMTS] "Paged
+ * KV-Cache with Radix Tree Prefix Cache": requests sharing a system prompt,
+ * tool definitions or few-shot examples point at the same physical blocks;
+ * [LLMI] "7. Practical applications": identical document prefixes shared
+ * across requests). Computes exactly pkv_paged_decode_attention for
+ * sequences whose tables are prefix_table ++ block_tables[b]:
+ *   K_b[t] = prefix block prefix_table[t / bs]            for t < prefix_len,
+ *            block block_tables[b][(t - prefix_len) / bs]  otherwise,
+ * over ctx_b = prefix_len + suffix_lens[b] tokens, but reads the prefix's
+ * K/V once for all B sequences: the sharers' (sequence, head) rows attend to
+ * the prefix together on the matrix cores (split over prefix_partition-token
+ * partitions), each sequence's own suffix runs through the decode partition
+ * kernel, and one log-sum-exp merge combines both.
+ *
+ * prefix_table: int32 [prefix_len / bs] on the device; prefix_len must be a
+ * multiple of the block size (0: no prefix, plain decode). block_tables:
+ * int32 [B, max_blocks_per_seq] of suffix blocks; suffix_lens: int32 [B]
+ * <= max_suffix_len <= max_blocks_per_seq * bs. Partition sizes are block
+ * multiples; 0 picks them. workspace: at least
+ * pkv_cascade_workspace_bytes(...) for the same arguments. Other arguments
+ * as for pkv_paged_decode_attention.
+ * ------------------------------------------------------------------------- */
+size_t pkv_cascade_workspace_bytes(const pkv_cache_desc* desc, int32_t B, int32_t n_q,
+                                   int32_t prefix_len, int32_t prefix_partition,
+                                   int32_t max_suffix_len, int32_t suffix_partition);
+
+pkv_status pkv_cascade_decode_attention(
+    const pkv_cache_desc* desc, void* out, int32_t out_dtype, const void* q, const void* k_cache,
+    const void* v_cache, const int32_t* prefix_table, int32_t prefix_len,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* suffix_lens,
+    int32_t B, int32_t n_q, int32_t max_suffix_len, float scale, const float* k_scale,
+    const float* v_scale, int32_t prefix_partition, int32_t suffix_partition, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Swap of KV blocks to host memory and back ([LLMI] "9. Failure modes and
  * limitations": under memory pressure a request is preempted by evicting its
  * KV blocks to host RAM over PCIe and restoring them later; [MTKV] "C++ Block

@@ -354,3 +354,23 @@ def swap_in(k_cache, v_cache, block_ids, host):
             k[blk] = host[0, i]
             v[blk] = host[1, i]
     return k, v
+
+
+# ---------------------------------------------------------------------------
+# A batch sharing a prompt prefix ([SMTS] "Paged KV-Cache with Radix Tree
+# Prefix Cache": requests with the same system prompt reference the same
+# physical blocks). Attention is defined on each sequence's whole table, the
+# shared prefix blocks followed by its own, so the oracle is decode attention
+# on the concatenated tables.
+
+def cascade_decode_attention(q_bits, k_cache, v_cache, prefix_table, prefix_len, block_tables,
+                             suffix_lens, scale, kv_dtype=BF16, k_scale=None, v_scale=None):
+    bs = k_cache.shape[2]
+    if prefix_len % bs:
+        raise ValueError("prefix_len must be a multiple of the block size")
+    pre = np.asarray(prefix_table[:prefix_len // bs], dtype=np.int32)
+    B = block_tables.shape[0]
+    tables = np.concatenate([np.tile(pre, (B, 1)), block_tables], axis=1).astype(np.int32)
+    ctx = (prefix_len + np.asarray(suffix_lens)).astype(np.int32)
+    return decode_attention(q_bits, k_cache, v_cache, tables, ctx, scale, kv_dtype, k_scale,
+                            v_scale)

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     OutOfBlocks,
     PkvError,
     cache_desc,
+    cascade_decode_attention,
     copy_blocks,
     decode_schedule,
     decode_workspace_bytes,

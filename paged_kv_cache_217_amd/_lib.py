@@ -71,6 +71,11 @@ SIGNATURES = {
     "pkv_paged_multi_query_attention": (_i32, [ctypes.POINTER(CacheDesc), _vp, _i32, _vp, _i32,
                                                _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                                _f32, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "pkv_cascade_workspace_bytes": (_sz, [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32,
+                                          _i32, _i32]),
+    "pkv_cascade_decode_attention": (_i32, [ctypes.POINTER(CacheDesc), _vp, _i32, _vp, _vp, _vp,
+                                            _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
+                                            _vp, _vp, _i32, _i32, _vp, _sz, _vp]),
     "pkv_decode_schedule_bytes": (_sz, [_i32, _i32, _i32]),
     "pkv_decode_schedule": (_i32, [_vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "pkv_splitk_reduce": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -308,6 +313,33 @@ def paged_multi_query_attention(q, query_lens, k_cache, v_cache, block_tables, c
         _ptr(context_lens), B, n_q, int(max_context_len), float(scale), _ptr(k_scale),
         _ptr(v_scale), P, _ptr(workspace), workspace.numel(), _stream(stream)),
         "pkv_paged_multi_query_attention")
+    return out
+
+
+def cascade_decode_attention(q, k_cache, v_cache, prefix_table, prefix_len, block_tables,
+                             suffix_lens, scale, max_suffix_len, k_scale=None, v_scale=None,
+                             prefix_partition=0, suffix_partition=0, out=None,
+                             out_dtype=torch.float32, workspace=None, stream=None):
+    """Decode attention over prefix_table ++ block_tables[b] with the shared
+    prefix's K/V read once for the whole batch (see pkv.h)."""
+    desc, B, n_q, d = _decode_common(q, k_cache, v_cache, block_tables, suffix_lens,
+                                     k_scale, v_scale)
+    if prefix_len:
+        _need(prefix_table, torch.int32, "prefix_table")
+    if out is None:
+        out = torch.empty((B, n_q, d), dtype=out_dtype, device=q.device)
+    if workspace is None:
+        nbytes = int(lib().pkv_cascade_workspace_bytes(
+            ctypes.byref(desc), B, n_q, int(prefix_len), int(prefix_partition),
+            int(max_suffix_len), int(suffix_partition)))
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().pkv_cascade_decode_attention(
+        ctypes.byref(desc), _ptr(out), _out_code(out.dtype), _ptr(q), _ptr(k_cache),
+        _ptr(v_cache), _ptr(prefix_table) if prefix_len else None, int(prefix_len),
+        _ptr(block_tables), block_tables.shape[1], _ptr(suffix_lens), B, n_q,
+        int(max_suffix_len), float(scale), _ptr(k_scale), _ptr(v_scale), int(prefix_partition),
+        int(suffix_partition), _ptr(workspace), workspace.numel(), _stream(stream)),
+        "pkv_cascade_decode_attention")
     return out
 
 

@@ -379,6 +379,147 @@ pkv_status pkv_paged_multi_query_attention(const pkv_cache_desc* desc, void* out
                                             max_blocks_per_seq * desc->block_size));
 }
 
+// ---------------------------------------------------------------- cascade
+
+namespace {
+
+struct CascadePlan {
+  int32_t Pp, Pp_max;      // prefix partition size and count (0, 0: no prefix)
+  int32_t Ps, Ps_max;      // suffix partition size and count (0, 0: no suffix)
+  size_t suffix_bytes, prefix_bytes;
+};
+
+pkv_status plan_cascade(const pkv_cache_desc* desc, int32_t B, int32_t n_q, int32_t prefix_len,
+                        int32_t prefix_partition, int32_t max_suffix_len,
+                        int32_t suffix_partition, CascadePlan* pl) {
+  pkv_status st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (B < 0 || n_q <= 0 || n_q % desc->n_kv != 0 || prefix_len < 0 || max_suffix_len < 0 ||
+      prefix_partition < 0 || suffix_partition < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (prefix_len % desc->block_size != 0) return PKV_ERR_INVALID_ARG;
+  if ((prefix_partition % desc->block_size) != 0 || (suffix_partition % desc->block_size) != 0)
+    return PKV_ERR_INVALID_ARG;
+  *pl = CascadePlan{};
+  if (prefix_len > 0) {
+    // the sharers' (sequence, head) rows are the query rows of one prefix pass
+    pl->Pp = prefix_partition > 0 ? prefix_partition
+                                  : pick_partition_mq(desc, 1, B, n_q, prefix_len);
+    if (pl->Pp >= prefix_len) pl->Pp = prefix_len;
+    pl->Pp_max = static_cast<int32_t>(cdiv(prefix_len, pl->Pp));
+    pl->prefix_bytes = workspace_bytes(B, n_q, desc->d_head, pl->Pp_max);
+  }
+  if (max_suffix_len > 0) {
+    pl->Ps = suffix_partition > 0 ? suffix_partition
+                                  : pick_partition(desc, B, n_q, max_suffix_len);
+    pl->Ps_max = static_cast<int32_t>(cdiv(max_suffix_len, pl->Ps));
+    pl->suffix_bytes = workspace_bytes(B, n_q, desc->d_head, pl->Ps_max);
+  }
+  if (static_cast<int64_t>(pl->Pp_max) + pl->Ps_max > kMaxReducePartitions)
+    return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+}  // namespace
+
+size_t pkv_cascade_workspace_bytes(const pkv_cache_desc* desc, int32_t B, int32_t n_q,
+                                   int32_t prefix_len, int32_t prefix_partition,
+                                   int32_t max_suffix_len, int32_t suffix_partition) {
+  CascadePlan pl;
+  if (plan_cascade(desc, B, n_q, prefix_len, prefix_partition, max_suffix_len,
+                   suffix_partition, &pl) != PKV_OK)
+    return 0;
+  return pl.prefix_bytes + pl.suffix_bytes;
+}
+
+pkv_status pkv_cascade_decode_attention(
+    const pkv_cache_desc* desc, void* out, int32_t out_dtype, const void* q, const void* k_cache,
+    const void* v_cache, const int32_t* prefix_table, int32_t prefix_len,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* suffix_lens,
+    int32_t B, int32_t n_q, int32_t max_suffix_len, float scale, const float* k_scale,
+    const float* v_scale, int32_t prefix_partition, int32_t suffix_partition, void* workspace,
+    size_t workspace_bytes_, void* stream) {
+  CascadePlan pl;
+  pkv_status st = plan_cascade(desc, B, n_q, prefix_len, prefix_partition, max_suffix_len,
+                               suffix_partition, &pl);
+  if (st != PKV_OK) return st;
+  if (out_dtype != PKV_FP32 && out_dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !suffix_lens || !block_tables)
+    return PKV_ERR_INVALID_ARG;
+  if (prefix_len > 0 && !prefix_table) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
+  if (desc->kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (!pkv::decode_supported(desc->d_head, desc->block_size, n_q / desc->n_kv, desc->kv_dtype))
+    return PKV_ERR_UNSUPPORTED;
+  if (B > 65535 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_suffix_len) >
+      static_cast<int64_t>(max_blocks_per_seq) * desc->block_size)
+    return PKV_ERR_INVALID_ARG;
+  const size_t need = pl.prefix_bytes + pl.suffix_bytes;
+  if (need > 0 && (!workspace || workspace_bytes_ < need)) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && !aligned16(workspace)) return PKV_ERR_INVALID_ARG;
+  const hipStream_t s = as_stream(stream);
+  char* ws = static_cast<char*>(workspace);
+
+  Workspace wp{}, wsuf{};
+  if (pl.Pp_max > 0) {
+    // prefix pass: one virtual sequence whose B query tokens are the sharers,
+    // every row seeing the whole prefix
+    wp = carve(ws, B, n_q, pl.Pp_max);
+    pkv::DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint8_t*>(k_cache);
+    a.v_cache = static_cast<const uint8_t*>(v_cache);
+    a.block_tables = prefix_table;
+    a.context_lens = nullptr;
+    a.fixed_ctx = prefix_len;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.B = 1;
+    a.Q = B;
+    a.non_causal = true;
+    a.n_q = n_q;
+    a.n_kv = desc->n_kv;
+    a.d = desc->d_head;
+    a.bs = desc->block_size;
+    a.num_blocks = desc->num_blocks;
+    a.max_blocks = prefix_len / desc->block_size;
+    a.kv_dtype = desc->kv_dtype;
+    a.partition = pl.Pp;
+    a.P_max = pl.Pp_max;
+    a.scale = scale;
+    a.write_partials = true;
+    a.ws_m = wp.m;
+    a.ws_l = wp.l;
+    a.ws_o = wp.o;
+    hipError_t e = pkv::launch_multi_query_partition(a, s);
+    if (e != hipSuccess) return PKV_ERR_HIP;
+  }
+  if (pl.Ps_max > 0) {
+    wsuf = carve(ws + pl.prefix_bytes, B, n_q, pl.Ps_max);
+    pkv::DecodeArgs a;
+    st = prepare_decode(desc, q, k_cache, v_cache, block_tables, max_blocks_per_seq, suffix_lens,
+                        B, n_q, max_suffix_len, scale, k_scale, v_scale, pl.Ps, &a);
+    if (st != PKV_OK) return st;
+    a.ws_m = wsuf.m;
+    a.ws_l = wsuf.l;
+    a.ws_o = wsuf.o;
+    a.write_partials = true;
+    a.wave_partitions = use_wave_partitions(a.partition);
+    hipError_t e = pkv::launch_decode_partition(a, s);
+    if (e != hipSuccess) return PKV_ERR_HIP;
+  } else {
+    wsuf = wp;                       // no suffix partitions: never read (np = 0)
+  }
+  return from_hip(pkv::launch_splitk_reduce(
+      out, out_dtype, wsuf.m, wsuf.l, wsuf.o, suffix_lens, B, n_q, desc->d_head,
+      pl.Ps_max > 0 ? pl.Ps_max : 1, pl.Ps > 0 ? pl.Ps : 1, s, 1, nullptr,
+      max_blocks_per_seq * desc->block_size, pl.Pp_max > 0 ? wp.m : nullptr, wp.l, wp.o,
+      pl.Pp_max));
+}
+
 size_t pkv_swap_bytes(const pkv_cache_desc* desc, int32_t n_blocks) {
   if (check_desc(desc) != PKV_OK || n_blocks < 0) return 0;
   return static_cast<size_t>(2 * static_cast<int64_t>(n_blocks) * pkv::swap_block_bytes(*desc));

@@ -276,10 +276,16 @@ __device__ __forceinline__ float wave_sum(float x) {
 // a row reads every partition of its context, otherwise query i of q_len sits
 // at position ctx - q_len + i and reads only the partitions up to it; rows past
 // q_len read none and are written as zeros.
+// A second source (m2, l2, o2: P2 partitions per row, all present) is merged
+// after a row's own partitions: the shared-prefix partials of a cascade.
 struct ReduceRows {
   const int32_t* context_lens;
   const int32_t* query_lens;
   int Q, n_q, P_max, partition, ctx_cap;
+  const float* m2;
+  const float* l2;
+  const float* o2;
+  int P2;
 };
 
 __device__ __forceinline__ int row_partitions(const ReduceRows& r, int64_t row) {
@@ -306,13 +312,21 @@ __global__ __launch_bounds__(256) void splitk_reduce_wave_kernel(
   const int64_t bh = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (bh >= n_rows) return;                          // whole wave
   const int P_max = rows.P_max;
-  const int np = row_partitions(rows, bh);
+  const int np1 = row_partitions(rows, bh);
+  const int np = np1 + rows.P2;
   const float* mb = m + static_cast<int64_t>(bh) * P_max;
   const float* lb = l + static_cast<int64_t>(bh) * P_max;
   const float* ob = o + static_cast<int64_t>(bh) * P_max * D;
+  const float* mb2 = rows.m2 + static_cast<int64_t>(bh) * rows.P2;
+  const float* lb2 = rows.l2 + static_cast<int64_t>(bh) * rows.P2;
+  const float* ob2 = rows.o2 + static_cast<int64_t>(bh) * rows.P2 * D;
+  auto pm = [&](int j) { return j < np1 ? mb[j] : mb2[j - np1]; };
+  auto pl = [&](int j) { return j < np1 ? lb[j] : lb2[j - np1]; };
+  auto po = [&](int j) { return j < np1 ? ob + static_cast<int64_t>(j) * D
+                                        : ob2 + static_cast<int64_t>(j - np1) * D; };
 
   float mx = -INFINITY;
-  for (int jj = lane; jj < np; jj += 64) mx = fmaxf(mx, mb[jj]);
+  for (int jj = lane; jj < np; jj += 64) mx = fmaxf(mx, pm(jj));
   const float M = wave_max(mx);
   float acc[DL];
 #pragma unroll
@@ -320,12 +334,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_wave_kernel(
   float lsum = 0.0f;
   for (int j0 = 0; j0 < np; j0 += 64) {
     const int jl = j0 + lane;
-    const float wl = jl < np ? lb[jl] * fast_exp2(mb[jl] - M) : 0.0f;
+    const float wl = jl < np ? pl(jl) * fast_exp2(pm(jl) - M) : 0.0f;
     lsum += wl;
     const int n = min(64, np - j0);
     for (int jj = 0; jj < n; ++jj) {
       const float wj = __shfl(wl, jj);
-      const float* row = ob + static_cast<int64_t>(j0 + jj) * D;
+      const float* row = po(j0 + jj);
 #pragma unroll
       for (int k = 0; k < DL; ++k) acc[k] = fmaf(wj, row[lane + 64 * k], acc[k]);
     }
@@ -358,13 +372,21 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
   const int wv = t >> 6;
   const int64_t bh = blockIdx.x;
   const int P_max = rows.P_max;
-  const int np = row_partitions(rows, bh);
+  const int np1 = row_partitions(rows, bh);
+  const int np = np1 + rows.P2;
   const float* mb = m + static_cast<int64_t>(bh) * P_max;
   const float* lb = l + static_cast<int64_t>(bh) * P_max;
   const float* ob = o + static_cast<int64_t>(bh) * P_max * D;
+  const float* mb2 = rows.m2 + static_cast<int64_t>(bh) * rows.P2;
+  const float* lb2 = rows.l2 + static_cast<int64_t>(bh) * rows.P2;
+  const float* ob2 = rows.o2 + static_cast<int64_t>(bh) * rows.P2 * D;
+  auto pm = [&](int j) { return j < np1 ? mb[j] : mb2[j - np1]; };
+  auto pl = [&](int j) { return j < np1 ? lb[j] : lb2[j - np1]; };
+  auto po = [&](int j) { return j < np1 ? ob + static_cast<int64_t>(j) * D
+                                        : ob2 + static_cast<int64_t>(j - np1) * D; };
 
   float mx = -INFINITY;
-  for (int jj = t; jj < np; jj += 256) mx = fmaxf(mx, mb[jj]);
+  for (int jj = t; jj < np; jj += 256) mx = fmaxf(mx, pm(jj));
   mx = wave_max(mx);
   if (lane == 0) red[wv] = mx;
   __syncthreads();
@@ -372,7 +394,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
   __syncthreads();
   float ls = 0.0f;
   for (int jj = t; jj < np; jj += 256) {
-    const float wj = lb[jj] * fast_exp2(mb[jj] - M);
+    const float wj = pl(jj) * fast_exp2(pm(jj) - M);
     w[jj] = wj;
     ls += wj;
   }
@@ -386,7 +408,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (int jj = pg; jj < np; jj += PG) {
     const float wj = w[jj];
-    const float4 v = *reinterpret_cast<const float4*>(ob + static_cast<int64_t>(jj) * D + 4 * dg);
+    const float4 v = *reinterpret_cast<const float4*>(po(jj) + 4 * dg);
     acc.x = fmaf(wj, v.x, acc.x);
     acc.y = fmaf(wj, v.y, acc.y);
     acc.z = fmaf(wj, v.z, acc.z);
@@ -468,11 +490,13 @@ hipError_t launch_decode_partition(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_splitk_reduce(void* out, int out_dtype, const float* m, const float* l,
                                 const float* o, const int32_t* context_lens, int B, int n_q,
                                 int d, int P_max, int partition, hipStream_t stream, int Q,
-                                const int32_t* query_lens, int ctx_cap) {
-  if (P_max > kMaxReducePartitions || (d != 64 && d != 128)) return hipErrorInvalidValue;
-  const ReduceRows rows{context_lens, query_lens, Q, n_q, P_max, partition, ctx_cap};
+                                const int32_t* query_lens, int ctx_cap, const float* m2,
+                                const float* l2, const float* o2, int P2) {
+  if (P_max + P2 > kMaxReducePartitions || (d != 64 && d != 128)) return hipErrorInvalidValue;
+  const ReduceRows rows{context_lens, query_lens, Q, n_q, P_max, partition, ctx_cap,
+                        m2, l2, o2, m2 ? P2 : 0};
   const int64_t n_rows = static_cast<int64_t>(B) * Q * n_q;
-  if (P_max <= kWaveReduceMaxPartitions) {
+  if (P_max + rows.P2 <= kWaveReduceMaxPartitions) {
     const unsigned grid = static_cast<unsigned>((n_rows + 3) / 4);
     if (d == 128)
       splitk_reduce_wave_kernel<128><<<grid, 256, 0, stream>>>(out, out_dtype, m, l, o, rows,

@@ -77,14 +77,18 @@ void multi_query_lds_mfma(DecodeArgs a) {
   const int row0 = (wid % groups) * GR;
   const int b = blockIdx.y;
   const int j = gridDim.z - 1 - blockIdx.z;
-  const int ctx = min(a.context_lens[b], a.max_blocks * BS);
-  const int ql = max(0, min(min(a.query_lens[b], a.Q), ctx));
+  const int ctx = min(a.context_lens ? a.context_lens[b] : a.fixed_ctx, a.max_blocks * BS);
+  // causal: query i of q_len sits at position ctx - q_len + i; non-causal
+  // (a shared prefix read for many sequences' queries): every row sees all
+  const int ql = a.non_causal ? (ctx > 0 ? a.Q : 0)
+                              : max(0, min(min(a.query_lens[b], a.Q), ctx));
+  auto qpos = [&](int i) -> int { return a.non_causal ? ctx - 1 : ctx - ql + i; };
   const int t0 = j * a.partition;
 
   // last position among rows [r0, r1), or -1 if none of them has a query
   auto last_pos = [&](int r0, int r1) -> int {
     const int i_hi = min((min(r1, rows) - 1) / G, ql - 1);
-    return r0 / G < ql && r0 < rows ? ctx - ql + i_hi : -1;
+    return r0 / G < ql && r0 < rows ? qpos(i_hi) : -1;
   };
   const int p_grp = last_pos(row0, row0 + GR);
   if (t0 > p_grp) {
@@ -111,7 +115,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
 
   // this wave's rows
   const int wrow0 = row0 + wave * TPW * 16;
-  const int p_lo = ctx - ql + wrow0 / G;
+  const int p_lo = qpos(wrow0 / G);
   auto dimbase = [&](int kk) -> int {
     return FP8 ? 64 * (kk >> 1) + 16 * g4 + 8 * (kk & 1) : 32 * kk + 8 * g4;
   };
@@ -122,7 +126,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
     const int row = wrow0 + 16 * t + c;
     const int qi = row / G;
     const bool live_row = row < rows && qi < ql;
-    pos[t] = ctx - ql + qi;
+    pos[t] = qpos(qi);
     const int64_t qrow =
         live_row ? (static_cast<int64_t>(b) * a.Q + qi) * a.n_q + g * G + row % G : 0;
 #pragma unroll

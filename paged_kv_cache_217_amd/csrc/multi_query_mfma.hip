@@ -71,8 +71,12 @@ void multi_query_partition_mfma(DecodeArgs a) {
   const int row0 = (blockIdx.x % groups) * GR;        // first row of the group
   const int b = blockIdx.y;
   const int j = gridDim.z - 1 - blockIdx.z;
-  const int ctx = min(a.context_lens[b], a.max_blocks * BS);
-  const int ql = max(0, min(min(a.query_lens[b], a.Q), ctx));
+  const int ctx = min(a.context_lens ? a.context_lens[b] : a.fixed_ctx, a.max_blocks * BS);
+  // causal: query i of q_len sits at position ctx - q_len + i; non-causal
+  // (a shared prefix read for many sequences' queries): every row sees all
+  const int ql = a.non_causal ? (ctx > 0 ? a.Q : 0)
+                              : max(0, min(min(a.query_lens[b], a.Q), ctx));
+  auto qpos = [&](int i) -> int { return a.non_causal ? ctx - 1 : ctx - ql + i; };
   const int t0 = j * a.partition;
 
   __shared__ float sm_m[NW][TPW * 16];
@@ -82,7 +86,7 @@ void multi_query_partition_mfma(DecodeArgs a) {
   // last position of the query among rows [r0, r1) (r1 > r0), or -1 if none
   auto last_pos = [&](int r0, int r1) -> int {
     const int i_hi = min((min(r1, rows) - 1) / G, ql - 1);
-    return r0 / G < ql && r0 < rows ? ctx - ql + i_hi : -1;
+    return r0 / G < ql && r0 < rows ? qpos(i_hi) : -1;
   };
   if (t0 > last_pos(row0, row0 + GR)) {
     // no row of this group reads this partition; a single pass still owes the
@@ -106,7 +110,7 @@ void multi_query_partition_mfma(DecodeArgs a) {
   const int tl = wave % R;
   const int st = wave / R;
   const int wrow0 = row0 + tl * TPW * 16;             // first row of the wave
-  const int p_lo = ctx - ql + wrow0 / G;              // smallest position of the wave
+  const int p_lo = qpos(wrow0 / G);              // smallest position of the wave
   const int p_hi = last_pos(wrow0, wrow0 + TPW * 16); // largest (-1: none)
   const int t1 = min(t0 + a.partition, p_hi + 1);    // tokens past p_hi are never read
   const int blk0 = t0 / BS;
@@ -123,7 +127,7 @@ void multi_query_partition_mfma(DecodeArgs a) {
     const int row = wrow0 + 16 * t + c;
     const int qi = row / G;
     const bool live_row = row < rows && qi < ql;
-    pos[t] = ctx - ql + qi;                           // last token this row may see
+    pos[t] = qpos(qi);                           // last token this row may see
     const int64_t qrow =
         live_row ? (static_cast<int64_t>(b) * a.Q + qi) * a.n_q + g * G + row % G : 0;
 #pragma unroll

@@ -38,6 +38,8 @@ struct DecodeArgs {
   // q is [B, Q, n_q, d], out and partial rows are (sequence, query, head)
   int Q;                      // 1 for single-token decode
   const int32_t* query_lens;  // [B]; nullptr for single-token decode
+  bool non_causal;            // multi-query only: every row sees the whole context
+  int fixed_ctx;              // context length of every sequence when context_lens is null
 };
 
 // Schedule buffer: int32 header of kScheduleHeader words, then int2 items.
@@ -53,7 +55,9 @@ hipError_t launch_splitk_reduce(void* out, int out_dtype, const float* m, const 
                                 const float* o, const int32_t* context_lens, int B, int n_q,
                                 int d, int P_max, int partition, hipStream_t stream,
                                 int Q = 1, const int32_t* query_lens = nullptr,
-                                int ctx_cap = INT32_MAX);
+                                int ctx_cap = INT32_MAX, const float* m2 = nullptr,
+                                const float* l2 = nullptr, const float* o2 = nullptr,
+                                int P2 = 0);
 hipError_t launch_multi_query_partition(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_multi_query_lds(const DecodeArgs& a, hipStream_t stream);
 

@@ -1,0 +1,85 @@
+"""GPU parity of shared-prefix (cascade) decode attention against the oracle.
+
+Bars as for decode (max abs 1e-2 BF16 / 3e-2 FP8, relative L2 1e-4), and
+agreement with plain decode attention over the concatenated tables. Cases
+put the prefix rows (sequences x G) on both multi-query kernels (fewer and
+more than 128 rows per KV head), cover FP8, MQA, an empty prefix, empty
+suffixes, ragged suffixes with NaN-poisoned tails, and explicit partitions.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import paged as ref
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+MAX_ABS = {W.BF16: 1e-2, W.FP8: 3e-2}
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_217_amd as m
+    return m
+
+
+def shared_prefix_case(suffix, prefix_len, n_q, n_kv, d, bs, dtype, seed):
+    """Sequence 0 of the generated structure is the prefix; the rest are suffixes."""
+    w = W.custom("cascade", [prefix_len] + list(suffix), n_q, n_kv, d, bs, dtype, seed=seed)
+    kc, vc, ks, vs = W.make_cache(w)
+    prefix_table = w.block_tables[0, :max(1, prefix_len // bs)].copy()
+    tables = np.ascontiguousarray(w.block_tables[1:])
+    slen = np.array(suffix, dtype=np.int32)
+    B = len(suffix)
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, n_q, d), generator=g).to(torch.bfloat16)
+    return w, kc, vc, ks, vs, prefix_table, tables, slen, q
+
+
+CASES = [
+    # suffix lengths, prefix_len, n_q, n_kv, d, bs, dtype, prefix partition, suffix partition
+    ([5, 0, 40, 129], 64, 8, 2, 64, 16, W.BF16, 0, 0),           # 16 prefix rows: register kernel
+    ([300, 17, 1000], 4096, 64, 8, 128, 16, W.BF16, 0, 0),
+    ([1, 50, 260, 33, 7, 900, 64, 12, 300, 5, 120, 77, 1, 2, 3, 400, 18, 19, 20, 21],
+     2048, 64, 8, 128, 16, W.BF16, 0, 0),                        # 160 prefix rows: LDS kernel
+    ([100, 0, 700], 1024, 64, 8, 128, 32, W.FP8, 256, 64),
+    ([33, 1], 512, 64, 1, 128, 16, W.BF16, 128, 0),              # MQA: 128 rows
+    ([40, 97], 0, 16, 8, 128, 16, W.BF16, 0, 0),                 # no prefix
+    ([0, 0, 0], 1024, 64, 8, 128, 16, W.BF16, 0, 0),             # no suffix
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
+def test_cascade_matches_oracle_and_plain_decode(pkv, case):
+    suffix, plen, n_q, n_kv, d, bs, dt, Pp, Ps = case
+    w, kc, vc, ks, vs, pt, tables, slen, q = shared_prefix_case(
+        suffix, plen, n_q, n_kv, d, bs, dt, seed=100 + CASES.index(case))
+    t = lambda x: None if x is None else x.to(DEV)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    max_s = int(slen.max())
+    out = pkv.cascade_decode_attention(
+        q.to(DEV), kd, vd, torch.from_numpy(pt).to(DEV), plen, torch.from_numpy(tables).to(DEV),
+        torch.from_numpy(slen).to(DEV), w.scale, max_s, k_scale=t(ks), v_scale=t(vs),
+        prefix_partition=Pp, suffix_partition=Ps)
+    # the same attention through plain decode on the concatenated tables
+    full = np.concatenate([np.tile(pt[:plen // bs], (len(suffix), 1)), tables], axis=1)
+    cl = (plen + slen).astype(np.int32)
+    plain = pkv.paged_decode_attention(q.to(DEV), kd, vd, torch.from_numpy(full).to(DEV),
+                                       torch.from_numpy(cl).to(DEV), w.scale, int(cl.max()),
+                                       k_scale=t(ks), v_scale=t(vs))
+    torch.cuda.synchronize()
+    expect = ref.cascade_decode_attention(W.bits(q), W.bits(kc), W.bits(vc), pt, plen, tables,
+                                          slen, w.scale, dt,
+                                          None if ks is None else ks.numpy(),
+                                          None if vs is None else vs.numpy())
+    got = out.cpu().double().numpy()
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - expect))
+    rel = np.linalg.norm(got - expect) / max(np.linalg.norm(expect), 1e-30)
+    assert err <= MAX_ABS[dt], f"max abs error {err:.3e}"
+    assert rel <= 1e-4, f"relative L2 {rel:.3e}"
+    assert np.max(np.abs(got - plain.cpu().double().numpy())) <= 2 * MAX_ABS[dt] / 10
