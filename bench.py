@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gqa_70b",
                     choices=["gqa_70b", "mha_7b", "gqa_70b_fp8", "long_prefix", "tiny",
-                             "spec_verify_70b", "chunked_prefill_70b"])
+                             "spec_verify_70b", "chunked_prefill_70b", "shared_prompt_70b"])
     ap.add_argument("--layers", type=int, default=0, help="override layer count (0: workload's)")
     ap.add_argument("--partition", type=int, default=0, help="split-K partition (0: library)")
     ap.add_argument("--schedule", type=int, default=1,
@@ -121,6 +121,9 @@ def main():
     w = W.ALL[args.workload]()
     if w.Q > 1:
         bench_multi_query(args, w, pkv, W, np, torch, dev)
+        return
+    if w.notes.get("prefix_len"):
+        bench_cascade(args, w, pkv, W, np, torch, dev)
         return
     layers = args.layers or w.layers
     B, n_q, n_kv, d, bs = w.B, w.n_q, w.n_kv, w.d, w.bs
@@ -344,6 +347,106 @@ def bench_swap(args, pkv, W, np, torch, dev):
         "roofline": {"bound": "host link", "achieved": round(gb / (t_out * 1e-3), 2),
                      "peak": 64.0, "unit": "GB/s", "frac": round(gb / (t_out * 1e-3) / 64.0, 4),
                      "note": "peak = PCIe 5.0 x16 nominal per direction", "traffic": None},
+    }
+    print(json.dumps(result), flush=True)
+
+
+def bench_cascade(args, w, pkv, W, np, torch, dev):
+    """A batch sharing a prompt prefix: per layer, kv_append of the new token,
+    then decode attention through pkv_cascade_decode_attention (prefix read
+    once) and, for comparison, through plain decode on the same full tables."""
+    layers = args.layers or w.layers
+    B, n_q, n_kv, d, bs = w.B, w.n_q, w.n_kv, w.d, w.bs
+    plen = w.notes["prefix_len"]
+    pb = plen // bs
+    caches = [W.make_cache(w, device=dev, seed_offset=1000 * layer, poison_unused=False)
+              for layer in range(layers)]
+    q = W.make_query(w, device=dev, layers=layers) if layers > 1 else W.make_query(w, device=dev)[None]
+    k_new, v_new = W.make_new_tokens(w, T=layers * B, device=dev)
+    k_new = k_new.view(layers, B, n_kv, d)
+    v_new = v_new.view(layers, B, n_kv, d)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    cl = torch.from_numpy(w.context_lens).to(dev)
+    pt = torch.from_numpy(w.block_tables[0, :pb].copy()).to(dev)
+    st = torch.from_numpy(np.ascontiguousarray(w.block_tables[:, pb:])).to(dev)
+    slen_np = (w.context_lens - plen).astype(np.int32)
+    slen = torch.from_numpy(slen_np).to(dev)
+    max_ctx, max_s = int(w.context_lens.max()), int(slen_np.max())
+    pos = torch.from_numpy((w.context_lens - 1).astype(np.int32)).to(dev)
+    slots = torch.empty(B, dtype=torch.int64, device=dev)
+    out = torch.empty((B, n_q, d), dtype=torch.float32, device=dev)
+    desc = pkv.cache_desc(caches[0][0])
+    import ctypes
+    cws = torch.empty(max(16, pkv.lib().pkv_cascade_workspace_bytes(
+        ctypes.byref(desc), B, n_q, plen, 0, max_s, args.partition)), dtype=torch.uint8,
+        device=dev)
+    P = pkv.default_partition_size(caches[0][0], B, n_q, max_ctx)
+    dws, _ = pkv.make_workspace(caches[0][0], B, n_q, max_ctx, P)
+    stream = torch.cuda.current_stream()
+    log(f"[bench] workload {w.name}: B={B} prefix={plen} suffix {slen_np.min()}..{max_s} "
+        f"layers={layers}")
+
+    def step(cascade, ev=None):
+        pkv.slot_mapping(bt, pos, bs, out=slots)
+        for layer in range(layers):
+            kc, vc, ks, vs = caches[layer]
+            pkv.kv_append(kc, vc, k_new[layer], v_new[layer], slots, ks, vs)
+            if ev is not None:
+                ev[layer][0].record(stream)
+            if cascade:
+                pkv.cascade_decode_attention(q[layer], kc, vc, pt, plen, st, slen, w.scale, max_s,
+                                             suffix_partition=args.partition, out=out,
+                                             workspace=cws)
+            else:
+                pkv.paged_decode_attention(q[layer], kc, vc, bt, cl, w.scale, max_ctx,
+                                           partition_size=P, out=out, workspace=dws)
+            if ev is not None:
+                ev[layer][1].record(stream)
+
+    res = {}
+    for cascade in (True, False):
+        for _ in range(args.warmup):
+            step(cascade)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step(cascade)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(layers)]
+              for _ in range(args.steps)]
+        for s_ in range(args.steps):
+            step(cascade, ev[s_])
+        torch.cuda.synchronize()
+        att = [e[0].elapsed_time(e[1]) for st_ in ev for e in st_]
+        res[cascade] = (e0.elapsed_time(e1) / args.steps, sum(att) / len(att))
+        log(f"[bench] {'cascade' if cascade else 'plain'}: {res[cascade][0]:.3f} ms/step, "
+            f"attention {res[cascade][1] * 1000:.1f} us/layer")
+    ms_step, ms_att = res[True]
+    row = n_kv * d * w.p * 2
+    unique = (plen + int(slen_np.sum())) * row          # prefix once + every suffix
+    logical = int(w.context_lens.sum()) * row            # what each sequence attends over
+    att_bytes = unique + B * n_q * d * (2 + 4) + (pb + sum(-(-int(x) // bs) for x in slen_np)) * 4
+    achieved = att_bytes / (ms_att * 1e-3) / 1e9
+    result = {
+        "metric": "shared-prefix decode attention: decode tokens/s",
+        "value": round(B / (ms_step * 1e-3 / layers), 1), "unit": "decode tokens/s per layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "prefix_len": plen,
+                   "suffix_partition": args.partition or "library default",
+                   "suffix_len": [int(slen_np.min()), max_s], "n_q": n_q, "n_kv": n_kv,
+                   "d_head": d, "block_size": bs, "layers": layers, "kv_dtype": w.kv_dtype},
+        "attention_us_per_layer": {"cascade": round(ms_att * 1000, 1),
+                                   "plain_decode": round(res[False][1] * 1000, 1)},
+        "speedup_vs_plain_decode": round(res[False][1] / ms_att, 2),
+        "logical_kv_gbs": round(logical / (ms_att * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "cascade (prefix pass + suffix partitions + merge)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": att_bytes,
+                     "traffic": None},
     }
     print(json.dumps(result), flush=True)
 

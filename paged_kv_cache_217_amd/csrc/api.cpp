@@ -41,15 +41,19 @@ int32_t pick_partition(const pkv_cache_desc* d, int32_t B, int32_t n_q, int32_t 
       static_cast<int64_t>(B) * d->n_kv * ((G + head_tile(G) - 1) / head_tile(G)), max_ctx);
 }
 
-// Multi-query workgroups each own 16 (query, head) rows of one KV head. A
-// launch whose row tiles alone fill four rounds of the chip runs in a single
-// pass: splitting it would only add partials (fp32, d_head + 2 words per row
-// and partition) that outweigh the K/V a prompt chunk reads.
+// Workgroups of a multi-query launch per partition: the LDS kernel takes 128
+// (query, head) rows of a KV head per workgroup, the register kernel 32 (two
+// 16-row tiles) or one tile. A launch that fills a round of the chip this way
+// runs in a single pass: splitting it would only add partials (fp32,
+// d_head + 2 words per row and partition), which for a prompt chunk outweigh
+// the K/V it reads. Fewer workgroups split the context as decode does.
 int32_t pick_partition_mq(const pkv_cache_desc* d, int32_t B, int32_t Q, int32_t n_q,
                           int32_t max_ctx) {
   const int64_t rows = static_cast<int64_t>(Q) * (n_q / d->n_kv);
-  const int64_t units = static_cast<int64_t>(B) * d->n_kv * cdiv(rows, 16);
-  if (units >= 4 * 512) return static_cast<int32_t>(std::max<int64_t>(32, cdiv(max_ctx, 32) * 32));
+  const int64_t tiles = cdiv(rows, 16);
+  const int64_t per_head = tiles >= 8 ? cdiv(rows, 128) : (tiles >= 2 ? cdiv(tiles, 2) : 1);
+  const int64_t units = static_cast<int64_t>(B) * d->n_kv * per_head;
+  if (units >= 512) return static_cast<int32_t>(std::max<int64_t>(32, cdiv(max_ctx, 32) * 32));
   return pick_partition_units(units, max_ctx);
 }
 

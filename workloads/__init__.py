@@ -211,9 +211,33 @@ def chunked_prefill_70b(layers=4):
                     query_lens=np.full(4, 512, dtype=np.int32))
 
 
+def shared_prompt_70b(layers=8):
+    """64 sequences sharing a 16384-token prompt (1024 blocks, the same physical
+    blocks in every table) followed by private suffixes of U{256..4096} tokens;
+    64/8 heads, d=128, bs=16, bf16."""
+    g = _gen(STRUCT_SEED + 8)
+    B, bs, prefix = 64, 16, 16384
+    suffix = torch.randint(256, 4097, (B,), generator=g).numpy().astype(np.int32)
+    pb = prefix // bs
+    need = [-(-int(x) // bs) for x in suffix]
+    pool = pb + sum(need)
+    perm = torch.randperm(pool, generator=g).numpy().astype(np.int32)
+    mb = pb + max(need)
+    bt = np.zeros((B, mb), dtype=np.int32)
+    bt[:, :pb] = perm[:pb]
+    at = pb
+    for b, n in enumerate(need):
+        bt[b, pb:pb + n] = perm[at:at + n]
+        at += n
+    ctx = (prefix + suffix).astype(np.int32)
+    return Workload("shared_prompt_70b", B, 64, 8, 128, bs, BF16, ctx, bt, pool,
+                    1.0 / math.sqrt(128), layers=layers, shared_prefix_blocks=pb,
+                    notes={"seed": 8, "prefix_len": prefix})
+
+
 ALL = {"tiny": tiny, "mha_7b": mha_7b, "gqa_70b": gqa_70b, "gqa_70b_fp8": gqa_70b_fp8,
        "long_prefix": long_shared_prefix, "spec_verify_70b": spec_verify_70b,
-       "chunked_prefill_70b": chunked_prefill_70b}
+       "chunked_prefill_70b": chunked_prefill_70b, "shared_prompt_70b": shared_prompt_70b}
 
 
 # ---------------------------------------------------------------- values
