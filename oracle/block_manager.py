@@ -36,6 +36,27 @@ memory and promoted back to HBM with asynchronous copies). Readings:
     and change nothing;
   * a swapped sequence cannot append, fork or export its table; free() drops
     it.
+
+Prefix cache ([LLMI] "8. Design Alternatives": a hash prefix cache over
+16/32-token blocks, and an LRU radix tree over paged blocks; [SMTS] "Paged
+KV-Cache with Radix Tree Prefix Cache": requests sharing a system prompt
+reference the same physical blocks). Readings:
+  * the cache is a radix tree whose nodes are full blocks, each keyed under
+    its parent by its block_size token ids (exact: no hashing collisions);
+  * match_prefix(seq, tokens) on a new sequence shares the longest chain of
+    cached blocks that equals whole blocks of `tokens` (ref + 1 each) and
+    makes them its table; it returns the number of tokens matched;
+  * cache_prefix(seq, tokens) registers the sequence's first
+    len(tokens) // block_size blocks under that chain; a block whose key is
+    already cached (by another block) is left out, and so is everything after
+    it;
+  * a cached block whose count drops to 0 is not returned to the pool but
+    becomes evictable; matching it again revives it;
+  * allocation pops the free pool; when it is empty, the least recently used
+    evictable block with no cached children is evicted (its key removed) and
+    used instead; "use" is a match, a registration or a release to count 0,
+    stamped from one counter;
+  * num_free counts the pool only.
 """
 
 
@@ -51,13 +72,93 @@ class BlockManagerModel:
         self.tables = {}
         self.lens = {}
         self.swapped = set()
+        self.node_of = {}        # cached block -> (parent block or None, token tuple)
+        self.children = {}       # (parent block or None, token tuple) -> cached block
+        self.n_children = {}     # cached block -> number of cached children
+        self.stamp = {}          # cached block -> last use
+        self.clock = 0
+
+    def _tick(self, blk):
+        self.clock += 1
+        self.stamp[blk] = self.clock
+
+    def _evictable(self):
+        return [b for b in self.node_of if self.ref[b] == 0 and self.n_children[b] == 0]
+
+    def _uncache(self, blk):
+        parent, key = self.node_of.pop(blk)
+        del self.children[(parent, key)]
+        del self.n_children[blk]
+        del self.stamp[blk]
+        if parent is not None:
+            self.n_children[parent] -= 1
 
     def _pop(self):
         if not self.free_pool:
-            raise OutOfBlocks("KV block pool exhausted; preempt a sequence")
+            victims = self._evictable()
+            if not victims:
+                raise OutOfBlocks("KV block pool exhausted; preempt a sequence")
+            blk = min(victims, key=lambda b: self.stamp[b])
+            self._uncache(blk)
+            self.ref[blk] += 1
+            return blk
         blk = self.free_pool.pop()
         self.ref[blk] += 1
         return blk
+
+    def _release(self, blk):
+        self.ref[blk] -= 1
+        if self.ref[blk] == 0:
+            if blk in self.node_of:
+                self._tick(blk)              # evictable, keeps its data and key
+            else:
+                self.free_pool.append(blk)
+
+    def match_prefix(self, seq, tokens):
+        """Share the longest cached chain of whole blocks of `tokens` with a new sequence."""
+        if seq in self.tables or seq in self.swapped:
+            raise KeyError("match_prefix needs a new sequence")
+        bs = self.block_size
+        parent, blocks = None, []
+        for i in range(len(tokens) // bs):
+            blk = self.children.get((parent, tuple(tokens[i * bs:(i + 1) * bs])))
+            if blk is None:
+                break
+            blocks.append(blk)
+            parent = blk
+        for blk in blocks:
+            self.ref[blk] += 1
+            self._tick(blk)
+        self.tables[seq] = blocks
+        self.lens[seq] = len(blocks) * bs
+        return len(blocks) * bs
+
+    def cache_prefix(self, seq, tokens):
+        """Register the sequence's first len(tokens) // block_size blocks in the cache."""
+        if seq not in self.tables:
+            raise KeyError("cache_prefix needs a resident sequence")
+        bs = self.block_size
+        n = len(tokens) // bs
+        table = self.tables[seq]
+        if n > len(table) or n * bs > self.lens[seq]:
+            raise ValueError("more tokens than the sequence holds")
+        parent = None
+        for i in range(n):
+            key = (parent, tuple(tokens[i * bs:(i + 1) * bs]))
+            blk = table[i]
+            have = self.children.get(key)
+            if have is None:
+                if blk in self.node_of:          # cached under another key: stop
+                    break
+                self.children[key] = blk
+                self.node_of[blk] = key
+                self.n_children[blk] = 0
+                if parent is not None:
+                    self.n_children[parent] += 1
+            elif have != blk:
+                break                            # the prefix is cached by other blocks
+            self._tick(blk)
+            parent = blk
 
     def append_slot(self, seq):
         """Reserve the next token slot of `seq`; returns (slot, cow_src, cow_dst)."""
@@ -93,9 +194,7 @@ class BlockManagerModel:
             del self.lens[seq]
             return
         for blk in self.tables.pop(seq):
-            self.ref[blk] -= 1
-            if self.ref[blk] == 0:
-                self.free_pool.append(blk)
+            self._release(blk)
         del self.lens[seq]
 
     def swap_out(self, seq):
@@ -104,9 +203,7 @@ class BlockManagerModel:
             raise KeyError("swap_out needs a resident sequence")
         blocks = self.tables.pop(seq)
         for blk in blocks:
-            self.ref[blk] -= 1
-            if self.ref[blk] == 0:
-                self.free_pool.append(blk)
+            self._release(blk)
         self.swapped.add(seq)
         return blocks
 
@@ -115,12 +212,27 @@ class BlockManagerModel:
         if seq not in self.swapped:
             raise KeyError("swap_in needs a swapped sequence")
         n = -(-self.lens[seq] // self.block_size)
-        if len(self.free_pool) < n:
+        if len(self.free_pool) + len(self._evictable_chain()) < n:
             raise OutOfBlocks("not enough free blocks to swap in")
         blocks = [self._pop() for _ in range(n)]
         self.tables[seq] = blocks
         self.swapped.discard(seq)
         return blocks
+
+    def _evictable_chain(self):
+        """Blocks that repeated leaf evictions could free, in eviction order."""
+        n_children = dict(self.n_children)
+        out, cand = [], set(self._evictable())
+        while cand:
+            blk = min(cand, key=lambda b: self.stamp[b])
+            cand.discard(blk)
+            out.append(blk)
+            parent = self.node_of[blk][0]
+            if parent is not None:
+                n_children[parent] -= 1
+                if n_children[parent] == 0 and self.ref[parent] == 0:
+                    cand.add(parent)
+        return out
 
     def export_table(self, seqs, max_blocks, pad=0):
         rows = []
