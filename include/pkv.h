@@ -376,6 +376,22 @@ pkv_status pkv_swap_in(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
  * For both, *n_blocks receives the block count; blocks_out == NULL only
  * queries it; capacity below it is an invalid argument (no change).
  * is_swapped: 1 swapped, 0 resident, -1 unknown sequence.
+ *
+ * Prefix cache ([LLMI] "8. Design Alternatives": hash prefix caching and an
+ * LRU radix tree over paged blocks): a radix tree of full blocks, each keyed
+ * under its parent by its block_size token ids (int32, caller's vocabulary).
+ * match_prefix(seq, tokens): seq must be new; it starts as the longest chain
+ * of cached blocks equal to whole blocks of `tokens`, shared (ref_count + 1)
+ * -- *matched_tokens receives their token count; the caller appends the rest.
+ * cache_prefix(seq, tokens): registers seq's first n_tokens / block_size
+ * blocks (all full, n_tokens <= its length) under that chain; a key already
+ * cached by another block ends the registration there (first copy wins).
+ * A cached block whose count drops to 0 keeps its contents and key and is
+ * evictable; a match revives it. When the free pool is empty, allocation
+ * evicts the least recently used evictable block that has no cached
+ * children ("use": a match, a registration, or the release to count 0).
+ * num_free counts the pool only; num_cached all cached blocks; num_evictable
+ * the cached leaves with count 0 now.
  * ------------------------------------------------------------------------- */
 typedef struct pkv_bm pkv_bm;
 
@@ -394,6 +410,12 @@ pkv_status pkv_bm_swap_out(pkv_bm* bm, int64_t seq, int32_t* blocks_out, int32_t
 pkv_status pkv_bm_swap_in(pkv_bm* bm, int64_t seq, int32_t* blocks_out, int32_t capacity,
                           int32_t* n_blocks);
 int32_t pkv_bm_is_swapped(const pkv_bm* bm, int64_t seq);
+pkv_status pkv_bm_match_prefix(pkv_bm* bm, int64_t seq, const int32_t* tokens, int64_t n_tokens,
+                               int64_t* matched_tokens);
+pkv_status pkv_bm_cache_prefix(pkv_bm* bm, int64_t seq, const int32_t* tokens,
+                               int64_t n_tokens);
+int32_t pkv_bm_num_cached(const pkv_bm* bm);
+int32_t pkv_bm_num_evictable(const pkv_bm* bm);
 int32_t pkv_bm_num_free(const pkv_bm* bm);
 int32_t pkv_bm_ref_count(const pkv_bm* bm, int32_t block);
 

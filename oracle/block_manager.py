@@ -164,12 +164,18 @@ class BlockManagerModel:
         """Reserve the next token slot of `seq`; returns (slot, cow_src, cow_dst)."""
         if seq in self.swapped:
             raise ValueError("sequence is swapped out")
+        created = seq not in self.tables
         table = self.tables.setdefault(seq, [])
         pos = self.lens.get(seq, 0)
         bs = self.block_size
         cow = (-1, -1)
         if pos % bs == 0:
-            table.append(self._pop())
+            try:
+                table.append(self._pop())
+            except OutOfBlocks:
+                if created:                     # exhaustion changes nothing
+                    del self.tables[seq]
+                raise
         else:
             last = table[-1]
             if self.ref[last] > 1:

@@ -87,6 +87,11 @@ SIGNATURES = {
     "pkv_bm_swap_out": (_i32, [_vp, ctypes.c_int64, _c_int32_p, _i32, _c_int32_p]),
     "pkv_bm_swap_in": (_i32, [_vp, ctypes.c_int64, _c_int32_p, _i32, _c_int32_p]),
     "pkv_bm_is_swapped": (_i32, [_vp, ctypes.c_int64]),
+    "pkv_bm_match_prefix": (_i32, [_vp, ctypes.c_int64, _c_int32_p, ctypes.c_int64,
+                                   _c_int64_p]),
+    "pkv_bm_cache_prefix": (_i32, [_vp, ctypes.c_int64, _c_int32_p, ctypes.c_int64]),
+    "pkv_bm_num_cached": (_i32, [_vp]),
+    "pkv_bm_num_evictable": (_i32, [_vp]),
     "pkv_gather_kv": (_i32, [ctypes.POINTER(CacheDesc), _vp, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pkv_bm_create": (_i32, [_i32, _i32, ctypes.POINTER(_vp)]),
     "pkv_bm_destroy": (None, [_vp]),
@@ -505,6 +510,26 @@ class BlockManager:
     def swap_in(self, seq):
         """Fresh blocks (logical order) for a swapped sequence, to fill with pkv_swap_in."""
         return self._swap(lib().pkv_bm_swap_in, "pkv_bm_swap_in", seq)
+
+    def match_prefix(self, seq, tokens):
+        """Start a new sequence on the longest cached chain of whole blocks of
+        `tokens`; returns the number of tokens matched."""
+        buf = (ctypes.c_int32 * max(len(tokens), 1))(*tokens)
+        n = ctypes.c_int64()
+        _check(lib().pkv_bm_match_prefix(self._h, seq, buf, len(tokens), ctypes.byref(n)),
+               "pkv_bm_match_prefix")
+        return n.value
+
+    def cache_prefix(self, seq, tokens):
+        """Register the sequence's first len(tokens) // block_size blocks."""
+        buf = (ctypes.c_int32 * max(len(tokens), 1))(*tokens)
+        _check(lib().pkv_bm_cache_prefix(self._h, seq, buf, len(tokens)), "pkv_bm_cache_prefix")
+
+    def num_cached(self):
+        return int(lib().pkv_bm_num_cached(self._h))
+
+    def num_evictable(self):
+        return int(lib().pkv_bm_num_evictable(self._h))
 
     def is_swapped(self, seq):
         return int(lib().pkv_bm_is_swapped(self._h, seq))

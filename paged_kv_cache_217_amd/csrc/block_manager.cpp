@@ -8,9 +8,19 @@
 // Sequences sharing a prefix reference the same blocks through copy-on-write
 // pointers. The allocation rules below fix what the page leaves open; they
 // are stated in pkv.h.
+//
+// Prefix cache ([LLMI] "LLM inference: prefill, decode, KV cache", "8. Design
+// Alternatives": a hash prefix cache over paged blocks and an LRU radix tree
+// over paged blocks): a radix tree whose nodes are full blocks keyed under
+// their parent by their token ids. match_prefix shares the longest cached
+// chain with a new sequence; cache_prefix registers a sequence's blocks; a
+// cached block released to count 0 stays (evictable) and revives on a match;
+// an empty free pool evicts the least recently used unreferenced leaf.
 #include <cstdint>
 #include <new>
+#include <set>
 #include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "pkv.h"
@@ -26,12 +36,94 @@ struct pkv_bm {
   };
   std::unordered_map<int64_t, Seq> seqs;
 
+  // ---- prefix cache
+  struct Key {
+    int32_t parent;                    // -1: the root
+    std::vector<int32_t> tokens;       // block_size token ids
+    bool operator==(const Key& o) const { return parent == o.parent && tokens == o.tokens; }
+  };
+  struct KeyHash {
+    size_t operator()(const Key& k) const {
+      uint64_t h = 1469598103934665603ull ^ static_cast<uint32_t>(k.parent);
+      for (int32_t t : k.tokens) h = (h ^ static_cast<uint32_t>(t)) * 1099511628211ull;
+      return static_cast<size_t>(h);
+    }
+  };
+  static constexpr int32_t kNotCached = -2;
+  std::unordered_map<Key, int32_t, KeyHash> children;
+  std::vector<int32_t> cached_parent;  // per block: kNotCached, -1 (root) or parent block
+  std::vector<Key> cached_key;
+  std::vector<int32_t> n_children;     // cached children of a cached block
+  std::vector<uint64_t> stamp;         // last use
+  uint64_t clock = 0;
+  int32_t n_cached = 0;
+  std::set<std::pair<uint64_t, int32_t>> evictable;   // (stamp, block) of idle cached leaves
+
+  bool cached(int32_t b) const { return cached_parent[b] != kNotCached; }
+  bool idle_leaf(int32_t b) const { return cached(b) && ref[b] == 0 && n_children[b] == 0; }
+  // keeps `evictable` equal to the idle cached leaves; call after any change
+  // to a block's count, children, stamp or cache membership
+  void update(int32_t b) {
+    evictable.erase({stamp[b], b});
+    if (idle_leaf(b)) evictable.insert({stamp[b], b});
+  }
+  void tick(int32_t b) {
+    evictable.erase({stamp[b], b});
+    stamp[b] = ++clock;
+    update(b);
+  }
+  void uncache(int32_t b) {
+    evictable.erase({stamp[b], b});
+    children.erase(cached_key[b]);
+    const int32_t parent = cached_parent[b];
+    cached_parent[b] = kNotCached;
+    cached_key[b] = Key{};
+    n_children[b] = 0;
+    n_cached -= 1;
+    if (parent >= 0) {
+      n_children[parent] -= 1;
+      update(parent);
+    }
+  }
+
   bool pop(int32_t* blk) {
-    if (free_pool.empty()) return false;
+    if (free_pool.empty()) {
+      if (evictable.empty()) return false;
+      *blk = evictable.begin()->second;          // least recently used idle leaf
+      uncache(*blk);
+      ref[*blk] += 1;
+      return true;
+    }
     *blk = free_pool.back();
     free_pool.pop_back();
     ref[*blk] += 1;
     return true;
+  }
+
+  void release(int32_t b) {
+    ref[b] -= 1;
+    if (ref[b] == 0) {
+      if (cached(b))
+        tick(b);                                 // stays cached, now evictable
+      else
+        free_pool.push_back(b);
+    }
+  }
+
+  // blocks that repeated leaf evictions could free (swap-in admission)
+  int64_t reclaimable() const {
+    std::vector<int32_t> kids(n_children);
+    std::vector<int32_t> stack;
+    for (const auto& e : evictable) stack.push_back(e.second);
+    int64_t n = 0;
+    while (!stack.empty()) {
+      const int32_t b = stack.back();
+      stack.pop_back();
+      n += 1;
+      const int32_t parent = cached_parent[b];
+      if (parent >= 0 && --kids[parent] == 0 && ref[parent] == 0) stack.push_back(parent);
+    }
+    return n;
   }
 };
 
@@ -45,6 +137,10 @@ pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size, pkv_bm** out) {
   bm->free_pool.resize(num_blocks);
   for (int32_t i = 0; i < num_blocks; ++i) bm->free_pool[i] = i;
   bm->ref.assign(num_blocks, 0);
+  bm->cached_parent.assign(num_blocks, pkv_bm::kNotCached);
+  bm->cached_key.resize(num_blocks);
+  bm->n_children.assign(num_blocks, 0);
+  bm->stamp.assign(num_blocks, 0);
   *out = bm;
   return PKV_OK;
 }
@@ -56,6 +152,7 @@ pkv_status pkv_bm_append_slot(pkv_bm* bm, int64_t seq, int64_t* slot, int32_t* c
   if (!bm || !slot || !cow_src || !cow_dst) return PKV_ERR_INVALID_ARG;
   auto found = bm->seqs.find(seq);
   if (found != bm->seqs.end() && found->second.swapped) return PKV_ERR_INVALID_ARG;
+  const bool created = found == bm->seqs.end();
   auto& s = bm->seqs[seq];
   const int64_t pos = s.len;
   const int32_t bs = bm->block_size;
@@ -63,7 +160,7 @@ pkv_status pkv_bm_append_slot(pkv_bm* bm, int64_t seq, int64_t* slot, int32_t* c
   if (pos % bs == 0) {
     int32_t blk;
     if (!bm->pop(&blk)) {
-      if (s.blocks.empty() && s.len == 0) bm->seqs.erase(seq);  // leave no trace
+      if (created) bm->seqs.erase(seq);                 // exhaustion changes nothing
       return PKV_ERR_OUT_OF_BLOCKS;
     }
     s.blocks.push_back(blk);
@@ -72,7 +169,7 @@ pkv_status pkv_bm_append_slot(pkv_bm* bm, int64_t seq, int64_t* slot, int32_t* c
     if (bm->ref[last] > 1) {
       int32_t fresh;
       if (!bm->pop(&fresh)) return PKV_ERR_OUT_OF_BLOCKS;
-      bm->ref[last] -= 1;
+      bm->ref[last] -= 1;                               // still >= 1: stays referenced
       s.blocks.back() = fresh;
       src = last;
       dst = fresh;
@@ -100,10 +197,7 @@ pkv_status pkv_bm_free(pkv_bm* bm, int64_t seq) {
   if (!bm) return PKV_ERR_INVALID_ARG;
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return PKV_ERR_INVALID_ARG;
-  for (int32_t blk : it->second.blocks) {
-    bm->ref[blk] -= 1;
-    if (bm->ref[blk] == 0) bm->free_pool.push_back(blk);
-  }
+  for (int32_t blk : it->second.blocks) bm->release(blk);
   bm->seqs.erase(it);
   return PKV_OK;
 }
@@ -142,10 +236,8 @@ pkv_status pkv_bm_swap_out(pkv_bm* bm, int64_t seq, int32_t* blocks_out, int32_t
   if (!blocks_out) return PKV_OK;                       // size query, no change
   if (capacity < n) return PKV_ERR_INVALID_ARG;
   for (int32_t i = 0; i < n; ++i) {
-    const int32_t blk = s.blocks[i];
-    blocks_out[i] = blk;
-    bm->ref[blk] -= 1;
-    if (bm->ref[blk] == 0) bm->free_pool.push_back(blk);
+    blocks_out[i] = s.blocks[i];
+    bm->release(s.blocks[i]);
   }
   s.blocks.clear();
   s.swapped = true;
@@ -162,7 +254,9 @@ pkv_status pkv_bm_swap_in(pkv_bm* bm, int64_t seq, int32_t* blocks_out, int32_t 
   *n_blocks = static_cast<int32_t>(need);
   if (!blocks_out) return PKV_OK;                       // size query, no change
   if (capacity < need) return PKV_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(bm->free_pool.size()) < need) return PKV_ERR_OUT_OF_BLOCKS;
+  if (static_cast<int64_t>(bm->free_pool.size()) < need &&
+      static_cast<int64_t>(bm->free_pool.size()) + bm->reclaimable() < need)
+    return PKV_ERR_OUT_OF_BLOCKS;
   for (int64_t i = 0; i < need; ++i) {
     int32_t blk;
     bm->pop(&blk);
@@ -171,6 +265,73 @@ pkv_status pkv_bm_swap_in(pkv_bm* bm, int64_t seq, int32_t* blocks_out, int32_t 
   }
   s.swapped = false;
   return PKV_OK;
+}
+
+pkv_status pkv_bm_match_prefix(pkv_bm* bm, int64_t seq, const int32_t* tokens, int64_t n_tokens,
+                               int64_t* matched_tokens) {
+  if (!bm || !matched_tokens || n_tokens < 0 || (n_tokens > 0 && !tokens))
+    return PKV_ERR_INVALID_ARG;
+  if (bm->seqs.count(seq)) return PKV_ERR_INVALID_ARG;
+  const int32_t bs = bm->block_size;
+  std::vector<int32_t> blocks;
+  int32_t parent = -1;
+  for (int64_t i = 0; i + 1 <= n_tokens / bs; ++i) {
+    pkv_bm::Key key{parent, std::vector<int32_t>(tokens + i * bs, tokens + (i + 1) * bs)};
+    auto hit = bm->children.find(key);
+    if (hit == bm->children.end()) break;
+    blocks.push_back(hit->second);
+    parent = hit->second;
+  }
+  for (int32_t b : blocks) {
+    bm->ref[b] += 1;
+    bm->tick(b);
+  }
+  pkv_bm::Seq s;
+  s.blocks = blocks;
+  s.len = static_cast<int64_t>(blocks.size()) * bs;
+  bm->seqs.emplace(seq, std::move(s));
+  *matched_tokens = static_cast<int64_t>(blocks.size()) * bs;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_cache_prefix(pkv_bm* bm, int64_t seq, const int32_t* tokens,
+                               int64_t n_tokens) {
+  if (!bm || n_tokens < 0 || (n_tokens > 0 && !tokens)) return PKV_ERR_INVALID_ARG;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end() || it->second.swapped) return PKV_ERR_INVALID_ARG;
+  const auto& s = it->second;
+  const int32_t bs = bm->block_size;
+  const int64_t n = n_tokens / bs;
+  if (n > static_cast<int64_t>(s.blocks.size()) || n * bs > s.len) return PKV_ERR_INVALID_ARG;
+  int32_t parent = -1;
+  for (int64_t i = 0; i < n; ++i) {
+    pkv_bm::Key key{parent, std::vector<int32_t>(tokens + i * bs, tokens + (i + 1) * bs)};
+    const int32_t blk = s.blocks[i];
+    auto have = bm->children.find(key);
+    if (have == bm->children.end()) {
+      if (bm->cached(blk)) break;                     // cached under another key
+      bm->children.emplace(key, blk);
+      bm->cached_parent[blk] = parent;
+      bm->cached_key[blk] = std::move(key);
+      bm->n_children[blk] = 0;
+      bm->n_cached += 1;
+      if (parent >= 0) {
+        bm->n_children[parent] += 1;
+        bm->update(parent);
+      }
+    } else if (have->second != blk) {
+      break;                                          // the prefix is cached by other blocks
+    }
+    bm->tick(blk);
+    parent = blk;
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_bm_num_cached(const pkv_bm* bm) { return bm ? bm->n_cached : -1; }
+
+int32_t pkv_bm_num_evictable(const pkv_bm* bm) {
+  return bm ? static_cast<int32_t>(bm->evictable.size()) : -1;
 }
 
 int32_t pkv_bm_is_swapped(const pkv_bm* bm, int64_t seq) {

@@ -281,6 +281,79 @@ def test_swap_entry_points_validate():
             _lib.PKV_ERR_UNSUPPORTED
 
 
+def test_block_manager_prefix_cache_matches_the_model():
+    rng = random.Random(2174)
+    prompts = [[rng.randrange(3) for _ in range(rng.randrange(1, 14))] for _ in range(7)]
+    for trial in range(40):
+        nb, bs = rng.choice([(6, 2), (10, 4), (16, 2), (24, 4)])
+        lib_bm = pkv.BlockManager(nb, bs)
+        model = BlockManagerModel(nb, bs)
+        live, swapped = [], []
+        next_id = 0
+
+        def both(fn_lib, fn_model):
+            try:
+                expect = fn_model()
+            except ModelOutOfBlocks:
+                with pytest.raises(pkv.OutOfBlocks):
+                    fn_lib()
+                return None, False
+            got = fn_lib()
+            assert got == expect
+            return got, True
+
+        for step in range(250):
+            op = rng.random()
+            if op < 0.3:
+                seq, next_id = next_id, next_id + 1
+                tokens = rng.choice(prompts)
+                both(lambda: lib_bm.match_prefix(seq, tokens),
+                     lambda: model.match_prefix(seq, tokens))
+                live.append(seq)
+                ok = True
+                for _ in range(len(tokens) - model.lens[seq]):
+                    _, ok = both(lambda: lib_bm.append_slot(seq), lambda: model.append_slot(seq))
+                    if not ok:
+                        break
+                if ok:
+                    lib_bm.cache_prefix(seq, tokens)
+                    model.cache_prefix(seq, tokens)
+            elif op < 0.5 and live:
+                seq = rng.choice(live)
+                both(lambda: lib_bm.append_slot(seq), lambda: model.append_slot(seq))
+            elif op < 0.6 and live:
+                parent = rng.choice(live)
+                model.fork(parent, next_id)
+                lib_bm.fork(parent, next_id)
+                live.append(next_id)
+                next_id += 1
+            elif op < 0.7 and live:
+                seq = live.pop(rng.randrange(len(live)))
+                assert lib_bm.swap_out(seq) == model.swap_out(seq)
+                swapped.append(seq)
+            elif op < 0.8 and swapped:
+                seq = rng.choice(swapped)
+                _, ok = both(lambda: lib_bm.swap_in(seq), lambda: model.swap_in(seq))
+                if ok:
+                    swapped.remove(seq)
+                    live.append(seq)
+            else:
+                pool = live + swapped
+                if pool:
+                    seq = pool[rng.randrange(len(pool))]
+                    (live if seq in live else swapped).remove(seq)
+                    model.free(seq)
+                    lib_bm.free(seq)
+            assert lib_bm.num_free() == len(model.free_pool)
+            assert lib_bm.num_cached() == len(model.node_of)
+            assert lib_bm.num_evictable() == len(model._evictable())
+        for blk in range(nb):
+            assert lib_bm.ref_count(blk) == model.ref[blk]
+        mb = max([len(t) for t in model.tables.values()] + [1])
+        assert lib_bm.export_table(live, mb) == model.export_table(live, mb)
+        lib_bm.close()
+
+
 def test_block_manager_errors():
     bm = pkv.BlockManager(2, 4)
     with pytest.raises(pkv.PkvError):
