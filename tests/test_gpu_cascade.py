@@ -83,3 +83,51 @@ def test_cascade_matches_oracle_and_plain_decode(pkv, case):
     assert err <= MAX_ABS[dt], f"max abs error {err:.3e}"
     assert rel <= 1e-4, f"relative L2 {rel:.3e}"
     assert np.max(np.abs(got - plain.cpu().double().numpy())) <= 2 * MAX_ABS[dt] / 10
+
+
+def test_prefix_cache_feeds_cascade_attention(pkv):
+    """Sequences start from a cached system prompt (pkv_bm_match_prefix), add
+    their own tokens, and attend through the cascade path; the result equals
+    plain decode over the block manager's tables and the oracle."""
+    n_kv, n_q, d, bs, nb = 8, 64, 128, 16, 512
+    bm = pkv.BlockManager(nb, bs)
+    kd = torch.zeros((nb, n_kv, bs, d), dtype=torch.bfloat16, device=DEV)
+    vd = torch.zeros_like(kd)
+    g = torch.Generator(device="cpu").manual_seed(2175)
+
+    def write(seq, n):
+        slots = [bm.append_slot(seq)[0] for _ in range(n)]
+        k = torch.randn((n, n_kv, d), generator=g).to(torch.bfloat16).to(DEV)
+        v = torch.randn((n, n_kv, d), generator=g).to(torch.bfloat16).to(DEV)
+        pkv.kv_append(kd, vd, k, v, torch.tensor(slots, dtype=torch.int64, device=DEV))
+
+    system = [int(x) for x in torch.randint(0, 32000, (1000,), generator=g)]
+    assert bm.match_prefix(0, system) == 0
+    write(0, len(system))
+    bm.cache_prefix(0, system)
+    B = 12
+    for s in range(1, B + 1):
+        assert bm.match_prefix(s, system + [s]) == 992          # 62 whole blocks
+        write(s, 8 + 37 * s)                                    # the rest, then private tokens
+    seqs = list(range(1, B + 1))
+    mb = 96
+    full = np.array(bm.export_table(seqs, mb), dtype=np.int32)
+    lens = np.array([bm.seq_len(s) for s in seqs], dtype=np.int32)
+    pb = 992 // bs
+    assert (full[:, :pb] == full[0, :pb]).all()                 # the shared chain
+    prefix_table = np.ascontiguousarray(full[0, :pb])
+    suffix = np.ascontiguousarray(full[:, pb:])
+    slen = (lens - 992).astype(np.int32)
+    q = torch.randn((B, n_q, d), generator=g).to(torch.bfloat16).to(DEV)
+    out = pkv.cascade_decode_attention(q, kd, vd, torch.from_numpy(prefix_table).to(DEV), 992,
+                                       torch.from_numpy(suffix).to(DEV),
+                                       torch.from_numpy(slen).to(DEV), 0.0884, int(slen.max()))
+    plain = pkv.paged_decode_attention(q, kd, vd, torch.from_numpy(full).to(DEV),
+                                       torch.from_numpy(lens).to(DEV), 0.0884, int(lens.max()))
+    torch.cuda.synchronize()
+    expect = ref.decode_attention(W.bits(q), W.bits(kd), W.bits(vd), full, lens, 0.0884)
+    got = out.cpu().double().numpy()
+    assert np.max(np.abs(got - expect)) <= 1e-2
+    assert np.linalg.norm(got - expect) / np.linalg.norm(expect) <= 1e-4
+    assert np.max(np.abs(got - plain.cpu().double().numpy())) <= 2e-3
+    bm.close()
