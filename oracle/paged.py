@@ -37,10 +37,12 @@ Readings where the pages are silent (each also listed in the design notes):
 import numpy as np
 
 from . import bf16 as _bf16
+from . import fp4_e2m1 as _fp4
 from . import fp8_e4m3 as _fp8
 
 BF16 = "bf16"
 FP8 = "fp8_e4m3"
+FP4 = "fp4_e2m1"
 
 
 # --------------------------------------------------------------------------
@@ -99,6 +101,11 @@ def dequantize(raw, kv_dtype, scale=None):
         vals = _fp8.decode(raw)
         s = np.asarray(scale, dtype=np.float32).astype(np.float64)
         return vals * s[:, None]
+    if kv_dtype == FP4:
+        # raw rows are packed bytes [..., d / 2]
+        vals = _fp4.decode(_fp4.unpack(raw))
+        s = np.asarray(scale, dtype=np.float32).astype(np.float64)
+        return vals * s[:, None]
     raise ValueError(kv_dtype)
 
 
@@ -129,7 +136,8 @@ def decode_attention(q_bits, k_cache, v_cache, block_tables, context_lens, scale
     """Paged single-token decode attention for a batch, float64 output.
 
     q_bits:        uint16 [B, n_q, d] bfloat16 patterns
-    k/v_cache:     [num_blocks, n_kv, bs, d] uint16 (BF16) or uint8 (FP8)
+    k/v_cache:     [num_blocks, n_kv, bs, d] uint16 (BF16) or uint8 (FP8), or
+                   [num_blocks, n_kv, bs, d / 2] packed uint8 (FP4)
     block_tables:  int32 [B, max_blocks]
     context_lens:  int32 [B]
     scale:         softmax scale (float)
@@ -242,7 +250,8 @@ def kv_append(k_cache, v_cache, k_new_bits, v_new_bits, slots, kv_dtype=BF16,
 
     k/v_new_bits: uint16 [T, n_kv, d] bfloat16 patterns. A negative slot is
     skipped. BF16 caches store the pattern unchanged. FP8 caches store
-    encode(float32(x) / float32(scale[kv_head])) per element.
+    encode(float32(x) / float32(scale[kv_head])) per element; FP4 caches
+    store the same with the E2M1 encoder, two codes per byte.
     [LLMI] flow step 5 and "Why We Need the Key-Value (KV) Cache": the new
     token's key and value are appended to the cache.
     """
@@ -258,6 +267,13 @@ def kv_append(k_cache, v_cache, k_new_bits, v_new_bits, slots, kv_dtype=BF16,
         if kv_dtype == BF16:
             kc[blk, :, off, :] = k_new_bits[i]
             vc[blk, :, off, :] = v_new_bits[i]
+        elif kv_dtype == FP4:
+            ks = np.asarray(k_scale, dtype=np.float32)
+            vs = np.asarray(v_scale, dtype=np.float32)
+            kc[blk, :, off, :] = _fp4.pack(
+                _fp4.quantize_f32_div(_bf16.to_f32(k_new_bits[i]), ks[:, None]))
+            vc[blk, :, off, :] = _fp4.pack(
+                _fp4.quantize_f32_div(_bf16.to_f32(v_new_bits[i]), vs[:, None]))
         else:
             ks = np.asarray(k_scale, dtype=np.float32)
             vs = np.asarray(v_scale, dtype=np.float32)
