@@ -54,7 +54,7 @@ typedef enum {
   PKV_ERR_HIP = 5
 } pkv_status;
 
-typedef enum { PKV_BF16 = 0, PKV_FP8_E4M3 = 1, PKV_FP32 = 2 } pkv_dtype;
+typedef enum { PKV_BF16 = 0, PKV_FP8_E4M3 = 1, PKV_FP32 = 2, PKV_FP4_E2M1 = 3 } pkv_dtype;
 
 /* Geometry of one layer's K/V pools (both share it). kv_dtype is a pkv_dtype:
  * PKV_BF16 or PKV_FP8_E4M3. */

@@ -25,6 +25,7 @@ PKV_ERR_HIP = 5
 PKV_BF16 = 0
 PKV_FP8_E4M3 = 1
 PKV_FP32 = 2
+PKV_FP4_E2M1 = 3
 
 
 class PkvError(RuntimeError):
@@ -162,7 +163,9 @@ def kv_dtype_of(cache):
         return PKV_BF16
     if cache.dtype in (torch.uint8, torch.float8_e4m3fn):
         return PKV_FP8_E4M3
-    raise TypeError(f"cache dtype {cache.dtype} is neither bfloat16 nor FP8 codes")
+    if cache.dtype == torch.float4_e2m1fn_x2:
+        return PKV_FP4_E2M1
+    raise TypeError(f"cache dtype {cache.dtype} is neither bfloat16, FP8 nor FP4 codes")
 
 
 def cache_desc(k_cache):
@@ -170,7 +173,10 @@ def cache_desc(k_cache):
     if k_cache.dim() != 4:
         raise ValueError("cache must be [num_blocks, n_kv, block_size, d_head]")
     n, h, bs, d = k_cache.shape
-    return CacheDesc(n, bs, h, d, kv_dtype_of(k_cache))
+    kv = kv_dtype_of(k_cache)
+    if kv == PKV_FP4_E2M1:
+        d *= 2                              # float4_e2m1fn_x2: two codes per element
+    return CacheDesc(n, bs, h, d, kv)
 
 
 def _out_code(dtype):
@@ -226,7 +232,7 @@ def _resolve_partition(k_cache, B, n_q, max_context_len, partition_size):
 
 def make_workspace(k_cache, B, n_q, max_context_len, partition_size=0):
     P = _resolve_partition(k_cache, B, n_q, max_context_len, partition_size)
-    nbytes = decode_workspace_bytes(B, n_q, k_cache.shape[3], max_context_len, P)
+    nbytes = decode_workspace_bytes(B, n_q, cache_desc(k_cache).d_head, max_context_len, P)
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=k_cache.device), P
 
 
@@ -243,10 +249,10 @@ def _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_s
     B, n_q, d = q.shape
     if d != desc.d_head or block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("q / block_tables / context_lens shapes disagree with the cache")
-    if desc.kv_dtype == PKV_FP8_E4M3:
+    if desc.kv_dtype in (PKV_FP8_E4M3, PKV_FP4_E2M1):
         for s in (k_scale, v_scale):
             if s is None:
-                raise ValueError("FP8 caches need k_scale and v_scale")
+                raise ValueError("FP8 and FP4 caches need k_scale and v_scale")
             _need(s, torch.float32, "scale")
     return desc, B, n_q, d
 
@@ -443,7 +449,7 @@ def gather_kv(k_cache, v_cache, block_table_row, context_len, stream=None):
     """Dense [ctx, n_kv, d] copies of one sequence's raw K/V rows."""
     desc = cache_desc(k_cache)
     _need(block_table_row, torch.int32, "block_table_row")
-    shape = (int(context_len), desc.n_kv, desc.d_head)
+    shape = (int(context_len), desc.n_kv, k_cache.shape[3])   # elements of the cache dtype
     k_out = torch.empty(shape, dtype=k_cache.dtype, device=k_cache.device)
     v_out = torch.empty(shape, dtype=v_cache.dtype, device=v_cache.device)
     _check(lib().pkv_gather_kv(ctypes.byref(desc), _ptr(k_out), _ptr(v_out), _ptr(k_cache),

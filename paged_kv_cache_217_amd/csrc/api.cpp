@@ -23,7 +23,8 @@ pkv_status from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HI
 
 pkv_status check_desc(const pkv_cache_desc* d) {
   if (!d || d->num_blocks <= 0 || d->n_kv <= 0) return PKV_ERR_INVALID_ARG;
-  if (d->kv_dtype != PKV_BF16 && d->kv_dtype != PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+  if (d->kv_dtype != PKV_BF16 && d->kv_dtype != PKV_FP8_E4M3 && d->kv_dtype != PKV_FP4_E2M1)
+    return PKV_ERR_UNSUPPORTED;
   if (d->block_size != 16 && d->block_size != 32) return PKV_ERR_UNSUPPORTED;
   if (d->d_head != 64 && d->d_head != 128) return PKV_ERR_UNSUPPORTED;
   return PKV_OK;
@@ -141,7 +142,7 @@ pkv_status prepare_decode(const pkv_cache_desc* desc, const void* q, const void*
   if (B > 0 && (!q || !k_cache || !v_cache || !block_tables || !context_lens))
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
-  if (desc->kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (desc->kv_dtype != PKV_BF16 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
   const int G = n_q / desc->n_kv;
   if (!pkv::decode_supported(desc->d_head, desc->block_size, G, desc->kv_dtype))
     return PKV_ERR_UNSUPPORTED;
@@ -212,7 +213,7 @@ pkv_status pkv_kv_append(const pkv_cache_desc* desc, void* k_cache, void* v_cach
   if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping) return PKV_ERR_INVALID_ARG;
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
     return PKV_ERR_INVALID_ARG;
-  if (desc->kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (desc->kv_dtype != PKV_BF16 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
   return from_hip(pkv::launch_kv_append(*desc, k_cache, v_cache, k_new, v_new, slot_mapping, T,
                                         k_scale, v_scale, as_stream(stream)));
 }
@@ -344,6 +345,7 @@ pkv_status pkv_paged_multi_query_attention(const pkv_cache_desc* desc, void* out
                                            int32_t partition_size, void* workspace,
                                            size_t workspace_bytes_, void* stream) {
   if (Q <= 0) return PKV_ERR_INVALID_ARG;
+  if (desc && desc->kv_dtype == PKV_FP4_E2M1) return PKV_ERR_UNSUPPORTED;   // decode only
   if (desc && check_desc(desc) == PKV_OK && n_q > 0 && n_q % desc->n_kv == 0 &&
       partition_size == 0 && B >= 0 && max_context_len >= 0)
     partition_size = pick_partition_mq(desc, B, Q, n_q, max_context_len);
@@ -398,6 +400,7 @@ pkv_status plan_cascade(const pkv_cache_desc* desc, int32_t B, int32_t n_q, int3
                         int32_t suffix_partition, CascadePlan* pl) {
   pkv_status st = check_desc(desc);
   if (st != PKV_OK) return st;
+  if (desc->kv_dtype == PKV_FP4_E2M1 && prefix_len > 0) return PKV_ERR_UNSUPPORTED;
   if (B < 0 || n_q <= 0 || n_q % desc->n_kv != 0 || prefix_len < 0 || max_suffix_len < 0 ||
       prefix_partition < 0 || suffix_partition < 0)
     return PKV_ERR_INVALID_ARG;
@@ -454,7 +457,7 @@ pkv_status pkv_cascade_decode_attention(
     return PKV_ERR_INVALID_ARG;
   if (prefix_len > 0 && !prefix_table) return PKV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
-  if (desc->kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (desc->kv_dtype != PKV_BF16 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
   if (!pkv::decode_supported(desc->d_head, desc->block_size, n_q / desc->n_kv, desc->kv_dtype))
     return PKV_ERR_UNSUPPORTED;
   if (B > 65535 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;

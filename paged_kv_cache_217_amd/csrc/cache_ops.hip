@@ -29,8 +29,9 @@ __global__ void slot_mapping_kernel(const int32_t* __restrict__ block_tables, in
   slots[b] = slot;
 }
 
-// One thread per 8 elements of one (token, head) row.
-template <bool FP8>
+// One thread per 8 elements of one (token, head) row. FMT: 0 bf16 copy,
+// 1 FP8 E4M3 store, 2 FP4 E2M1 store (two codes per byte, low nibble first).
+template <int FMT>
 __global__ void kv_append_kernel(uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
                                  const uint16_t* __restrict__ k_new,
                                  const uint16_t* __restrict__ v_new,
@@ -53,7 +54,24 @@ __global__ void kv_append_kernel(uint8_t* __restrict__ k_cache, uint8_t* __restr
   const int64_t dst = ((blk * n_kv + h) * bs + off) * d + c * 8;  // element index
   const uint4 kw = *reinterpret_cast<const uint4*>(k_new + src);
   const uint4 vw = *reinterpret_cast<const uint4*>(v_new + src);
-  if constexpr (!FP8) {
+  if constexpr (FMT == 2) {
+    const float ks = k_scale[h];
+    const float vs = v_scale[h];
+    const uint32_t kin[4] = {kw.x, kw.y, kw.z, kw.w};
+    const uint32_t vin[4] = {vw.x, vw.y, vw.z, vw.w};
+    uint32_t kout = 0, vout = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float k0, k1, v0, v1;
+      bf16x2_to_f32(kin[i], k0, k1);
+      bf16x2_to_f32(vin[i], v0, v1);
+      // IEEE binary32 division, then the saturating encode; element 2i low nibble
+      kout |= (f32_to_fp4_e2m1_sat(k0 / ks) | (f32_to_fp4_e2m1_sat(k1 / ks) << 4)) << (8 * i);
+      vout |= (f32_to_fp4_e2m1_sat(v0 / vs) | (f32_to_fp4_e2m1_sat(v1 / vs) << 4)) << (8 * i);
+    }
+    *reinterpret_cast<uint32_t*>(k_cache + dst / 2) = kout;
+    *reinterpret_cast<uint32_t*>(v_cache + dst / 2) = vout;
+  } else if constexpr (FMT == 0) {
     *reinterpret_cast<uint4*>(k_cache + dst * 2) = kw;
     *reinterpret_cast<uint4*>(v_cache + dst * 2) = vw;
   } else {
@@ -76,6 +94,12 @@ __global__ void kv_append_kernel(uint8_t* __restrict__ k_cache, uint8_t* __restr
     *reinterpret_cast<uint2*>(k_cache + dst) = make_uint2(kout[0], kout[1]);
     *reinterpret_cast<uint2*>(v_cache + dst) = make_uint2(vout[0], vout[1]);
   }
+}
+
+// bytes of one element row of d_head elements
+static int row_bytes_of(const pkv_cache_desc& d) {
+  return d.kv_dtype == PKV_FP4_E2M1 ? d.d_head / 2
+                                    : d.d_head * (d.kv_dtype == PKV_FP8_E4M3 ? 1 : 2);
 }
 
 // Block (src -> dst) copy of every head's tile; grid (pairs, 2 caches).
@@ -173,20 +197,23 @@ hipError_t launch_kv_append(const pkv_cache_desc& d, void* k_cache, void* v_cach
   auto* kn = static_cast<const uint16_t*>(k_new);
   auto* vn = static_cast<const uint16_t*>(v_new);
   if (d.kv_dtype == PKV_FP8_E4M3)
-    kv_append_kernel<true><<<grid, threads, 0, stream>>>(kc, vc, kn, vn, slots, T, d.n_kv,
-                                                         d.d_head, d.block_size, d.num_blocks,
-                                                         k_scale, v_scale);
+    kv_append_kernel<1><<<grid, threads, 0, stream>>>(kc, vc, kn, vn, slots, T, d.n_kv,
+                                                      d.d_head, d.block_size, d.num_blocks,
+                                                      k_scale, v_scale);
+  else if (d.kv_dtype == PKV_FP4_E2M1)
+    kv_append_kernel<2><<<grid, threads, 0, stream>>>(kc, vc, kn, vn, slots, T, d.n_kv,
+                                                      d.d_head, d.block_size, d.num_blocks,
+                                                      k_scale, v_scale);
   else
-    kv_append_kernel<false><<<grid, threads, 0, stream>>>(kc, vc, kn, vn, slots, T, d.n_kv,
-                                                          d.d_head, d.block_size, d.num_blocks,
-                                                          k_scale, v_scale);
+    kv_append_kernel<0><<<grid, threads, 0, stream>>>(kc, vc, kn, vn, slots, T, d.n_kv,
+                                                      d.d_head, d.block_size, d.num_blocks,
+                                                      k_scale, v_scale);
   return hipGetLastError();
 }
 
 hipError_t launch_copy_blocks(const pkv_cache_desc& d, void* k_cache, void* v_cache,
                               const int32_t* pairs, int n_pairs, hipStream_t stream) {
-  const int64_t block_bytes = static_cast<int64_t>(d.n_kv) * d.block_size * d.d_head *
-                              (d.kv_dtype == PKV_FP8_E4M3 ? 1 : 2);
+  const int64_t block_bytes = static_cast<int64_t>(d.n_kv) * d.block_size * row_bytes_of(d);
   copy_blocks_kernel<<<dim3(n_pairs, 2), 256, 0, stream>>>(
       static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), pairs, block_bytes,
       d.num_blocks);
@@ -196,7 +223,7 @@ hipError_t launch_copy_blocks(const pkv_cache_desc& d, void* k_cache, void* v_ca
 hipError_t launch_gather(const pkv_cache_desc& d, void* k_out, void* v_out, const void* k_cache,
                          const void* v_cache, const int32_t* table, int ctx,
                          hipStream_t stream) {
-  const int row_bytes = d.d_head * (d.kv_dtype == PKV_FP8_E4M3 ? 1 : 2);
+  const int row_bytes = row_bytes_of(d);
   const int64_t total = static_cast<int64_t>(ctx) * d.n_kv * (row_bytes / 16);
   const int threads = 256;
   gather_kernel<<<static_cast<unsigned>((total + threads - 1) / threads), threads, 0, stream>>>(
@@ -207,8 +234,7 @@ hipError_t launch_gather(const pkv_cache_desc& d, void* k_out, void* v_out, cons
 }
 
 int64_t swap_block_bytes(const pkv_cache_desc& d) {
-  return static_cast<int64_t>(d.n_kv) * d.block_size * d.d_head *
-         (d.kv_dtype == PKV_FP8_E4M3 ? 1 : 2);
+  return static_cast<int64_t>(d.n_kv) * d.block_size * row_bytes_of(d);
 }
 
 hipError_t launch_swap_pack(const pkv_cache_desc& d, const void* k_cache, const void* v_cache,

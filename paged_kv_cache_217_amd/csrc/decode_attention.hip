@@ -453,12 +453,14 @@ static int head_tile(int G) { return G <= 8 ? G : 8; }
 bool decode_supported(int d, int bs, int G, int kv_dtype) {
   if (d != 64 && d != 128) return false;
   if (bs != 16 && bs != 32) return false;
-  if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3) return false;
+  if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3 && kv_dtype != PKV_FP4_E2M1) return false;
+  if (kv_dtype == PKV_FP4_E2M1 && d != 128) return false;   // matrix-core kernel, 64-byte rows
   if (G == 1 || G == 2 || G == 4 || G == 8) return true;
   return G > 0 && G % 8 == 0;
 }
 
 hipError_t launch_decode_partition_valu(const DecodeArgs& a, hipStream_t s) {
+  if (a.kv_dtype == PKV_FP4_E2M1) return hipErrorInvalidValue;   // matrix-core kernel only
   const int G = a.n_q / a.n_kv;
   const int GT = head_tile(G);
   const dim3 grid(a.P_max, a.n_kv * (G / GT), a.B);

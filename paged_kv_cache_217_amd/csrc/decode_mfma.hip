@@ -58,24 +58,37 @@ namespace pkv {
 
 using namespace mfma;
 
+// KV element formats of the kernel template.
+constexpr int kFmtBf16 = 0, kFmtFp8 = 1, kFmtFp4 = 2;
+
 // Two waves per SIMD: the register budget is 256 per lane (arch + acc).
-template <int D, int BS, bool FP8, int NW, bool SPLIT_P>
+template <int D, int BS, int FMT, int NW, bool SPLIT_P>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_partition_mfma(DecodeArgs a) {
-  constexpr int CT = FP8 ? 64 : 32;           // tokens per chunk
+  constexpr bool FP8 = FMT == kFmtFp8;
+  constexpr bool FP4 = FMT == kFmtFp4;        // two E2M1 codes per byte, d = 128 only
+  constexpr bool QNT = FMT != kFmtBf16;       // per-head scales
+  constexpr int CT = FP4 ? 128 : FP8 ? 64 : 32;   // tokens per chunk (16 KiB of K+V)
   constexpr int NRG = CT / 16;                // 16-token row groups per chunk
   constexpr int NKS = CT / 32;                // 32-token PV k-steps per chunk
   constexpr int NKK = D / 32;                 // QK MFMA steps over d
-  constexpr int NKL = FP8 ? NKK / 2 : NKK;    // 16-byte K loads per row group
+  constexpr int NKL = FP4 ? 1 : FP8 ? NKK / 2 : NKK;   // 16-byte K loads per row group
   constexpr int NJ = D / 16;                  // PV MFMAs per k-step (16 dims each)
   constexpr int DPL = D / 16;                 // dims per lane per V row
   constexpr int BPC = CT / BS;                // blocks per chunk
-  constexpr int EB = FP8 ? 1 : 2;             // bytes per element
-  constexpr int VB = DPL * EB;                // bytes per V load (DPL dims)
+  constexpr int EB = FP8 ? 1 : 2;             // bytes per element (bf16, FP8)
+  constexpr int RB = FP4 ? D / 2 : D * EB;    // bytes per token row
+  constexpr int VB = FP4 ? DPL / 2 : FP8 ? DPL : 2 * DPL;   // bytes per V load (DPL dims)
   constexpr int NVS = 8 * NKS;                // V token slots per chunk
   using VT = typename Vec<VB>::T;
   constexpr int VW = (DPL * 2) / 4;           // bf16 words per V row slice (after conversion)
+  // a chunk is computed in sub-chunks of at most 4 row groups (64 tokens),
+  // which bounds the score registers
+  constexpr int NSUB = NRG > 4 ? NRG / 4 : 1;
+  constexpr int RGS = NRG / NSUB;
+  constexpr int KSS = NKS / NSUB;
   static_assert(CT % BS == 0 && NKL >= 1, "chunk shape");
+  static_assert(!FP4 || D == 128, "FP4 rows are 64 bytes: one 16-byte load per lane group");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -139,6 +152,7 @@ void decode_partition_mfma(DecodeArgs a) {
 
   // dims of MFMA step kk used by lane (c, g4); K and Q follow the same map
   auto dimbase = [&](int kk) -> int {
+    if constexpr (FP4) return 32 * g4 + 8 * kk;       // lane's 16 bytes hold dims 32 g4 ..
     return FP8 ? 64 * (kk >> 1) + 16 * g4 + 8 * (kk & 1) : 32 * kk + 8 * g4;
   };
 
@@ -155,9 +169,9 @@ void decode_partition_mfma(DecodeArgs a) {
     }
   }
   float qscale = a.scale * kLog2e;
-  if constexpr (FP8) qscale *= a.k_scale[g];
+  if constexpr (QNT) qscale *= a.k_scale[g];
 
-  const int64_t tile_bytes = static_cast<int64_t>(BS) * D * EB;
+  const int64_t tile_bytes = FP4 ? static_cast<int64_t>(BS) * RB : static_cast<int64_t>(BS) * D * EB;
   const int64_t head_off = static_cast<int64_t>(g) * tile_bytes;
   const int64_t block_stride = static_cast<int64_t>(a.n_kv) * tile_bytes;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
@@ -192,21 +206,26 @@ void decode_partition_mfma(DecodeArgs a) {
       const int bi = t / BS;
 #pragma unroll
       for (int kl = 0; kl < NKL; ++kl) {
-        const int dim = FP8 ? 64 * kl + 16 * g4 : 32 * kl + 8 * g4;
-        if (have[bi])
-          ld_stream(ch.k[rg][kl], kb[bi] + ((t % BS) * D + dim) * EB);
-        else
+        if (!have[bi]) {
           ch.k[rg][kl] = make_uint4(0, 0, 0, 0);
+        } else if constexpr (FP4) {
+          ld_stream(ch.k[rg][kl], kb[bi] + (t % BS) * RB + 16 * g4);
+        } else {
+          const int dim = FP8 ? 64 * kl + 16 * g4 : 32 * kl + 8 * g4;
+          ld_stream(ch.k[rg][kl], kb[bi] + ((t % BS) * D + dim) * EB);
+        }
       }
     }
 #pragma unroll
     for (int s = 0; s < NVS; ++s) {
       const int t = v_tok(s);
       const int bi = t / BS;
-      if (have[bi])
-        ld_stream(ch.v[s], vb[bi] + ((t % BS) * D + DPL * c) * EB);
-      else
+      if (!have[bi])
         ch.v[s] = VT{};
+      else if constexpr (FP4)
+        ld_stream(ch.v[s], vb[bi] + (t % BS) * RB + VB * c);
+      else
+        ld_stream(ch.v[s], vb[bi] + ((t % BS) * D + DPL * c) * EB);
     }
   };
 
@@ -219,42 +238,49 @@ void decode_partition_mfma(DecodeArgs a) {
 
   auto compute = [&](Chunk& ch, int ci) {
     const int tok0 = (blk0 + ci * BPC) * BS;           // first token of the chunk
-    // ---- scores: s[4*rg + i] is token 16*rg + 4*g4 + i for head c
-    float s[4 * NRG];
 #pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) {
+    for (int sub = 0; sub < NSUB; ++sub) {
+    // ---- scores: s[4*r + i] is token 16*(sub*RGS + r) + 4*g4 + i for head c
+    float s[4 * RGS];
+#pragma unroll
+    for (int r = 0; r < RGS; ++r) {
+      const int rg = sub * RGS + r;
       f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         bf16x8_t kop;
-        if constexpr (!FP8) {
+        if constexpr (FMT == kFmtBf16) {
           kop = __builtin_bit_cast(bf16x8_t, ch.k[rg][kk]);
-        } else {
+        } else if constexpr (FP8) {
           const uint4 w = ch.k[rg][kk >> 1];
           const uint32_t w0 = (kk & 1) ? w.z : w.x;
           const uint32_t w1 = (kk & 1) ? w.w : w.y;
           kop = as_bf16x8(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
                           fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
+        } else {
+          const uint32_t w = word(ch.k[rg][0], kk);    // 8 codes: dims 32 g4 + 8 kk ..
+          kop = as_bf16x8(fp4x2_to_bf16x2<0>(w), fp4x2_to_bf16x2<1>(w),
+                          fp4x2_to_bf16x2<2>(w), fp4x2_to_bf16x2<3>(w));
         }
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sc, 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[4 * rg + i] = sc[i] * qscale;
+      for (int i = 0; i < 4; ++i) s[4 * r + i] = sc[i] * qscale;
     }
     if (tok0 + CT > t1) {                              // only the partition's last chunk
 #pragma unroll
-      for (int rg = 0; rg < NRG; ++rg)
+      for (int r = 0; r < RGS; ++r)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (tok0 + 16 * rg + 4 * g4 + i >= t1) s[4 * rg + i] = -INFINITY;
+          if (tok0 + 16 * (sub * RGS + r) + 4 * g4 + i >= t1) s[4 * r + i] = -INFINITY;
 #pragma unroll
-      for (int si = 0; si < NVS; ++si)
+      for (int si = sub * 8 * KSS; si < (sub + 1) * 8 * KSS; ++si)
         if (tok0 + v_tok(si) >= t1) ch.v[si] = VT{};
     }
     // ---- online softmax for head c (shared by the 4 k-group lanes)
     float mx = s[0];
 #pragma unroll
-    for (int i = 1; i < 4 * NRG; ++i) mx = fmaxf(mx, s[i]);
+    for (int i = 1; i < 4 * RGS; ++i) mx = fmaxf(mx, s[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     m_true = fmaxf(m_true, mx);
@@ -268,12 +294,13 @@ void decode_partition_mfma(DecodeArgs a) {
       m_ref = m_new;
     }
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
+    for (int kq = 0; kq < KSS; ++kq) {
+      const int ks = sub * KSS + kq;
       // P^T operand of k-step ks: slots 0-3 row group 2ks, 4-7 row group 2ks+1
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = fast_exp2(s[8 * ks + i] - m_ref);
+        p[i] = fast_exp2(s[8 * kq + i] - m_ref);
         l += p[i];
       }
       uint32_t ph[4], pl[4];
@@ -294,16 +321,22 @@ void decode_partition_mfma(DecodeArgs a) {
       uint32_t vw[8][VW];
 #pragma unroll
       for (int si = 0; si < 8; ++si) {
-        if constexpr (!FP8) {
+        if constexpr (FMT == kFmtBf16) {
 #pragma unroll
           for (int w = 0; w < VW; ++w) vw[si][w] = word(ch.v[8 * ks + si], w);
-        } else {
+        } else if constexpr (FP8) {
 #pragma unroll
           for (int w = 0; w < VW / 2; ++w) {
             const uint32_t x = word(ch.v[8 * ks + si], w);
             vw[si][2 * w] = fp8x2_to_bf16x2<false>(x);
             vw[si][2 * w + 1] = fp8x2_to_bf16x2<true>(x);
           }
+        } else {
+          const uint32_t x = word(ch.v[8 * ks + si], 0);   // 8 codes: dims DPL c ..
+          vw[si][0] = fp4x2_to_bf16x2<0>(x);
+          vw[si][1] = fp4x2_to_bf16x2<1>(x);
+          vw[si][2] = fp4x2_to_bf16x2<2>(x);
+          vw[si][3] = fp4x2_to_bf16x2<3>(x);
         }
       }
 #pragma unroll
@@ -319,6 +352,7 @@ void decode_partition_mfma(DecodeArgs a) {
         if constexpr (SPLIT_P)
           acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo, acc[jj], 0, 0, 0);
       }
+    }
     }
   };
 
@@ -353,7 +387,7 @@ void decode_partition_mfma(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) sm_acc[wave][c][DPL * (4 * g4 + i) + jj] = acc[jj][i] * f;
   __syncthreads();
 
-  const float vscale = FP8 ? a.v_scale[g] : 1.0f;
+  const float vscale = QNT ? a.v_scale[g] : 1.0f;
   if (wave_parts) {
     // every wave's partition is a partial of its own
     for (int i = threadIdx.x; i < NW * nh * D; i += blockDim.x) {
@@ -410,10 +444,20 @@ void decode_partition_mfma(DecodeArgs a) {
 
 constexpr int kMfmaWaves = 4;
 
-template <int D, int BS, bool FP8>
+template <int D, int BS, int FMT>
 static hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  decode_partition_mfma<D, BS, FP8, kMfmaWaves, true><<<grid, kMfmaWaves * 64, 0, s>>>(a);
+  decode_partition_mfma<D, BS, FMT, kMfmaWaves, true><<<grid, kMfmaWaves * 64, 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <int D, int BS>
+static hipError_t launch_mfma_fmt(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  if (a.kv_dtype == PKV_FP8_E4M3) return launch_mfma<D, BS, kFmtFp8>(a, grid, s);
+  if (a.kv_dtype == PKV_FP4_E2M1) {
+    if constexpr (D == 128) return launch_mfma<D, BS, kFmtFp4>(a, grid, s);
+    return hipErrorInvalidValue;
+  }
+  return launch_mfma<D, BS, kFmtBf16>(a, grid, s);
 }
 
 hipError_t launch_decode_partition_mfma(const DecodeArgs& a, hipStream_t s) {
@@ -423,15 +467,9 @@ hipError_t launch_decode_partition_mfma(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid = a.schedule != nullptr
                         ? dim3(static_cast<unsigned>(static_cast<int64_t>(hxn) * a.B * a.P_max), 1, 1)
                         : dim3(hxn, a.B, gz);
-  const bool fp8 = a.kv_dtype == PKV_FP8_E4M3;
-  if (a.d == 128) {
-    if (a.bs == 16) return fp8 ? launch_mfma<128, 16, true>(a, grid, s)
-                               : launch_mfma<128, 16, false>(a, grid, s);
-    return fp8 ? launch_mfma<128, 32, true>(a, grid, s) : launch_mfma<128, 32, false>(a, grid, s);
-  }
-  if (a.bs == 16) return fp8 ? launch_mfma<64, 16, true>(a, grid, s)
-                             : launch_mfma<64, 16, false>(a, grid, s);
-  return fp8 ? launch_mfma<64, 32, true>(a, grid, s) : launch_mfma<64, 32, false>(a, grid, s);
+  if (a.d == 128)
+    return a.bs == 16 ? launch_mfma_fmt<128, 16>(a, grid, s) : launch_mfma_fmt<128, 32>(a, grid, s);
+  return a.bs == 16 ? launch_mfma_fmt<64, 16>(a, grid, s) : launch_mfma_fmt<64, 32>(a, grid, s);
 }
 
 }  // namespace pkv

@@ -86,6 +86,14 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// 2 FP4 E2M1 codes (byte B of w: low nibble first) -> 2 bf16 in one word,
+// exact (every E2M1 value is a bf16 value).
+template <int B>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w) {
+  auto r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   bf16x2_t v;

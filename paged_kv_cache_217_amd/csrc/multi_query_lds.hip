@@ -401,6 +401,7 @@ static hipError_t launch_lds(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_multi_query_lds(const DecodeArgs& a, hipStream_t s) {
+  if (a.kv_dtype == PKV_FP4_E2M1) return hipErrorInvalidValue;   // not built for FP4
   const bool fp8 = a.kv_dtype == PKV_FP8_E4M3;
   if (a.d == 128) {
     if (a.bs == 16) return fp8 ? launch_lds<128, 16, true>(a, s) : launch_lds<128, 16, false>(a, s);

@@ -460,6 +460,7 @@ static int forced_mq_kernel() {
 }
 
 hipError_t launch_multi_query_partition(const DecodeArgs& a, hipStream_t s) {
+  if (a.kv_dtype == PKV_FP4_E2M1) return hipErrorInvalidValue;   // not built for FP4
   const int G = a.n_q / a.n_kv;
   const int tiles = (a.Q * G + 15) / 16;
   const int forced = forced_mq_kernel();

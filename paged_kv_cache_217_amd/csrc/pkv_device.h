@@ -61,6 +61,28 @@ __device__ __forceinline__ uint32_t f32_to_fp8_e4m3_sat(float x) {
   return sign | code;
 }
 
+// float32 -> FP4 E2M1 code (0..15): round to nearest, ties to the even code;
+// magnitudes >= 6 (infinity included) saturate to 6; NaN stores +0 (the format
+// has neither); the sign is kept. Magnitudes step by 0.5 below 2, by 1 in
+// [2, 4) and by 2 in [4, 6]; rintf rounds half to even, which is the even code
+// in every range.
+__device__ __forceinline__ uint32_t f32_to_fp4_e2m1_sat(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t mag = u & 0x7fffffffu;
+  if (mag > 0x7f800000u) return 0u;                             // NaN
+  const uint32_t sign = (u >> 28) & 0x8u;
+  const float a = __uint_as_float(mag);
+  if (a >= 6.0f) return sign | 0x7u;
+  uint32_t code;
+  if (a < 2.0f)
+    code = static_cast<uint32_t>(__builtin_rintf(a * 2.0f));          // 0..4
+  else if (a < 4.0f)
+    code = static_cast<uint32_t>(__builtin_rintf(a)) + 2u;            // 4..6
+  else
+    code = static_cast<uint32_t>(__builtin_rintf(a * 0.5f)) + 4u;     // 6..7
+  return sign | code;
+}
+
 // ---------------------------------------------------------------- misc
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -12,11 +12,13 @@ queries, +90 for new tokens) on the device where they are created. Test-only sha
 
 FP8 caches are produced from N(0,1) data with one float32 scale per
 (K or V, KV head) equal to absmax / 448; the quotient is clamped to +-448 and
-cast with torch's float8_e4m3fn conversion (round to nearest even).
+cast with torch's float8_e4m3fn conversion (round to nearest even). FP4
+caches hold uniformly random bytes (two E2M1 codes each, every pattern
+valid; torch has no FP4 cast) with per-(K or V, KV head) scales U[0.25, 0.5).
 
 Poisoning: with `poison=True`, pool blocks that no table references and the
 slots of a sequence's last block past its length hold NaN (bfloat16 0x7FC0,
-FP8 0x7F). Table entries past a sequence's last block point at block 0 and
+FP8 0x7F), or for FP4, which has no NaN, the largest magnitude (0x77). Table entries past a sequence's last block point at block 0 and
 are never read.
 """
 
@@ -29,6 +31,7 @@ import torch
 
 BF16 = "bf16"
 FP8 = "fp8_e4m3"
+FP4 = "fp4_e2m1"
 
 STRUCT_SEED = 217000
 VALUE_SEED = 217100
@@ -64,7 +67,7 @@ class Workload:
 
     @property
     def p(self):
-        return 1 if self.kv_dtype == FP8 else 2
+        return 0.5 if self.kv_dtype == FP4 else 1 if self.kv_dtype == FP8 else 2
 
     @property
     def total_tokens(self):
@@ -255,6 +258,14 @@ def fp8_from_normal(x):
     return codes, s
 
 
+def fp4_codes(shape, g, device):
+    """Uniformly random FP4 E2M1 bytes (two codes each; every pattern is a
+    valid pair) and per-head scales, for caches whose last dimension is d / 2."""
+    codes = torch.randint(0, 256, shape, generator=g, device=device, dtype=torch.int32)
+    scale = 0.25 + torch.rand((shape[1],), generator=g, device=device, dtype=torch.float32) / 4
+    return codes.to(torch.uint8), scale
+
+
 def used_mask(w):
     """bool [num_blocks]: blocks referenced by some sequence's live entries."""
     used = np.zeros(w.num_blocks, dtype=bool)
@@ -268,6 +279,9 @@ def poison(w, k_cache, v_cache):
     """Set unused blocks and tail slots to NaN in place (bf16 or FP8 patterns)."""
     if w.kv_dtype == FP8:
         kv_k, kv_v, nanval = k_cache, v_cache, 0x7F
+    elif w.kv_dtype == FP4:
+        # E2M1 has no NaN: the largest magnitude in both nibbles instead
+        kv_k, kv_v, nanval = k_cache.view(torch.uint8), v_cache.view(torch.uint8), 0x77
     else:
         kv_k, kv_v, nanval = k_cache.view(torch.int16), v_cache.view(torch.int16), 0x7FC0
     unused = torch.from_numpy(~used_mask(w)).to(k_cache.device)
@@ -286,7 +300,13 @@ def make_cache(w, device="cpu", seed_offset=0, poison_unused=True):
     """Random K/V pools [num_blocks, n_kv, bs, d] (bf16, or uint8 FP8 codes + scales)."""
     g = _gen(VALUE_SEED + w.notes.get("seed", 0) + seed_offset, device)
     shape = (w.num_blocks, w.n_kv, w.bs, w.d)
-    if w.kv_dtype == FP8:
+    if w.kv_dtype == FP4:
+        half = shape[:3] + (w.d // 2,)
+        k_cache, k_scale = fp4_codes(half, g, device)
+        v_cache, v_scale = fp4_codes(half, g, device)
+        k_cache = k_cache.view(torch.float4_e2m1fn_x2)
+        v_cache = v_cache.view(torch.float4_e2m1fn_x2)
+    elif w.kv_dtype == FP8:
         kx = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
         k_cache, k_scale = fp8_from_normal(kx)
         del kx
@@ -329,6 +349,6 @@ def bits(t):
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.uint8:
         return t.numpy()
-    if t.dtype == torch.float8_e4m3fn:
+    if t.dtype in (torch.float8_e4m3fn, torch.float4_e2m1fn_x2):
         return t.view(torch.uint8).numpy()
     raise TypeError(t.dtype)
