@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gqa_70b",
-                    choices=["gqa_70b", "mha_7b", "gqa_70b_fp8", "long_prefix", "tiny",
+                    choices=["gqa_70b", "mha_7b", "gqa_70b_fp8", "gqa_70b_fp4", "long_prefix", "tiny",
                              "spec_verify_70b", "chunked_prefill_70b", "shared_prompt_70b"])
     ap.add_argument("--layers", type=int, default=0, help="override layer count (0: workload's)")
     ap.add_argument("--partition", type=int, default=0, help="split-K partition (0: library)")
@@ -128,7 +128,7 @@ def main():
     layers = args.layers or w.layers
     B, n_q, n_kv, d, bs = w.B, w.n_q, w.n_kv, w.d, w.bs
     max_ctx = int(w.context_lens.max())
-    fp8 = w.kv_dtype == W.FP8
+    fp8 = w.kv_dtype in (W.FP8, W.FP4)          # quantised: per-head scales
     log(f"[bench] workload {w.name}: B={B} n_q={n_q} n_kv={n_kv} d={d} bs={bs} "
         f"{w.kv_dtype} layers={layers} tokens={w.total_tokens} pool={w.num_blocks} blocks/layer")
 
@@ -240,7 +240,7 @@ def main():
                   + B * n_q * d * 2                               # q
                   + sum(-(-int(c) // bs) for c in w.context_lens) * 4   # block-table entries
                   + (sum(nP) * n_q * (d + 2) * 4 if split else B * n_q * d * 4)  # partials/out
-                  + (2 * n_kv * 4 if fp8 else 0))                 # FP8 scales
+                  + (2 * n_kv * 4 if fp8 else 0))                 # FP8 / FP4 scales
     achieved = part_bytes / (ms_part * 1e-3) / 1e9
     kv_gbs = kv_bytes_layer * layers / (ms_step * 1e-3) / 1e9
     tok_s = B / (ms_step * 1e-3)
@@ -263,7 +263,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if not fp8 else "fp8_e4m3",
+        "dtype": w.kv_dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "context": max_ctx if len(set(
             w.context_lens.tolist())) == 1 else "varied", "tokens_per_layer": tokens,

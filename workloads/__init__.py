@@ -154,6 +154,17 @@ def gqa_70b(layers=80):
                     1.0 / math.sqrt(128), layers=layers, notes={"seed": 3})
 
 
+def gqa_70b_fp4(layers=80):
+    """The 70B decode step with an FP4 E2M1 cache: B=64 x 8192 tokens, 64/8
+    heads, d=128, bs=32 (2 KiB per (block, head) tile), 80 layer pools."""
+    ctx = np.full(64, 8192, dtype=np.int32)
+    pool = 64 * 256
+    perm = torch.randperm(pool, generator=_gen(STRUCT_SEED + 9)).numpy().astype(np.int32)
+    bt = _tables_from_perm(ctx, 32, perm)
+    return Workload("gqa_70b_fp4_80_layers", 64, 64, 8, 128, 32, FP4, ctx, bt, pool,
+                    1.0 / math.sqrt(128), layers=layers, notes={"seed": 9})
+
+
 def lognormal_lengths(n, median, sigma, cap, g):
     z = torch.randn(n, generator=g, dtype=torch.float64).numpy()
     ctx = np.rint(np.exp(np.log(median) + sigma * z))
@@ -240,7 +251,8 @@ def shared_prompt_70b(layers=8):
 
 ALL = {"tiny": tiny, "mha_7b": mha_7b, "gqa_70b": gqa_70b, "gqa_70b_fp8": gqa_70b_fp8,
        "long_prefix": long_shared_prefix, "spec_verify_70b": spec_verify_70b,
-       "chunked_prefill_70b": chunked_prefill_70b, "shared_prompt_70b": shared_prompt_70b}
+       "chunked_prefill_70b": chunked_prefill_70b, "shared_prompt_70b": shared_prompt_70b,
+       "gqa_70b_fp4": gqa_70b_fp4}
 
 
 # ---------------------------------------------------------------- values
