@@ -234,7 +234,7 @@ def main():
     # ---------------------------------------------------------------- accounting
     p = w.p
     tokens = w.total_tokens
-    kv_bytes_layer = tokens * n_kv * d * p * 2
+    kv_bytes_layer = int(tokens * n_kv * d * p * 2)
     nP = [max(1, -(-int(c) // P)) if c > 0 else 0 for c in w.context_lens]
     part_bytes = (kv_bytes_layer                                  # K and V
                   + B * n_q * d * 2                               # q
