@@ -43,7 +43,9 @@ __global__ __launch_bounds__(R * S * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void multi_query_partition_mfma(DecodeArgs a) {
   constexpr int NW = R * S;
   constexpr int GR = 16 * TPW * R;            // rows per workgroup
-  constexpr int CT = FP8 ? 64 : 32;           // tokens per chunk
+  // tokens per chunk: FP8 rows are half as wide, so a single-tile wave takes
+  // twice the tokens per load; with two tiles the scores would not fit
+  constexpr int CT = FP8 && TPW == 1 ? 64 : 32;
   constexpr int NRG = CT / 16;                // 16-token row groups per chunk
   constexpr int NKS = CT / 32;                // 32-token PV k-steps per chunk
   constexpr int NKK = D / 32;                 // QK MFMA steps over d
@@ -82,6 +84,11 @@ void multi_query_partition_mfma(DecodeArgs a) {
   __shared__ float sm_m[NW][TPW * 16];
   __shared__ float sm_l[NW][TPW * 16];
   __shared__ float sm_acc[NW][TPW * 16][D + 4];
+  // with several tiles per wave the query operands are staged in LDS and read
+  // per chunk: held in registers for the whole loop they would not fit
+  constexpr bool QLDS = TPW > 1;
+  constexpr int QLD = D + 8;                          // padded row (bf16 elements)
+  __shared__ __align__(16) uint16_t sm_q[QLDS ? R * TPW * 16 : 1][QLD];
 
   // last position of the query among rows [r0, r1) (r1 > r0), or -1 if none
   auto last_pos = [&](int r0, int r1) -> int {
@@ -120,23 +127,54 @@ void multi_query_partition_mfma(DecodeArgs a) {
   auto dimbase = [&](int kk) -> int {
     return FP8 ? 64 * (kk >> 1) + 16 * g4 + 8 * (kk & 1) : 32 * kk + 8 * g4;
   };
-  bf16x8_t qop[TPW][NKK];
+  bf16x8_t qop[QLDS ? 1 : TPW][NKK];
   int pos[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int row = wrow0 + 16 * t + c;
-    const int qi = row / G;
-    const bool live_row = row < rows && qi < ql;
-    pos[t] = qpos(qi);                           // last token this row may see
-    const int64_t qrow =
-        live_row ? (static_cast<int64_t>(b) * a.Q + qi) * a.n_q + g * G + row % G : 0;
+    pos[t] = qpos(row / G);                      // last token this row may see
+  }
+  if constexpr (QLDS) {
+    // the workgroup's rows (zeros for rows without a query), then a barrier
+    for (int e = threadIdx.x; e < R * TPW * 16 * (D / 8); e += blockDim.x) {
+      const int r = e / (D / 8);
+      const int col = 8 * (e % (D / 8));
+      const int row = row0 + r;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (row < rows && row / G < ql)
+        w = *reinterpret_cast<const uint4*>(
+            a.q + ((static_cast<int64_t>(b) * a.Q + row / G) * a.n_q + g * G + row % G) * D +
+            col);
+      *reinterpret_cast<uint4*>(&sm_q[r][col]) = w;
+    }
+    __syncthreads();
+  } else {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      uint4 w = *reinterpret_cast<const uint4*>(a.q + qrow * D + dimbase(kk));
-      if (!live_row) w = make_uint4(0, 0, 0, 0);
-      qop[t][kk] = __builtin_bit_cast(bf16x8_t, w);
+    for (int t = 0; t < TPW; ++t) {
+      const int row = wrow0 + 16 * t + c;
+      const int qi = row / G;
+      const bool live_row = row < rows && qi < ql;
+      const int64_t qrow =
+          live_row ? (static_cast<int64_t>(b) * a.Q + qi) * a.n_q + g * G + row % G : 0;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        uint4 w = *reinterpret_cast<const uint4*>(a.q + qrow * D + dimbase(kk));
+        if (!live_row) w = make_uint4(0, 0, 0, 0);
+        qop[t][kk] = __builtin_bit_cast(bf16x8_t, w);
+      }
     }
   }
+  // query operand of tile t, step kk; `salt` is 0 for every real token index
+  // but not provably so, which keeps the LDS reads inside the chunk loop
+  auto q_operand = [&](int t, int kk, int salt) -> bf16x8_t {
+    if constexpr (!QLDS) {
+      return qop[t][kk];
+    } else {
+      const char* base = reinterpret_cast<const char*>(&sm_q[tl * TPW * 16 + 16 * t + c][0]);
+      return __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(base + 2 * dimbase(kk) + salt));
+    }
+  };
   float qscale = a.scale * kLog2e;
   if constexpr (FP8) qscale *= a.k_scale[g];
 
@@ -209,13 +247,21 @@ void multi_query_partition_mfma(DecodeArgs a) {
   // scores of chunk ci (base-2 units), masked causally and at the partition end
   auto qk = [&](const KChunk& kc, int ci, Scores& s) {
     const int tok0 = (blk0 + ci * BPC) * BS;
+    const int salt = (tok0 >> 31) & 16;
+    // d-step outermost: each query operand is read once per chunk and applied
+    // to every row group while it is live
+    f32x4_t sc[NRG][TPW];
 #pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) {
-      f32x4_t sc[TPW];
+    for (int rg = 0; rg < NRG; ++rg)
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) sc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int t = 0; t < TPW; ++t) sc[rg][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
+    for (int kk = 0; kk < NKK; ++kk) {
+      bf16x8_t qo[TPW];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) qo[t] = q_operand(t, kk, salt);
+#pragma unroll
+      for (int rg = 0; rg < NRG; ++rg) {
         bf16x8_t kop;
         if constexpr (!FP8) {
           kop = __builtin_bit_cast(bf16x8_t, kc.k[rg][kk]);
@@ -228,13 +274,15 @@ void multi_query_partition_mfma(DecodeArgs a) {
         }
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
-          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[t][kk], sc[t], 0, 0, 0);
+          sc[rg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qo[t], sc[rg][t], 0, 0, 0);
       }
+    }
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg)
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[t][4 * rg + i] = sc[t][i] * qscale;
-    }
+        for (int i = 0; i < 4; ++i) s[t][4 * rg + i] = sc[rg][t][i] * qscale;
     if (tok0 + CT > min(p_lo + 1, t1)) {
       // causal: each row sees tokens up to its own position, and nothing past
       // the partition's end (such slots were not loaded)
