@@ -107,6 +107,41 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group,
+// lane a supplies the address of 4 consecutive 16-bit elements M[a][0..3];
+// lane j receives M[4 i + j / 4][j % 4] for i = 0..3 (layout measured on
+// gfx950). Pointing lane a at row a / 4 of a matrix, columns 4 (a % 4) ..,
+// hands lane j column j of 4 consecutive rows: a 4 x 16 block transposed.
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  typedef short s4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4_t lds_s4_t;
+  const s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// x combined with the value of lane ^ 16 (resp. lane ^ 32) through the
+// gfx950 row-swap moves instead of an LDS permute
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace mfma
 
 }  // namespace pkv

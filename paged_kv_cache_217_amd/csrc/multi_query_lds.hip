@@ -167,10 +167,15 @@ void multi_query_lds_mfma(DecodeArgs a) {
       ld_stream(st.v[k], tile_rsrc(a.v_cache + p * block_stride + head_off, bytes), off, 0);
     }
   };
-  auto commit = [&](const Stage& st, int buf) {
+  // V slots past t1 may hold anything (NaN in a tail block): they are
+  // zeroed here, once per chunk, so that P = 0 times them gives 0. K needs
+  // nothing: the scores of those slots are replaced by -inf.
+  auto commit = [&](Stage& st, int buf, int ci) {
+    const int tok0 = t0 + ci * CT;
 #pragma unroll
     for (int k = 0; k < PIECES; ++k) {
       const int e = threadIdx.x + 256 * k;
+      if (tok0 + CT > t1 && tok0 + (16 * e) / RB >= t1) st.v[k] = make_uint4(0, 0, 0, 0);
       const int at = (16 * e) / RB * LR + (16 * e) % RB;
       *reinterpret_cast<uint4*>(&sk[buf][at]) = st.k[k];
       *reinterpret_cast<uint4*>(&sv[buf][at]) = st.v[k];
@@ -194,9 +199,11 @@ void multi_query_lds_mfma(DecodeArgs a) {
   }
 
   // per-lane LDS offsets: K token c at dims of lane group g4; V token 4 g4 at
-  // dims VB c / EB
+  // dims VB c / EB (FP8); bf16 V is read transposed: lane (c, g4) addresses
+  // token 4 g4 + c / 4, dims 4 (c % 4) .. of a 16-dim column block
   const int k_lane = c * LR + 16 * g4;
   const int v_lane = 4 * g4 * LR + VB * c;
+  const int v_tr = (4 * g4 + c / 4) * LR + 8 * (c % 4);
   auto compute = [&](int buf, int ci) {
     const uint8_t* kl_ = sk[buf];
     const uint8_t* vl_ = sv[buf];
@@ -253,8 +260,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
       float mx = s[t][0];
 #pragma unroll
       for (int i = 1; i < 4 * NRG; ++i) mx = fmaxf(mx, s[t][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_xor32(max_xor16(mx));
       m_true[t] = fmaxf(m_true[t], mx);
       const bool need = mx > m_ref[t] + kLazyRescale;
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -266,7 +272,6 @@ void multi_query_lds_mfma(DecodeArgs a) {
       }
       m_use[t] = m_ref[t] == -INFINITY ? 0.0f : m_ref[t];
     }
-    const bool tail = tok0 + CT > t1;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       bf16x8_t pop_hi[TPW], pop_lo[TPW];
@@ -289,16 +294,29 @@ void multi_query_lds_mfma(DecodeArgs a) {
         pop_hi[t] = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
         pop_lo[t] = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
       }
-      uint32_t vw[8][VW];
+      if constexpr (!FP8) {
+        // V^T operand of dims 16 jj ..: tokens 4 g4 .. (first half) and
+        // 16 + 4 g4 .. (second half) of the k-step, straight from LDS
 #pragma unroll
-      for (int si = 0; si < 8; ++si) {
-        const int tv = v_tok(8 * ks + si);
-        VT v = *reinterpret_cast<const VT*>(vl_ + v_lane + (tv - 4 * g4) * LR);
-        if (tail && tok0 + tv >= t1) v = VT{};        // slots past the end may hold NaN
-        if constexpr (!FP8) {
+        for (int jj = 0; jj < NJ; ++jj) {
+          const uint8_t* vt = vl_ + v_tr + 32 * ks * LR + 32 * jj;
+          const uint2 v0 = lds_read_tr16(vt);
+          const uint2 v1 = lds_read_tr16(vt + 16 * LR);
+          const bf16x8_t vop = as_bf16x8(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
-          for (int w = 0; w < VW; ++w) vw[si][w] = word(v, w);
-        } else {
+          for (int t = 0; t < TPW; ++t) {
+            acc[t][jj] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi[t], acc[t][jj], 0, 0, 0);
+            acc[t][jj] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[t], acc[t][jj], 0, 0, 0);
+          }
+        }
+      } else {
+        uint32_t vw[8][VW];
+#pragma unroll
+        for (int si = 0; si < 8; ++si) {
+          const int tv = v_tok(8 * ks + si);
+          const VT v = *reinterpret_cast<const VT*>(vl_ + v_lane + (tv - 4 * g4) * LR);
 #pragma unroll
           for (int w = 0; w < VW / 2; ++w) {
             const uint32_t x = word(v, w);
@@ -306,20 +324,22 @@ void multi_query_lds_mfma(DecodeArgs a) {
             vw[si][2 * w + 1] = fp8x2_to_bf16x2<true>(x);
           }
         }
-      }
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) {
-        const int w = jj >> 1;
-        const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t t4[4];
+        for (int jj = 0; jj < NJ; ++jj) {
+          const int w = jj >> 1;
+          const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+          uint32_t t4[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          t4[u] = __builtin_amdgcn_perm(vw[2 * u + 1][w], vw[2 * u][w], sel);
-        const bf16x8_t vop = as_bf16x8(t4[0], t4[1], t4[2], t4[3]);
+          for (int u = 0; u < 4; ++u)
+            t4[u] = __builtin_amdgcn_perm(vw[2 * u + 1][w], vw[2 * u][w], sel);
+          const bf16x8_t vop = as_bf16x8(t4[0], t4[1], t4[2], t4[3]);
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-          acc[t][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi[t], acc[t][jj], 0, 0, 0);
-          acc[t][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[t], acc[t][jj], 0, 0, 0);
+          for (int t = 0; t < TPW; ++t) {
+            acc[t][jj] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi[t], acc[t][jj], 0, 0, 0);
+            acc[t][jj] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[t], acc[t][jj], 0, 0, 0);
+          }
         }
       }
     }
@@ -333,8 +353,8 @@ void multi_query_lds_mfma(DecodeArgs a) {
     Stage sa, sb;
     fetch(sa, 0);
     if (n_ch > 1) fetch(sb, 1);
-    commit(sa, 0);
-    if (n_ch > 1) commit(sb, 1);
+    commit(sa, 0, 0);
+    if (n_ch > 1) commit(sb, 1, 1);
     __syncthreads();
     for (int ci = 0, h = 0; ci < n_ch; ci += 2, h ^= 1) {
       const bool more = ci + 2 < n_ch;
@@ -342,19 +362,22 @@ void multi_query_lds_mfma(DecodeArgs a) {
       if (ci + 3 < n_ch) fetch(sb, ci + 3);
       compute(2 * h, ci);
       if (ci + 1 < n_ch) compute(2 * h + 1, ci + 1);
-      if (more) commit(sa, 2 * (h ^ 1));
-      if (ci + 3 < n_ch) commit(sb, 2 * (h ^ 1) + 1);
+      if (more) commit(sa, 2 * (h ^ 1), ci + 2);
+      if (ci + 3 < n_ch) commit(sb, 2 * (h ^ 1) + 1, ci + 3);
       __syncthreads();
     }
   }
 
-  // outputs: lane (c, g4) holds dims DPL (4 g4 + i) + jj of row 16 t + c
+  // outputs: lane (c, g4) holds, of row 16 t + c, dims 16 jj + 4 g4 + i
+  // (bf16: V read transposed) or DPL (4 g4 + i) + jj (FP8)
+  auto odim = [&](int jj, int i) -> int {
+    return FP8 ? DPL * (4 * g4 + i) + jj : 16 * jj + 4 * g4 + i;
+  };
   const float vscale = FP8 ? a.v_scale[g] : 1.0f;
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     float lt = l[t];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    lt = sum_xor32(sum_xor16(lt));
     const float f = m_true[t] == -INFINITY ? 0.0f : fast_exp2(m_ref[t] - m_true[t]);
     const float L = lt * f;
     const int rr = wrow0 + 16 * t + c;
@@ -373,20 +396,20 @@ void multi_query_lds_mfma(DecodeArgs a) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj)
-          a.ws_o[mi * D + DPL * (4 * g4 + i) + jj] = acc[t][jj][i] * inv;
+          a.ws_o[mi * D + odim(jj, i)] = acc[t][jj][i] * inv;
     } else if (a.out_dtype == PKV_FP32) {
       float* o = static_cast<float*>(a.out) + orow * D;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) o[DPL * (4 * g4 + i) + jj] = acc[t][jj][i] * inv;
+        for (int jj = 0; jj < NJ; ++jj) o[odim(jj, i)] = acc[t][jj][i] * inv;
     } else {
       uint16_t* o = static_cast<uint16_t*>(a.out) + orow * D;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj)
-          o[DPL * (4 * g4 + i) + jj] = f32_to_bf16_rne(acc[t][jj][i] * inv);
+          o[odim(jj, i)] = f32_to_bf16_rne(acc[t][jj][i] * inv);
     }
   }
 }
