@@ -28,11 +28,14 @@
  * K_Buffer / V_Buffer shape): K and V caches are separate arrays
  * [num_blocks, n_kv, block_size, d_head]; element type bfloat16, or OCP FP8
  * E4M3FN codes (one byte) with one fp32 scale per KV head for K and one for
- * V ([SMTS] "Technical Q&A", per-head scaling factors). One (block, head)
- * tile of block_size * d_head elements is contiguous.
+ * V ([SMTS] "Technical Q&A", per-head scaling factors), or FP4 E2M1 codes
+ * (half a byte per element, as [MTKV] "The Anatomy of the KV-Cache Memory
+ * Wall" prices 4-bit KV; two codes per byte, element 2i in the low nibble,
+ * so a row is d_head / 2 bytes) with the same per-head scales. One (block,
+ * head) tile of block_size * d_head elements is contiguous.
  *
- * Supported geometry: block_size in {16, 32}; d_head in {64, 128};
- * n_q = G * n_kv with G in {1, 2, 4, 8, 16} or any multiple of 16.
+ * Supported geometry: block_size in {16, 32}; d_head in {64, 128} (FP4:
+ * 128); n_q = G * n_kv with G in {1, 2, 4, 8, 16} or any multiple of 16.
  * Anything else returns PKV_ERR_UNSUPPORTED.
  */
 #ifndef PKV_H
@@ -57,7 +60,7 @@ typedef enum {
 typedef enum { PKV_BF16 = 0, PKV_FP8_E4M3 = 1, PKV_FP32 = 2, PKV_FP4_E2M1 = 3 } pkv_dtype;
 
 /* Geometry of one layer's K/V pools (both share it). kv_dtype is a pkv_dtype:
- * PKV_BF16 or PKV_FP8_E4M3. */
+ * PKV_BF16, PKV_FP8_E4M3 or PKV_FP4_E2M1. */
 typedef struct {
   int32_t num_blocks;
   int32_t block_size;
@@ -96,9 +99,12 @@ pkv_status pkv_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_
  *   (same for V), with slot = slot_mapping[t] (int64, device).
  * store() copies the bfloat16 pattern for a BF16 cache; for an FP8 cache it is
  * E4M3FN(round-to-nearest-even, saturating at +-448)(float32(x) / k_scale[h]),
- * the division in IEEE binary32; NaN stores 0x7F.
+ * the division in IEEE binary32; NaN stores 0x7F. For an FP4 cache it is
+ * E2M1(round-to-nearest-even, saturating at +-6)(float32(x) / k_scale[h])
+ * (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; sign kept, -0 included); NaN
+ * stores +0.
  * k_new, v_new: bfloat16 [T, n_kv, d_head] (device). k_scale, v_scale: fp32
- * [n_kv] device pointers, required for FP8, ignored for BF16.
+ * [n_kv] device pointers, required for FP8 and FP4, ignored for BF16.
  * A negative slot is skipped (padding). A slot >= num_blocks * bs is skipped.
  * Two tokens with the same slot: the stored value is unspecified.
  * ------------------------------------------------------------------------- */
@@ -117,7 +123,8 @@ pkv_status pkv_kv_append(const pkv_cache_desc* desc, void* k_cache, void* v_cach
  *   out[b, h, :] = sum_{t < ctx_b} w_t * V_b[t, h / G, :],
  *   w = softmax_t(scale * q[b, h, :] . K_b[t, h / G, :]),
  * with K_b[t, g, :] = k_cache[block_tables[b, t / bs], g, t % bs, :]
- * (times k_scale[g] for FP8; likewise V with v_scale). ctx_b == 0 gives zeros.
+ * (decoded and times k_scale[g] for FP8 and FP4; likewise V with v_scale).
+ * ctx_b == 0 gives zeros.
  * Slots past ctx_b in a sequence's last block never contribute, whatever they
  * hold (NaN included); table entries past cdiv(ctx_b, bs) are never read.
  *

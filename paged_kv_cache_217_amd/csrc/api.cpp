@@ -345,7 +345,6 @@ pkv_status pkv_paged_multi_query_attention(const pkv_cache_desc* desc, void* out
                                            int32_t partition_size, void* workspace,
                                            size_t workspace_bytes_, void* stream) {
   if (Q <= 0) return PKV_ERR_INVALID_ARG;
-  if (desc && desc->kv_dtype == PKV_FP4_E2M1) return PKV_ERR_UNSUPPORTED;   // decode only
   if (desc && check_desc(desc) == PKV_OK && n_q > 0 && n_q % desc->n_kv == 0 &&
       partition_size == 0 && B >= 0 && max_context_len >= 0)
     partition_size = pick_partition_mq(desc, B, Q, n_q, max_context_len);
@@ -400,7 +399,6 @@ pkv_status plan_cascade(const pkv_cache_desc* desc, int32_t B, int32_t n_q, int3
                         int32_t suffix_partition, CascadePlan* pl) {
   pkv_status st = check_desc(desc);
   if (st != PKV_OK) return st;
-  if (desc->kv_dtype == PKV_FP4_E2M1 && prefix_len > 0) return PKV_ERR_UNSUPPORTED;
   if (B < 0 || n_q <= 0 || n_q % desc->n_kv != 0 || prefix_len < 0 || max_suffix_len < 0 ||
       prefix_partition < 0 || suffix_partition < 0)
     return PKV_ERR_INVALID_ARG;

@@ -58,9 +58,6 @@ namespace pkv {
 
 using namespace mfma;
 
-// KV element formats of the kernel template.
-constexpr int kFmtBf16 = 0, kFmtFp8 = 1, kFmtFp4 = 2;
-
 // Two waves per SIMD: the register budget is 256 per lane (arch + acc).
 template <int D, int BS, int FMT, int NW, bool SPLIT_P>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))

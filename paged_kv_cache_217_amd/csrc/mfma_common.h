@@ -14,6 +14,9 @@ namespace mfma {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyRescale = 8.0f;     // log2 of the largest weight allowed before rescaling
 
+// KV element formats of the kernel templates
+constexpr int kFmtBf16 = 0, kFmtFp8 = 1, kFmtFp4 = 2;
+
 template <int BYTES>
 struct Vec;
 template <>

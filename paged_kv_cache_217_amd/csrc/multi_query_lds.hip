@@ -34,23 +34,26 @@ namespace pkv {
 
 using namespace mfma;
 
-template <int D, int BS, bool FP8>
+template <int D, int BS, int FMT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void multi_query_lds_mfma(DecodeArgs a) {
+  constexpr bool FP8 = FMT == kFmtFp8;
+  constexpr bool FP4 = FMT == kFmtFp4;        // two E2M1 codes per byte, d = 128 only
+  constexpr bool QNT = FMT != kFmtBf16;       // per-head scales
   constexpr int NW = 4;                       // waves
   constexpr int TPW = 2;                      // 16-row tiles per wave
   constexpr int GR = NW * TPW * 16;           // rows per workgroup
-  constexpr int CT = FP8 ? 64 : 32;           // tokens per chunk
+  constexpr int CT = QNT ? 64 : 32;           // tokens per chunk
   constexpr int NRG = CT / 16;                // 16-token row groups per chunk
   constexpr int NKS = CT / 32;                // 32-token PV k-steps per chunk
   constexpr int NKK = D / 32;                 // QK MFMA steps over d
   constexpr int NJ = D / 16;                  // PV MFMAs per k-step
   constexpr int DPL = D / 16;                 // dims per lane per V row
-  constexpr int EB = FP8 ? 1 : 2;             // bytes per element
-  constexpr int VB = DPL * EB;                // bytes of one lane's V slice
+  constexpr int RB = FP4 ? D / 2 : FP8 ? D : 2 * D;   // bytes per token row
+  constexpr int VB = FP4 ? DPL / 2 : FP8 ? DPL : 2 * DPL;   // bytes of one lane's V slice
   using VT = typename Vec<VB>::T;
   constexpr int VW = (DPL * 2) / 4;           // bf16 words per V slice
-  constexpr int RB = D * EB;                  // bytes per token row
+  static_assert(!FP4 || D == 128, "FP4 is built for d = 128");
   constexpr int LR = RB + 16;                 // padded LDS row
   constexpr int CB = CT * RB;                 // bytes of K (or V) per chunk
   constexpr int LB = CT * LR;                 // LDS bytes of K (or V) per chunk
@@ -117,6 +120,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
   const int wrow0 = row0 + wave * TPW * 16;
   const int p_lo = qpos(wrow0 / G);
   auto dimbase = [&](int kk) -> int {
+    if constexpr (FP4) return 32 * g4 + 8 * kk;
     return FP8 ? 64 * (kk >> 1) + 16 * g4 + 8 * (kk & 1) : 32 * kk + 8 * g4;
   };
   bf16x8_t qop[TPW][NKK];
@@ -137,7 +141,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
     }
   }
   float qscale = a.scale * kLog2e;
-  if constexpr (FP8) qscale *= a.k_scale[g];
+  if constexpr (QNT) qscale *= a.k_scale[g];
 
   __shared__ __align__(16) uint8_t sk[4][LB];
   __shared__ __align__(16) uint8_t sv[4][LB];
@@ -199,7 +203,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
   }
 
   // per-lane LDS offsets: K token c at dims of lane group g4; V token 4 g4 at
-  // dims VB c / EB (FP8); bf16 V is read transposed: lane (c, g4) addresses
+  // dims DPL c (FP8, FP4); bf16 V is read transposed: lane (c, g4) addresses
   // token 4 g4 + c / 4, dims 4 (c % 4) .. of a 16-dim column block
   const int k_lane = c * LR + 16 * g4;
   const int v_lane = 4 * g4 * LR + VB * c;
@@ -222,8 +226,13 @@ void multi_query_lds_mfma(DecodeArgs a) {
       for (int rg = 0; rg < NRG; ++rg) {
         const uint8_t* kt = kl_ + k_lane + 16 * rg * LR;   // this lane's K token 16 rg + c
         bf16x8_t kop;
-        if constexpr (!FP8) {
+        if constexpr (FMT == kFmtBf16) {
           kop = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kt + 64 * kk));
+        } else if constexpr (FP4) {
+          // 32 codes at dims 32 g4 .., of which this step uses the 8 at 8 kk
+          const uint32_t w = word(*reinterpret_cast<const uint4*>(kt), kk);
+          kop = as_bf16x8(fp4x2_to_bf16x2<0>(w), fp4x2_to_bf16x2<1>(w),
+                          fp4x2_to_bf16x2<2>(w), fp4x2_to_bf16x2<3>(w));
         } else {
           // 16 FP8 codes at dims 64 (kk / 2) + 16 g4, of which this step uses 8
           const uint4 w = *reinterpret_cast<const uint4*>(kt + 64 * (kk >> 1));
@@ -294,7 +303,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
         pop_hi[t] = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
         pop_lo[t] = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
       }
-      if constexpr (!FP8) {
+      if constexpr (FMT == kFmtBf16) {
         // V^T operand of dims 16 jj ..: tokens 4 g4 .. (first half) and
         // 16 + 4 g4 .. (second half) of the k-step, straight from LDS
 #pragma unroll
@@ -317,11 +326,19 @@ void multi_query_lds_mfma(DecodeArgs a) {
         for (int si = 0; si < 8; ++si) {
           const int tv = v_tok(8 * ks + si);
           const VT v = *reinterpret_cast<const VT*>(vl_ + v_lane + (tv - 4 * g4) * LR);
+          if constexpr (FP4) {
+            const uint32_t x = word(v, 0);
+            vw[si][0] = fp4x2_to_bf16x2<0>(x);
+            vw[si][1] = fp4x2_to_bf16x2<1>(x);
+            vw[si][2] = fp4x2_to_bf16x2<2>(x);
+            vw[si][3] = fp4x2_to_bf16x2<3>(x);
+          } else {
 #pragma unroll
-          for (int w = 0; w < VW / 2; ++w) {
-            const uint32_t x = word(v, w);
-            vw[si][2 * w] = fp8x2_to_bf16x2<false>(x);
-            vw[si][2 * w + 1] = fp8x2_to_bf16x2<true>(x);
+            for (int w = 0; w < VW / 2; ++w) {
+              const uint32_t x = word(v, w);
+              vw[si][2 * w] = fp8x2_to_bf16x2<false>(x);
+              vw[si][2 * w + 1] = fp8x2_to_bf16x2<true>(x);
+            }
           }
         }
 #pragma unroll
@@ -369,11 +386,11 @@ void multi_query_lds_mfma(DecodeArgs a) {
   }
 
   // outputs: lane (c, g4) holds, of row 16 t + c, dims 16 jj + 4 g4 + i
-  // (bf16: V read transposed) or DPL (4 g4 + i) + jj (FP8)
+  // (bf16: V read transposed) or DPL (4 g4 + i) + jj (FP8, FP4)
   auto odim = [&](int jj, int i) -> int {
-    return FP8 ? DPL * (4 * g4 + i) + jj : 16 * jj + 4 * g4 + i;
+    return QNT ? DPL * (4 * g4 + i) + jj : 16 * jj + 4 * g4 + i;
   };
-  const float vscale = FP8 ? a.v_scale[g] : 1.0f;
+  const float vscale = QNT ? a.v_scale[g] : 1.0f;
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     float lt = l[t];
@@ -414,24 +431,27 @@ void multi_query_lds_mfma(DecodeArgs a) {
   }
 }
 
-template <int D, int BS, bool FP8>
+template <int D, int BS, int FMT>
 static hipError_t launch_lds(const DecodeArgs& a, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
   const int groups = (a.Q * G + 127) / 128;
   const dim3 grid(a.n_kv * groups, a.B, a.P_max);
-  multi_query_lds_mfma<D, BS, FP8><<<grid, 256, 0, s>>>(a);
+  multi_query_lds_mfma<D, BS, FMT><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
+template <int D, int BS>
+static hipError_t launch_lds_fmt(const DecodeArgs& a, hipStream_t s) {
+  if (a.kv_dtype == PKV_FP8_E4M3) return launch_lds<D, BS, kFmtFp8>(a, s);
+  if constexpr (D == 128)
+    if (a.kv_dtype == PKV_FP4_E2M1) return launch_lds<D, BS, kFmtFp4>(a, s);
+  if (a.kv_dtype != PKV_BF16) return hipErrorInvalidValue;
+  return launch_lds<D, BS, kFmtBf16>(a, s);
+}
+
 hipError_t launch_multi_query_lds(const DecodeArgs& a, hipStream_t s) {
-  if (a.kv_dtype == PKV_FP4_E2M1) return hipErrorInvalidValue;   // not built for FP4
-  const bool fp8 = a.kv_dtype == PKV_FP8_E4M3;
-  if (a.d == 128) {
-    if (a.bs == 16) return fp8 ? launch_lds<128, 16, true>(a, s) : launch_lds<128, 16, false>(a, s);
-    return fp8 ? launch_lds<128, 32, true>(a, s) : launch_lds<128, 32, false>(a, s);
-  }
-  if (a.bs == 16) return fp8 ? launch_lds<64, 16, true>(a, s) : launch_lds<64, 16, false>(a, s);
-  return fp8 ? launch_lds<64, 32, true>(a, s) : launch_lds<64, 32, false>(a, s);
+  if (a.d == 128) return a.bs == 16 ? launch_lds_fmt<128, 16>(a, s) : launch_lds_fmt<128, 32>(a, s);
+  return a.bs == 16 ? launch_lds_fmt<64, 16>(a, s) : launch_lds_fmt<64, 32>(a, s);
 }
 
 }  // namespace pkv

@@ -38,26 +38,31 @@ using namespace mfma;
 // (chunk streams) per tile set. The R waves of one stream read the same K/V
 // chunk at the same time, so a KV head's context crosses HBM once for all of
 // the group's tiles.
-template <int D, int BS, bool FP8, int TPW, int R, int S>
+template <int D, int BS, int FMT, int TPW, int R, int S>
 __global__ __launch_bounds__(R * S * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void multi_query_partition_mfma(DecodeArgs a) {
+  constexpr bool FP8 = FMT == kFmtFp8;
+  constexpr bool FP4 = FMT == kFmtFp4;        // two E2M1 codes per byte, d = 128 only
+  constexpr bool QNT = FMT != kFmtBf16;       // per-head scales
   constexpr int NW = R * S;
   constexpr int GR = 16 * TPW * R;            // rows per workgroup
-  // tokens per chunk: FP8 rows are half as wide, so a single-tile wave takes
-  // twice the tokens per load; with two tiles the scores would not fit
-  constexpr int CT = FP8 && TPW == 1 ? 64 : 32;
+  // tokens per chunk: quantised rows are narrower, so a single-tile wave
+  // takes twice the tokens per load; with two tiles the scores would not fit
+  constexpr int CT = QNT && TPW == 1 ? 64 : 32;
   constexpr int NRG = CT / 16;                // 16-token row groups per chunk
   constexpr int NKS = CT / 32;                // 32-token PV k-steps per chunk
   constexpr int NKK = D / 32;                 // QK MFMA steps over d
-  constexpr int NKL = FP8 ? NKK / 2 : NKK;    // 16-byte K loads per row group
+  // 16-byte K loads per row group (FP4: one load holds a lane's 32 dims)
+  constexpr int NKL = FP4 ? 1 : FP8 ? NKK / 2 : NKK;
   constexpr int NJ = D / 16;                  // PV MFMAs per k-step
   constexpr int DPL = D / 16;                 // dims per lane per V row
   constexpr int BPC = CT / BS;                // blocks per chunk
-  constexpr int EB = FP8 ? 1 : 2;             // bytes per element
-  constexpr int VB = DPL * EB;
+  constexpr int RB = FP4 ? D / 2 : FP8 ? D : 2 * D;   // bytes per token row
+  constexpr int VB = FP4 ? DPL / 2 : FP8 ? DPL : 2 * DPL;   // bytes of a lane's V slice
   constexpr int NVS = 8 * NKS;
   using VT = typename Vec<VB>::T;
   constexpr int VW = (DPL * 2) / 4;
+  static_assert(!FP4 || D == 128, "FP4 is built for d = 128");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -125,6 +130,7 @@ void multi_query_partition_mfma(DecodeArgs a) {
   const int n_ch = t0 < t1 ? (blk1 - blk0 + BPC - 1) / BPC : 0;
 
   auto dimbase = [&](int kk) -> int {
+    if constexpr (FP4) return 32 * g4 + 8 * kk;
     return FP8 ? 64 * (kk >> 1) + 16 * g4 + 8 * (kk & 1) : 32 * kk + 8 * g4;
   };
   bf16x8_t qop[QLDS ? 1 : TPW][NKK];
@@ -176,9 +182,9 @@ void multi_query_partition_mfma(DecodeArgs a) {
     }
   };
   float qscale = a.scale * kLog2e;
-  if constexpr (FP8) qscale *= a.k_scale[g];
+  if constexpr (QNT) qscale *= a.k_scale[g];
 
-  const int64_t tile_bytes = static_cast<int64_t>(BS) * D * EB;
+  const int64_t tile_bytes = static_cast<int64_t>(BS) * RB;
   const int64_t head_off = static_cast<int64_t>(g) * tile_bytes;
   const int64_t block_stride = static_cast<int64_t>(a.n_kv) * tile_bytes;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
@@ -206,8 +212,10 @@ void multi_query_partition_mfma(DecodeArgs a) {
     if (p < 0 || p >= a.num_blocks) p = 0;
     return tile_rsrc(cache + p * block_stride + head_off, have ? static_cast<int>(tile_bytes) : 0);
   };
-  const uint32_t k_lane = static_cast<uint32_t>((c * D + (FP8 ? 16 : 8) * g4) * EB);
-  const uint32_t v_lane = static_cast<uint32_t>((4 * g4 * D + DPL * c) * EB);
+  // lane (c, g4): K row c at 16 bytes per lane group (bf16: dims 8 g4 + 32 kl;
+  // FP8: 16 g4 + 64 kl; FP4: dims 32 g4 ..), V row 4 g4 at dims DPL c
+  const uint32_t k_lane = static_cast<uint32_t>(c * RB + 16 * g4);
+  const uint32_t v_lane = static_cast<uint32_t>(4 * g4 * RB + VB * c);
   auto load_k = [&](KChunk& kc, int ci) {
     __amdgpu_buffer_rsrc_t r[BPC];
 #pragma unroll
@@ -217,8 +225,7 @@ void multi_query_partition_mfma(DecodeArgs a) {
     for (int rg = 0; rg < NRG; ++rg)
 #pragma unroll
       for (int kl = 0; kl < NKL; ++kl)
-        ld_stream(kc.k[rg][kl], r[16 * rg / BS], k_lane,
-                  (((16 * rg) % BS) * D + (FP8 ? 64 : 32) * kl) * EB);
+        ld_stream(kc.k[rg][kl], r[16 * rg / BS], k_lane, ((16 * rg) % BS) * RB + 64 * kl);
   };
   auto load_v = [&](VChunk& vc, int ci) {
     __amdgpu_buffer_rsrc_t r[BPC];
@@ -228,7 +235,7 @@ void multi_query_partition_mfma(DecodeArgs a) {
 #pragma unroll
     for (int s = 0; s < NVS; ++s) {
       const int X = 2 * (s >> 3) + ((s & 7) >> 2);
-      ld_stream(vc.v[s], r[16 * X / BS], v_lane, (((16 * X) % BS + (s & 3)) * D) * EB);
+      ld_stream(vc.v[s], r[16 * X / BS], v_lane, ((16 * X) % BS + (s & 3)) * RB);
     }
   };
 
@@ -263,8 +270,13 @@ void multi_query_partition_mfma(DecodeArgs a) {
 #pragma unroll
       for (int rg = 0; rg < NRG; ++rg) {
         bf16x8_t kop;
-        if constexpr (!FP8) {
+        if constexpr (FMT == kFmtBf16) {
           kop = __builtin_bit_cast(bf16x8_t, kc.k[rg][kk]);
+        } else if constexpr (FP4) {
+          // 8 codes at dims 32 g4 + 8 kk
+          const uint32_t w = word(kc.k[rg][0], kk);
+          kop = as_bf16x8(fp4x2_to_bf16x2<0>(w), fp4x2_to_bf16x2<1>(w),
+                          fp4x2_to_bf16x2<2>(w), fp4x2_to_bf16x2<3>(w));
         } else {
           const uint4 w = kc.k[rg][kk >> 1];
           const uint32_t w0 = (kk & 1) ? w.z : w.x;
@@ -351,9 +363,15 @@ void multi_query_partition_mfma(DecodeArgs a) {
       uint32_t vw[8][VW];
 #pragma unroll
       for (int si = 0; si < 8; ++si) {
-        if constexpr (!FP8) {
+        if constexpr (FMT == kFmtBf16) {
 #pragma unroll
           for (int w = 0; w < VW; ++w) vw[si][w] = word(vc.v[8 * ks + si], w);
+        } else if constexpr (FP4) {
+          const uint32_t x = word(vc.v[8 * ks + si], 0);
+          vw[si][0] = fp4x2_to_bf16x2<0>(x);
+          vw[si][1] = fp4x2_to_bf16x2<1>(x);
+          vw[si][2] = fp4x2_to_bf16x2<2>(x);
+          vw[si][3] = fp4x2_to_bf16x2<3>(x);
         } else {
 #pragma unroll
           for (int w = 0; w < VW / 2; ++w) {
@@ -423,7 +441,7 @@ void multi_query_partition_mfma(DecodeArgs a) {
   }
   __syncthreads();
 
-  const float vscale = FP8 ? a.v_scale[g] : 1.0f;
+  const float vscale = QNT ? a.v_scale[g] : 1.0f;
   for (int e = threadIdx.x; e < GR * D; e += blockDim.x) {
     const int r = e / D;                               // group row
     const int dd = e % D;
@@ -480,20 +498,29 @@ static Group pick_group(int tiles) {
   return tiles >= 2 ? Group{2, 1, 4} : Group{1, 1, 4};
 }
 
-template <int D, int BS, bool FP8, int TPW, int R, int S>
+template <int D, int BS, int FMT, int TPW, int R, int S>
 static hipError_t launch_g(const DecodeArgs& a, int tiles, hipStream_t s) {
   constexpr int tpg = TPW * R;
   const dim3 grid(a.n_kv * ((tiles + tpg - 1) / tpg), a.B, a.P_max);
-  multi_query_partition_mfma<D, BS, FP8, TPW, R, S><<<grid, R * S * 64, 0, s>>>(a);
+  multi_query_partition_mfma<D, BS, FMT, TPW, R, S><<<grid, R * S * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <int D, int BS, bool FP8>
+template <int D, int BS, int FMT>
 static hipError_t launch_mq(const DecodeArgs& a, int tiles, hipStream_t s) {
   const Group gr = pick_group(tiles);
-  if (gr.TPW == 2) return launch_g<D, BS, FP8, 2, 1, 4>(a, tiles, s);
-  if (gr.R == 2) return launch_g<D, BS, FP8, 1, 2, 4>(a, tiles, s);
-  return launch_g<D, BS, FP8, 1, 1, 4>(a, tiles, s);
+  if (gr.TPW == 2) return launch_g<D, BS, FMT, 2, 1, 4>(a, tiles, s);
+  if (gr.R == 2) return launch_g<D, BS, FMT, 1, 2, 4>(a, tiles, s);
+  return launch_g<D, BS, FMT, 1, 1, 4>(a, tiles, s);
+}
+
+template <int D, int BS>
+static hipError_t launch_mq_fmt(const DecodeArgs& a, int tiles, hipStream_t s) {
+  if (a.kv_dtype == PKV_FP8_E4M3) return launch_mq<D, BS, kFmtFp8>(a, tiles, s);
+  if constexpr (D == 128)
+    if (a.kv_dtype == PKV_FP4_E2M1) return launch_mq<D, BS, kFmtFp4>(a, tiles, s);
+  if (a.kv_dtype != PKV_BF16) return hipErrorInvalidValue;
+  return launch_mq<D, BS, kFmtBf16>(a, tiles, s);
 }
 
 // Many rows per KV head (128 or more) share each K/V chunk through LDS
@@ -508,20 +535,14 @@ static int forced_mq_kernel() {
 }
 
 hipError_t launch_multi_query_partition(const DecodeArgs& a, hipStream_t s) {
-  if (a.kv_dtype == PKV_FP4_E2M1) return hipErrorInvalidValue;   // not built for FP4
+  if (a.kv_dtype == PKV_FP4_E2M1 && a.d != 128) return hipErrorInvalidValue;
   const int G = a.n_q / a.n_kv;
   const int tiles = (a.Q * G + 15) / 16;
   const int forced = forced_mq_kernel();
   if (forced == 2 || (forced == 0 && tiles >= 8)) return launch_multi_query_lds(a, s);
-  const bool fp8 = a.kv_dtype == PKV_FP8_E4M3;
-  if (a.d == 128) {
-    if (a.bs == 16) return fp8 ? launch_mq<128, 16, true>(a, tiles, s)
-                               : launch_mq<128, 16, false>(a, tiles, s);
-    return fp8 ? launch_mq<128, 32, true>(a, tiles, s) : launch_mq<128, 32, false>(a, tiles, s);
-  }
-  if (a.bs == 16) return fp8 ? launch_mq<64, 16, true>(a, tiles, s)
-                             : launch_mq<64, 16, false>(a, tiles, s);
-  return fp8 ? launch_mq<64, 32, true>(a, tiles, s) : launch_mq<64, 32, false>(a, tiles, s);
+  if (a.d == 128)
+    return a.bs == 16 ? launch_mq_fmt<128, 16>(a, tiles, s) : launch_mq_fmt<128, 32>(a, tiles, s);
+  return a.bs == 16 ? launch_mq_fmt<64, 16>(a, tiles, s) : launch_mq_fmt<64, 32>(a, tiles, s);
 }
 
 }  // namespace pkv

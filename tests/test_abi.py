@@ -134,6 +134,32 @@ def test_other_entry_points_validate():
                                512, None) == _lib.PKV_ERR_UNSUPPORTED
 
 
+def test_fp4_validation_on_every_attention_entry_point():
+    # FP4 is built for d_head 128 only and, like FP8, needs both scale arrays
+    L = _lib.lib()
+    fake = ctypes.c_void_p(0x1000)
+    f64 = _desc(d=64, dtype=_lib.PKV_FP4_E2M1)
+    f128 = _desc(d=128, dtype=_lib.PKV_FP4_E2M1)
+
+    def mq(d, ks, B=2):
+        return L.pkv_paged_multi_query_attention(ctypes.byref(d), fake, _lib.PKV_FP32, fake, 4,
+                                                 fake, fake, fake, fake, 4, fake, B, 4, 64,
+                                                 0.1, ks, ks, 0, None, 0, None)
+
+    def cascade(d, ks, B=2):
+        return L.pkv_cascade_decode_attention(ctypes.byref(d), fake, _lib.PKV_FP32, fake, fake,
+                                              fake, fake, 32, fake, 4, fake, B, 4, 32, 0.1, ks,
+                                              ks, 0, 0, fake, 1 << 20, None)
+
+    assert _decode(f64, ks=fake, vs=fake) == _lib.PKV_ERR_UNSUPPORTED
+    assert _decode(f128) == _lib.PKV_ERR_INVALID_ARG                  # no scales
+    assert mq(f64, fake) == _lib.PKV_ERR_UNSUPPORTED
+    assert mq(f128, None) == _lib.PKV_ERR_INVALID_ARG
+    assert mq(f128, fake, B=0) == _lib.PKV_OK
+    assert cascade(f64, fake) == _lib.PKV_ERR_UNSUPPORTED
+    assert cascade(f128, None) == _lib.PKV_ERR_INVALID_ARG
+
+
 # ------------------------------------------------------------------ host block manager
 
 def test_block_manager_matches_the_model_on_random_operations():

@@ -5,7 +5,9 @@ Bars: kv_append, copies, gathers and swaps are bit-exact; attention max abs
 error <= 3e-2 (as FP8: the oracle dequantises the same codes with the same
 scales) and relative L2 <= 1e-4. With one cached token the output is exactly
 that token's dequantised V row, which pins the hardware conversion's nibble
-order on all 256 byte patterns.
+order on all 256 byte patterns. Decode, multi-token queries (both kernels:
+fewer and more than 128 rows per KV head) and shared-prefix attention run on
+FP4 caches.
 """
 
 import numpy as np
@@ -134,3 +136,67 @@ def test_fp4_byte_movers(pkv):
     torch.cuda.synchronize()
     expect = ref.swap_out(W.bits(kd), W.bits(vd), ids)
     assert np.array_equal(host.numpy().reshape(expect.shape), expect)
+
+
+def close(got, expect, what):
+    assert np.all(np.isfinite(got)), what
+    err = np.max(np.abs(got - expect)) if got.size else 0.0
+    rel = np.linalg.norm(got - expect) / max(np.linalg.norm(expect), 1e-30)
+    assert err <= 3e-2 and rel <= 1e-4, (what, err, rel)
+
+
+MQ_SHAPES = [
+    # lengths, query lengths, Q, n_q, n_kv, bs, partition
+    ([40, 97, 600], [3, 4, 5], 5, 64, 8, 32, 0),         # 40 rows: register kernel
+    ([40, 97, 600], [3, 4, 5], 5, 64, 8, 16, 64),
+    ([1, 2, 31, 32, 33], [1, 2, 9, 16, 33], 33, 8, 4, 16, 32),
+    ([300, 1025], [40, 200], 200, 16, 2, 32, 0),         # 1600 rows: LDS kernel
+    ([300, 1025], [40, 200], 200, 16, 2, 16, 256),
+    ([77, 640, 5], [77, 130, 5], 130, 8, 8, 16, 96),     # 130 rows, mid-chunk partitions
+]
+
+
+@pytest.mark.parametrize("case", MQ_SHAPES, ids=[str(i) for i in range(len(MQ_SHAPES))])
+def test_fp4_multi_query_shapes(pkv, case):
+    lens, qlens, Q, n_q, n_kv, bs, P = case
+    w = W.custom("fp4mq", lens, n_q, n_kv, 128, bs, W.FP4, seed=140 + MQ_SHAPES.index(case))
+    kc, vc, ks, vs = W.make_cache(w)
+    q = W.make_multi_query(w, Q)
+    ql = np.asarray(qlens, dtype=np.int32)
+    out = pkv.paged_multi_query_attention(
+        q.to(DEV), torch.from_numpy(ql).to(DEV), kc.to(DEV), vc.to(DEV),
+        torch.from_numpy(w.block_tables).to(DEV), torch.from_numpy(w.context_lens).to(DEV),
+        w.scale, int(w.context_lens.max()), k_scale=ks.to(DEV), v_scale=vs.to(DEV),
+        partition_size=P)
+    torch.cuda.synchronize()
+    expect = ref.multi_query_attention(W.bits(q), W.bits(kc), W.bits(vc), w.block_tables,
+                                       w.context_lens, ql, w.scale, ref.FP4, ks.numpy(),
+                                       vs.numpy())
+    got = out.cpu().double().numpy()
+    for b, n in enumerate(ql):
+        assert not np.any(got[b, n:]), f"rows past query length {n} of seq {b} not zero"
+    close(got, expect, str(case))
+
+
+@pytest.mark.parametrize("rows", [16, 512])
+def test_fp4_cascade(pkv, rows):
+    # the prefix pass on the register kernel (2 sequences x G 8) or on the LDS
+    # kernel (64 x 8 rows)
+    B = rows // 8
+    suffix = [(37 * i) % 300 + (i % 3 == 0) * 700 for i in range(B)]
+    plen, n_q, n_kv, bs = 1024, 64, 8, 16
+    w = W.custom("fp4cas", [plen] + suffix, n_q, n_kv, 128, bs, W.FP4, seed=150 + rows)
+    kc, vc, ks, vs = W.make_cache(w)
+    pt = w.block_tables[0, :plen // bs].copy()
+    tables = np.ascontiguousarray(w.block_tables[1:])
+    slen = np.array(suffix, dtype=np.int32)
+    g = torch.Generator().manual_seed(151 + rows)
+    q = torch.randn((B, n_q, 128), generator=g).to(torch.bfloat16)
+    out = pkv.cascade_decode_attention(
+        q.to(DEV), kc.to(DEV), vc.to(DEV), torch.from_numpy(pt).to(DEV), plen,
+        torch.from_numpy(tables).to(DEV), torch.from_numpy(slen).to(DEV), w.scale,
+        int(slen.max()), k_scale=ks.to(DEV), v_scale=vs.to(DEV))
+    torch.cuda.synchronize()
+    expect = ref.cascade_decode_attention(W.bits(q), W.bits(kc), W.bits(vc), pt, plen, tables,
+                                          slen, w.scale, ref.FP4, ks.numpy(), vs.numpy())
+    close(out.cpu().double().numpy(), expect, f"cascade rows={rows}")
