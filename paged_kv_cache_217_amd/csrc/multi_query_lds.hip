@@ -321,21 +321,19 @@ void multi_query_lds_mfma(DecodeArgs a) {
           }
         }
       } else {
-        uint32_t vw[8][VW];
+        uint32_t vw[8][FP4 ? 1 : VW];
+        Fp4Pair vp[4];                   // FP4: slots 2u, 2u + 1 interleaved
+        VT vraw[8];
 #pragma unroll
         for (int si = 0; si < 8; ++si) {
           const int tv = v_tok(8 * ks + si);
-          const VT v = *reinterpret_cast<const VT*>(vl_ + v_lane + (tv - 4 * g4) * LR);
+          vraw[si] = *reinterpret_cast<const VT*>(vl_ + v_lane + (tv - 4 * g4) * LR);
           if constexpr (FP4) {
-            const uint32_t x = word(v, 0);
-            vw[si][0] = fp4x2_to_bf16x2<0>(x);
-            vw[si][1] = fp4x2_to_bf16x2<1>(x);
-            vw[si][2] = fp4x2_to_bf16x2<2>(x);
-            vw[si][3] = fp4x2_to_bf16x2<3>(x);
+            if (si % 2 == 1) vp[si / 2] = fp4_interleave(word(vraw[si - 1], 0), word(vraw[si], 0));
           } else {
 #pragma unroll
             for (int w = 0; w < VW / 2; ++w) {
-              const uint32_t x = word(v, w);
+              const uint32_t x = word(vraw[si], w);
               vw[si][2 * w] = fp8x2_to_bf16x2<false>(x);
               vw[si][2 * w + 1] = fp8x2_to_bf16x2<true>(x);
             }
@@ -343,12 +341,17 @@ void multi_query_lds_mfma(DecodeArgs a) {
         }
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj) {
-          const int w = jj >> 1;
-          const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
           uint32_t t4[4];
+          if constexpr (FP4) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            t4[u] = __builtin_amdgcn_perm(vw[2 * u + 1][w], vw[2 * u][w], sel);
+            for (int u = 0; u < 4; ++u) t4[u] = fp4_pair_dim(vp[u], jj);
+          } else {
+            const int w = jj >> 1;
+            const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              t4[u] = __builtin_amdgcn_perm(vw[2 * u + 1][w], vw[2 * u][w], sel);
+          }
           const bf16x8_t vop = as_bf16x8(t4[0], t4[1], t4[2], t4[3]);
 #pragma unroll
           for (int t = 0; t < TPW; ++t) {

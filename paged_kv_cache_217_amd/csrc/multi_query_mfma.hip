@@ -360,18 +360,16 @@ void multi_query_partition_mfma(DecodeArgs a) {
         pop_hi[t] = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
         pop_lo[t] = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
       }
-      uint32_t vw[8][VW];
+      uint32_t vw[8][FP4 ? 1 : VW];
+      Fp4Pair vp[4];                     // FP4: slots 2t, 2t + 1 interleaved
 #pragma unroll
       for (int si = 0; si < 8; ++si) {
         if constexpr (FMT == kFmtBf16) {
 #pragma unroll
           for (int w = 0; w < VW; ++w) vw[si][w] = word(vc.v[8 * ks + si], w);
         } else if constexpr (FP4) {
-          const uint32_t x = word(vc.v[8 * ks + si], 0);
-          vw[si][0] = fp4x2_to_bf16x2<0>(x);
-          vw[si][1] = fp4x2_to_bf16x2<1>(x);
-          vw[si][2] = fp4x2_to_bf16x2<2>(x);
-          vw[si][3] = fp4x2_to_bf16x2<3>(x);
+          if (si % 2 == 1)
+            vp[si / 2] = fp4_interleave(word(vc.v[8 * ks + si - 1], 0), word(vc.v[8 * ks + si], 0));
         } else {
 #pragma unroll
           for (int w = 0; w < VW / 2; ++w) {
@@ -383,12 +381,17 @@ void multi_query_partition_mfma(DecodeArgs a) {
       }
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) {
-        const int w = jj >> 1;
-        const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
         uint32_t t4[4];
+        if constexpr (FP4) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          t4[u] = __builtin_amdgcn_perm(vw[2 * u + 1][w], vw[2 * u][w], sel);
+          for (int u = 0; u < 4; ++u) t4[u] = fp4_pair_dim(vp[u], jj);
+        } else {
+          const int w = jj >> 1;
+          const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            t4[u] = __builtin_amdgcn_perm(vw[2 * u + 1][w], vw[2 * u][w], sel);
+        }
         const bf16x8_t vop = as_bf16x8(t4[0], t4[1], t4[2], t4[3]);
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
