@@ -154,59 +154,15 @@ void decode_partition_mfma(DecodeArgs a) {
   };
 
   // Q^T operand: lane (c, g4) holds q[h0 + c][dimbase(kk) .. +8] for each kk
-  bf16x8_t qop[FP4 ? 1 : NKK];
-  // FP4: the FP4 K codes go to the matrix cores as they are, against Q split
-  // into two E4M3 terms, Q = 2^e (q1 + q2 / 16), with 2^e a per-head power of
-  // two that puts max |Q| in [128, 256). Each term keeps 4 significant bits
-  // and a bf16 value has 8, so the sum is exact for every element within
-  // 2^13 of the head's largest (smaller ones are off by at most 2^-21 of it).
-  v8i_t q1 = {}, q2 = {};
-  int sb1 = 127, sb2 = 127;              // E8M0 block scales of the two terms
+  bf16x8_t qop[NKK];
   {
     const bool live = c < nh;
     const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * a.n_q + h0 + (live ? c : 0)) * D;
-    if constexpr (FP4) {
-      // B lane (c, g4): dims 16 g4 .. (bytes 0..15) and 64 + 16 g4 .. (16..31)
-      float x[32];
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          uint4 w = *reinterpret_cast<const uint4*>(qrow + 64 * half + 16 * g4 + 8 * u);
-          if (!live) w = make_uint4(0, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            bf16x2_to_f32(word(w, e), x[16 * half + 8 * u + 2 * e], x[16 * half + 8 * u + 2 * e + 1]);
-        }
-      float mx = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(x[i]));
-      mx = max_xor32(max_xor16(mx));
-      // 2^e with max |Q| / 2^e in [128, 256): e = floor(log2 max) - 7
-      const int e = mx > 0.0f ? min(max(__builtin_amdgcn_frexp_expf(mx) - 8, -120), 120) : 0;
-      const float inv = __builtin_ldexpf(1.0f, -e);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float y[4], r[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) y[u] = x[4 * i + u] * inv;
-        const uint32_t w1 = pack_fp8x4(y[0], y[1], y[2], y[3]);
-        r[0] = (y[0] - __builtin_amdgcn_cvt_f32_fp8(w1, 0)) * 16.0f;
-        r[1] = (y[1] - __builtin_amdgcn_cvt_f32_fp8(w1, 1)) * 16.0f;
-        r[2] = (y[2] - __builtin_amdgcn_cvt_f32_fp8(w1, 2)) * 16.0f;
-        r[3] = (y[3] - __builtin_amdgcn_cvt_f32_fp8(w1, 3)) * 16.0f;
-        q1[i] = static_cast<int>(w1);
-        q2[i] = static_cast<int>(pack_fp8x4(r[0], r[1], r[2], r[3]));
-      }
-      sb1 = 127 + e;
-      sb2 = 127 + e - 4;
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        uint4 w = *reinterpret_cast<const uint4*>(qrow + dimbase(kk));
-        if (!live) w = make_uint4(0, 0, 0, 0);
-        qop[kk] = __builtin_bit_cast(bf16x8_t, w);
-      }
+    for (int kk = 0; kk < NKK; ++kk) {
+      uint4 w = *reinterpret_cast<const uint4*>(qrow + dimbase(kk));
+      if (!live) w = make_uint4(0, 0, 0, 0);
+      qop[kk] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
   float qscale = a.scale * kLog2e;
@@ -287,16 +243,8 @@ void decode_partition_mfma(DecodeArgs a) {
     for (int r = 0; r < RGS; ++r) {
       const int rg = sub * RGS + r;
       f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (FP4) {
-        // token 16 rg + c, all 128 dims: 32 codes per lane group
-        const uint4 k4 = ch.k[rg][0];
-        const v8i_t ka = {static_cast<int>(k4.x), static_cast<int>(k4.y),
-                          static_cast<int>(k4.z), static_cast<int>(k4.w), 0, 0, 0, 0};
-        sc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, q1, sc, 4, 0, 0, 127, 0, sb1);
-        sc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, q2, sc, 4, 0, 0, 127, 0, sb2);
-      }
 #pragma unroll
-      for (int kk = 0; kk < (FP4 ? 0 : NKK); ++kk) {
+      for (int kk = 0; kk < NKK; ++kk) {
         bf16x8_t kop;
         if constexpr (FMT == kFmtBf16) {
           kop = __builtin_bit_cast(bf16x8_t, ch.k[rg][kk]);
@@ -306,6 +254,10 @@ void decode_partition_mfma(DecodeArgs a) {
           const uint32_t w1 = (kk & 1) ? w.w : w.y;
           kop = as_bf16x8(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
                           fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
+        } else {
+          const uint32_t w = word(ch.k[rg][0], kk);    // 8 codes: dims 32 g4 + 8 kk ..
+          kop = as_bf16x8(fp4x2_to_bf16x2<0>(w), fp4x2_to_bf16x2<1>(w),
+                          fp4x2_to_bf16x2<2>(w), fp4x2_to_bf16x2<3>(w));
         }
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sc, 0, 0, 0);
       }

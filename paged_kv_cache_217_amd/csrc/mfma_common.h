@@ -136,22 +136,6 @@ __device__ __forceinline__ uint32_t fp4_pair_dim(const Fp4Pair& p, int j) {
   }
 }
 
-// FP4 x FP8 matrix-core product (v_mfma_scale_f32_16x16x128_f8f6f4 with an
-// E2M1 A operand and an E4M3 B operand). Lane (r, g) of A holds the 32 codes
-// of row r at k = 32 g .. 32 g + 31 (two per byte, low nibble first; only its
-// first 4 registers are read). Measured on gfx950: lane (n, g) of B must then
-// hold, in bytes 0..15, k = 16 g .. 16 g + 15 and, in bytes 16..31,
-// k = 64 + 16 g .. 64 + 16 g + 15 of column n; the E8M0 block scale of B lane
-// (n, g) multiplies the products of k = 32 g .. 32 g + 31. The result layout
-// is that of every 16 x 16 MFMA: lane (n, g) holds rows 4 g .. 4 g + 3.
-typedef int v8i_t __attribute__((ext_vector_type(8)));
-
-// four floats as four E4M3 codes (nearest), value i in byte i
-__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
-  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true));
-}
-
 // Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group,
 // lane a supplies the address of 4 consecutive 16-bit elements M[a][0..3];
 // lane j receives M[4 i + j / 4][j % 4] for i = 0..3 (layout measured on

@@ -113,6 +113,34 @@ def test_fp4_decode_shapes(pkv, case):
     assert err <= 3e-2 and rel <= 1e-4, (err, rel)
 
 
+def test_fp4_decode_query_dynamic_range(pkv):
+    # the FP4 K.Q^T path splits each head's query into two E4M3 terms under a
+    # per-head power of two; elements far below the head's largest, zeros and
+    # negative zeros must still give the oracle's result
+    w = W.custom("fp4q", [700, 33, 2048], 64, 8, 128, 32, W.FP4, seed=135)
+    kc, vc, ks, vs = W.make_cache(w)
+    g = torch.Generator().manual_seed(136)
+    q = torch.randn((w.B, w.n_q, 128), generator=g)
+    q = q * torch.exp2(torch.randint(-24, 4, (w.B, w.n_q, 128), generator=g).float())
+    q[:, :, 5] = 900.0                          # one large element per head
+    q[:, 3, :] = 0.0                            # an all-zero head
+    q[:, 4, 7] = -0.0
+    q = q.to(torch.bfloat16)
+    out = pkv.paged_decode_attention(q.to(DEV), kc.to(DEV), vc.to(DEV),
+                                     torch.from_numpy(w.block_tables).to(DEV),
+                                     torch.from_numpy(w.context_lens).to(DEV), w.scale,
+                                     int(w.context_lens.max()), k_scale=ks.to(DEV),
+                                     v_scale=vs.to(DEV))
+    torch.cuda.synchronize()
+    expect = ref.decode_attention(W.bits(q), W.bits(kc), W.bits(vc), w.block_tables,
+                                  w.context_lens, w.scale, ref.FP4, ks.numpy(), vs.numpy())
+    got = out.cpu().double().numpy()
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - expect))
+    rel = np.linalg.norm(got - expect) / max(np.linalg.norm(expect), 1e-30)
+    assert err <= 3e-2 and rel <= 1e-4, (err, rel)
+
+
 def test_fp4_byte_movers(pkv):
     w = W.custom("fp4mv", [300, 45], 16, 8, 128, 16, W.FP4, seed=130)
     kc, vc, _, _ = W.make_cache(w)
