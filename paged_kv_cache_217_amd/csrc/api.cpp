@@ -34,12 +34,19 @@ pkv_status check_desc(const pkv_cache_desc* d) {
 // (the matrix-core kernel's head tile is 16 wide).
 int head_tile(int G) { return G <= 16 ? G : 16; }
 
-int32_t pick_partition_units(int64_t units, int32_t max_ctx);
+int32_t pick_partition_units(int64_t units, int32_t max_ctx, int64_t row_bytes);
+
+// bytes of K and V of one token of one KV head
+int64_t kv_row_bytes(const pkv_cache_desc* d) {
+  const int64_t elems = 2 * static_cast<int64_t>(d->d_head);
+  return d->kv_dtype == PKV_BF16 ? 2 * elems : d->kv_dtype == PKV_FP4_E2M1 ? elems / 2 : elems;
+}
 
 int32_t pick_partition(const pkv_cache_desc* d, int32_t B, int32_t n_q, int32_t max_ctx) {
   const int G = n_q / d->n_kv;
   return pick_partition_units(
-      static_cast<int64_t>(B) * d->n_kv * ((G + head_tile(G) - 1) / head_tile(G)), max_ctx);
+      static_cast<int64_t>(B) * d->n_kv * ((G + head_tile(G) - 1) / head_tile(G)), max_ctx,
+      kv_row_bytes(d));
 }
 
 // Workgroups of a multi-query launch per partition: the LDS kernel takes 128
@@ -55,21 +62,27 @@ int32_t pick_partition_mq(const pkv_cache_desc* d, int32_t B, int32_t Q, int32_t
   const int64_t per_head = tiles >= 8 ? cdiv(rows, 128) : (tiles >= 2 ? cdiv(tiles, 2) : 1);
   const int64_t units = static_cast<int64_t>(B) * d->n_kv * per_head;
   if (units >= 512) return static_cast<int32_t>(std::max<int64_t>(32, cdiv(max_ctx, 32) * 32));
-  return pick_partition_units(units, max_ctx);
+  return pick_partition_units(units, max_ctx, kv_row_bytes(d));
 }
 
-int32_t pick_partition_units(int64_t units, int32_t max_ctx) {
+int32_t pick_partition_units(int64_t units, int32_t max_ctx, int64_t row_bytes) {
   // The partition kernel holds two 4-wave workgroups per CU (its register
   // budget allows two waves per SIMD), so 512 workgroups fill the 256 CUs
   // once. A batch whose (sequence, KV head) pairs alone fill that round and
   // whose longest sequence is at most 8192 tokens runs in a single pass with
-  // no reduce. Otherwise partitions are at most 4096 tokens (a workgroup then
-  // streams <= 2 MiB of bf16 K+V, which bounds the tail of a launch over
-  // sequences of very different lengths) and shrink by halves while the grid
-  // would not fill one round.
+  // no reduce. Otherwise a partition holds at most 4 MiB of K+V (8192 tokens
+  // of bf16 at d_head 128, 16384 of FP8, 32768 of FP4; at least 4096), which
+  // bounds the tail of a launch over sequences of very different lengths,
+  // and halves while the grid would not fill one round. Longer partitions
+  // carry less per-workgroup overhead: measured on MI355X, 16 x 131072 bf16
+  // tokens take 1.33 ms at 4096 and 1.29 ms at 8192, and 256 FP8 sequences
+  // of lognormal length 327 us at 4096 and 312 us at 16384 (but 346 us in a
+  // single pass, where the longest sequence is the tail).
   constexpr int64_t kOneRound = 256 * 2;
+  constexpr int64_t kMaxPartitionBytes = int64_t{4} << 20;
   if (max_ctx <= 8192 && units >= kOneRound) return 8192;
   int64_t P = 4096;
+  while (2 * P * row_bytes <= kMaxPartitionBytes) P *= 2;
   while (P > 256 && units * cdiv(max_ctx, P) < kOneRound) P /= 2;
   while (cdiv(max_ctx, P) > kMaxReducePartitions) P *= 2;
   return static_cast<int32_t>(P);
