@@ -298,7 +298,8 @@ pkv_status pkv_gather_kv(const pkv_cache_desc* desc, void* k_out, void* v_out,
  * K/V once for all B sequences: the sharers' (sequence, head) rows attend to
  * the prefix together on the matrix cores (split over prefix_partition-token
  * partitions), each sequence's own suffix runs through the decode partition
- * kernel, and one log-sum-exp merge combines both.
+ * kernel (longest partitions first when there are several per sequence), and
+ * one log-sum-exp merge combines both.
  *
  * prefix_table: int32 [prefix_len / bs] on the device; prefix_len must be a
  * multiple of the block size (0: no prefix, plain decode). block_tables:
