@@ -16,10 +16,15 @@ Sources (web pages; cited by tag and section throughout this package):
 
 Modules:
   fp8_e4m3     -- OCP FP8 E4M3FN decode / round-to-nearest-even saturating encode
+  fp4_e2m1     -- FP4 E2M1 decode / round-to-nearest-even saturating encode,
+                  two codes per byte
   bf16         -- exact widening of bfloat16 bit patterns
   paged        -- gather through block tables, dense decode attention, split-K
-                  partials and their merge, slot mapping, kv_append, CoW copy
-  block_manager-- host block allocator model (ref counts, copy-on-write)
+                  partials and their merge, slot mapping, kv_append, CoW copy,
+                  multi-token-query attention, shared-prefix (cascade)
+                  attention, swap-out / swap-in of blocks
+  block_manager-- host block allocator model (ref counts, copy-on-write, swap,
+                  radix prefix cache with LRU eviction)
   sizing       -- KV-cache byte closed form and the capacity model
 
 Pin status (what each function is checked against in tests/, CPU only):
@@ -29,4 +34,4 @@ Pin status (what each function is checked against in tests/, CPU only):
   "parity unpinned".
 """
 
-from . import bf16, fp8_e4m3, paged, block_manager, sizing  # noqa: F401
+from . import bf16, fp8_e4m3, fp4_e2m1, paged, block_manager, sizing  # noqa: F401
