@@ -42,8 +42,16 @@ int64_t kv_row_bytes(const pkv_cache_desc* d) {
   return d->kv_dtype == PKV_BF16 ? 2 * elems : d->kv_dtype == PKV_FP4_E2M1 ? elems / 2 : elems;
 }
 
+int32_t pick_partition_mq(const pkv_cache_desc* d, int32_t B, int32_t Q, int32_t n_q,
+                          int32_t max_ctx);
+
+// More than 16 query heads per KV head: decode runs as a one-token multi-query
+// launch (see decode_on_multi_query), and its partition rule applies.
+bool decode_on_multi_query(int G) { return G > 16; }
+
 int32_t pick_partition(const pkv_cache_desc* d, int32_t B, int32_t n_q, int32_t max_ctx) {
   const int G = n_q / d->n_kv;
+  if (decode_on_multi_query(G)) return pick_partition_mq(d, B, 1, n_q, max_ctx);
   return pick_partition_units(
       static_cast<int64_t>(B) * d->n_kv * ((G + head_tile(G) - 1) / head_tile(G)), max_ctx,
       kv_row_bytes(d));
@@ -267,9 +275,24 @@ pkv_status pkv_paged_decode_attention(const pkv_cache_desc* desc, void* out, int
   if (st != PKV_OK) return st;
   a.out = out;
   a.out_dtype = out_dtype;
+  // With more than 16 query heads per KV head the partition kernel would run
+  // one workgroup per 16-head tile, each reading the KV head's K/V again. The
+  // multi-query kernel with one query per sequence that sees its whole
+  // context computes the same attention and applies each K/V chunk to two
+  // tiles per wave (a schedule, which only the partition kernel follows,
+  // keeps the partition kernel).
+  const bool on_mq = decode_on_multi_query(n_q / desc->n_kv) && a.schedule == nullptr;
+  if (on_mq) {
+    a.Q = 1;
+    a.non_causal = true;
+  }
+  auto launch = [&]() {
+    return on_mq ? pkv::launch_multi_query_partition(a, as_stream(stream))
+                 : pkv::launch_decode_partition(a, as_stream(stream));
+  };
   if (a.P_max == 1) {
     a.write_partials = false;
-    return from_hip(pkv::launch_decode_partition(a, as_stream(stream)));
+    return from_hip(launch());
   }
   const size_t need = workspace_bytes(B, n_q, a.d, a.P_max);
   if (!workspace || workspace_bytes_ < need) return PKV_ERR_WORKSPACE_TOO_SMALL;
@@ -279,8 +302,8 @@ pkv_status pkv_paged_decode_attention(const pkv_cache_desc* desc, void* out, int
   a.ws_l = w.l;
   a.ws_o = w.o;
   a.write_partials = true;
-  a.wave_partitions = a.schedule == nullptr && use_wave_partitions(a.partition);
-  hipError_t e = pkv::launch_decode_partition(a, as_stream(stream));
+  a.wave_partitions = !on_mq && a.schedule == nullptr && use_wave_partitions(a.partition);
+  hipError_t e = launch();
   if (e != hipSuccess) return PKV_ERR_HIP;
   return from_hip(pkv::launch_splitk_reduce(out, out_dtype, w.m, w.l, w.o, context_lens, B, n_q,
                                             a.d, a.P_max, a.partition, as_stream(stream)));
