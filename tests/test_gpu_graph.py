@@ -1,0 +1,128 @@
+"""Decode steps captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
+
+The library allocates, clears and synchronises nothing itself, so a whole
+step (slot mapping, kv_append, longest-first schedule, partition kernel,
+split-K reduce; and a multi-token-query launch) can be captured once and
+replayed. Each replay, with eager work and synchronisation between replays,
+must reproduce the eager result bit for bit; the eager result is checked
+against the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import paged as ref
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_217_amd as m
+    return m
+
+
+@pytest.mark.parametrize("dt,bs,n_q,n_kv", [(W.BF16, 16, 64, 8), (W.FP8, 32, 16, 2),
+                                            (W.BF16, 16, 64, 1)])
+def test_decode_step_replays(pkv, dt, bs, n_q, n_kv):
+    w = W.custom("graph", [300, 1000, 77, 2048, 5], n_q, n_kv, 128, bs, dt, seed=170)
+    kc, vc, ks, vs = W.make_cache(w)
+    q = W.make_query(w).to(DEV)
+    k_new, v_new = [x.to(DEV) for x in W.make_new_tokens(w)]
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    ksd = None if ks is None else ks.to(DEV)
+    vsd = None if vs is None else vs.to(DEV)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    cl = torch.from_numpy(w.context_lens).to(DEV)
+    pos = torch.from_numpy((w.context_lens - 1).astype(np.int32)).to(DEV)
+    mx, P = int(w.context_lens.max()), 256
+    out = torch.empty((w.B, n_q, 128), dtype=torch.float32, device=DEV)
+    ws, _ = pkv.make_workspace(kd, w.B, n_q, mx, P)
+    sched = pkv.decode_schedule(cl, mx, P)              # buffer reused by every call below
+
+    def step(use_schedule):
+        slots = pkv.slot_mapping(bt, pos, w.bs)
+        pkv.kv_append(kd, vd, k_new, v_new, slots, ksd, vsd)
+        s = pkv.decode_schedule(cl, mx, P, out=sched) if use_schedule else None
+        pkv.paged_decode_attention(q, kd, vd, bt, cl, w.scale, mx, k_scale=ksd, v_scale=vsd,
+                                   partition_size=P, out=out, workspace=ws, schedule=s)
+
+    for use_schedule in (False, True):
+        step(use_schedule)                              # eager (appending again is idempotent)
+        torch.cuda.synchronize()
+        eager = out.clone()
+        if not use_schedule:
+            ksn = None if ks is None else ks.numpy()
+            vsn = None if vs is None else vs.numpy()
+            ke, ve = ref.kv_append(W.bits(kc), W.bits(vc), W.bits(k_new.cpu()),
+                                   W.bits(v_new.cpu()),
+                                   ref.slot_mapping(w.block_tables, pos.cpu().numpy(), w.bs),
+                                   dt, ksn, vsn)
+            expect = ref.decode_attention(W.bits(q.cpu()), ke, ve, w.block_tables,
+                                          w.context_lens, w.scale, dt, ksn, vsn)
+            err = np.max(np.abs(eager.cpu().double().numpy() - expect))
+            assert err <= (1e-2 if dt == W.BF16 else 3e-2), err
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):                   # warm-up off the default stream
+            step(use_schedule)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(use_schedule)
+        for r in range(3):
+            out.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), f"replay {r} (schedule={use_schedule})"
+            # eager work between replays
+            pkv.paged_decode_attention(q, kd, vd, bt, cl, w.scale, mx, k_scale=ksd, v_scale=vsd)
+            torch.cuda.synchronize()
+
+
+def test_multi_query_replays(pkv):
+    w = W.custom("graphmq", [700, 33, 1500], 64, 8, 128, 16, W.BF16, seed=171)
+    kc, vc, _, _ = W.make_cache(w)
+    Q = 24
+    q = W.make_multi_query(w, Q).to(DEV)
+    ql = torch.tensor([24, 7, 24], dtype=torch.int32, device=DEV)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    cl = torch.from_numpy(w.context_lens).to(DEV)
+    mx, P = int(w.context_lens.max()), 512
+    out = torch.empty((w.B, Q, 64, 128), dtype=torch.float32, device=DEV)
+    nbytes = pkv.lib().pkv_multi_query_workspace_bytes(w.B, Q, 64, 128, mx, P)
+    ws = torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=DEV)
+
+    def step():
+        pkv.paged_multi_query_attention(q, ql, kd, vd, bt, cl, w.scale, mx, partition_size=P,
+                                        out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    expect = ref.multi_query_attention(W.bits(q.cpu()), W.bits(kc), W.bits(vc), w.block_tables,
+                                       w.context_lens, ql.cpu().numpy(), w.scale)
+    assert np.max(np.abs(eager.cpu().double().numpy() - expect)) <= 1e-2
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r}"
