@@ -125,23 +125,32 @@ void multi_query_lds_mfma(DecodeArgs a) {
   };
   bf16x8_t qop[TPW][NKK];
   int pos[TPW];
+  // Scores stay unscaled (q . k) until the exponent, where 2^(s qscale - m)
+  // is one fused multiply-add. That needs qscale > 0, so that the row maximum
+  // of the unscaled scores is that of the scaled ones: a negative product is
+  // made positive by negating Q (exact in bf16), a zero one by zeroing Q
+  // (every score is then 0, as 0 . q . k would be).
+  float qscale = a.scale * kLog2e;
+  if constexpr (QNT) qscale *= a.k_scale[g];
+  const uint32_t qflip = qscale < 0.0f ? 0x80008000u : 0u;
+  const bool qzero = qscale == 0.0f;
+  qscale = qzero ? 1.0f : fabsf(qscale);
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int row = wrow0 + 16 * t + c;
     const int qi = row / G;
-    const bool live_row = row < rows && qi < ql;
+    const bool live_row = row < rows && qi < ql && !qzero;
     pos[t] = qpos(qi);
     const int64_t qrow =
         live_row ? (static_cast<int64_t>(b) * a.Q + qi) * a.n_q + g * G + row % G : 0;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       uint4 w = *reinterpret_cast<const uint4*>(a.q + qrow * D + dimbase(kk));
+      w = make_uint4(w.x ^ qflip, w.y ^ qflip, w.z ^ qflip, w.w ^ qflip);
       if (!live_row) w = make_uint4(0, 0, 0, 0);
       qop[t][kk] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
-  float qscale = a.scale * kLog2e;
-  if constexpr (QNT) qscale *= a.k_scale[g];
 
   __shared__ __align__(16) uint8_t sk[4][LB];
   __shared__ __align__(16) uint8_t sv[4][LB];
@@ -251,7 +260,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[t][4 * rg + i] = sc[rg][t][i] * qscale;
+        for (int i = 0; i < 4; ++i) s[t][4 * rg + i] = sc[rg][t][i];
     if (tok0 + CT > min(p_lo + 1, t1)) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
@@ -269,7 +278,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
       float mx = s[t][0];
 #pragma unroll
       for (int i = 1; i < 4 * NRG; ++i) mx = fmaxf(mx, s[t][i]);
-      mx = max_xor32(max_xor16(mx));
+      mx = max_xor32(max_xor16(mx)) * qscale;          // base-2 units
       m_true[t] = fmaxf(m_true[t], mx);
       const bool need = mx > m_ref[t] + kLazyRescale;
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -289,7 +298,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
         float p[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          p[i] = fast_exp2(s[t][8 * ks + i] - m_use[t]);
+          p[i] = fast_exp2(fmaf(s[t][8 * ks + i], qscale, -m_use[t]));
           l[t] += p[i];
         }
         uint32_t ph[4], pl[4];

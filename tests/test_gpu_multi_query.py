@@ -143,3 +143,15 @@ def test_chunked_prefill_shape(pkv):
     Q = 512
     out, expect, ql = run_mq(pkv, w, Q, [512, 1, 1])
     check(out, expect, ql, W.BF16, "chunked prefill")
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 2.5])
+def test_negative_zero_and_large_scales(pkv, scale):
+    # the scale is applied inside the exponent's fused multiply-add; a
+    # negative one flips the softmax, zero makes it uniform over what each
+    # row sees, a large one makes it nearly hard (both kernels: 24 and 1024
+    # rows per KV head)
+    for Q, n_q in ((6, 32), (128, 64)):
+        w = W.custom("mqscale", [300, 77, 1029], n_q, 8, 128, 16, W.BF16, seed=90, scale=scale)
+        out, expect, ql = run_mq(pkv, w, Q, [Q, min(Q, 77), Q // 2])
+        check(out, expect, ql, W.BF16, f"scale {scale} Q {Q}")
