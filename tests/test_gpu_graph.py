@@ -2,11 +2,13 @@
 
 The library allocates, clears and synchronises nothing itself, so a whole
 step (slot mapping, kv_append, longest-first schedule, partition kernel,
-split-K reduce; and a multi-token-query launch) can be captured once and
-replayed. Each replay, with eager work and synchronisation between replays,
+split-K reduce), a multi-token-query launch and a shared-prefix (cascade)
+call can be captured once and replayed. Each replay, with eager work and synchronisation between replays,
 must reproduce the eager result bit for bit; the eager result is checked
 against the oracle.
 """
+
+import ctypes
 
 import numpy as np
 import pytest
@@ -124,5 +126,51 @@ def test_multi_query_replays(pkv):
         out.zero_()
         torch.cuda.synchronize()
         g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r}"
+
+
+def test_cascade_replays(pkv):
+    # prefix pass, suffix schedule and partitions, two-source merge
+    plen, suffix, n_q, n_kv, bs = 2048, [5, 700, 0, 2500, 33, 1200], 64, 8, 16
+    w = W.custom("graphcas", [plen] + suffix, n_q, n_kv, 128, bs, W.BF16, seed=172)
+    kc, vc, _, _ = W.make_cache(w)
+    pt = torch.from_numpy(w.block_tables[0, :plen // bs].copy()).to(DEV)
+    tables = torch.from_numpy(np.ascontiguousarray(w.block_tables[1:])).to(DEV)
+    slen = torch.tensor(suffix, dtype=torch.int32, device=DEV)
+    B = len(suffix)
+    g = torch.Generator().manual_seed(173)
+    q = torch.randn((B, n_q, 128), generator=g).to(torch.bfloat16).to(DEV)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    out = torch.empty((B, n_q, 128), dtype=torch.float32, device=DEV)
+    desc = pkv.cache_desc(kd)
+    nbytes = pkv.lib().pkv_cascade_workspace_bytes(ctypes.byref(desc), B, n_q, plen, 0,
+                                                    max(suffix), 0)
+    ws = torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=DEV)
+
+    def step():
+        pkv.cascade_decode_attention(q, kd, vd, pt, plen, tables, slen, w.scale, max(suffix),
+                                     out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    expect = ref.cascade_decode_attention(W.bits(q.cpu()), W.bits(kc), W.bits(vc),
+                                          pt.cpu().numpy(), plen, tables.cpu().numpy(),
+                                          np.array(suffix, dtype=np.int32), w.scale)
+    assert np.max(np.abs(eager.cpu().double().numpy() - expect)) <= 1e-2
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step()
+    for r in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {r}"
