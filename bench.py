@@ -279,7 +279,9 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": part_bytes,
-                     "traffic": traffic},
+                     "traffic": traffic["total"] if traffic else None,
+                     "traffic_read": traffic["read"] if traffic else None,
+                     "traffic_written": traffic["written"] if traffic else None},
     }
 
     # ---------------------------------------------------------------- oracle on the CPU
@@ -557,7 +559,9 @@ def bench_multi_query(args, w, pkv, W, np, torch, dev):
         c = json.load(open(MQ_COUNTERS)).get(w.name, {})
         if c.get("kernel_hash") == kernel_hash(MQ_KERNEL_SOURCES) and c.get("partition") == P:
             traffic = c.get("traffic_bytes_per_launch")
-    roof["traffic"] = traffic
+    roof["traffic"] = traffic["total"] if traffic else None
+    roof["traffic_read"] = traffic["read"] if traffic else None
+    roof["traffic_written"] = traffic["written"] if traffic else None
     new_tokens = int(ql.sum())
     result = {
         "metric": "multi-query paged attention: query tokens/s, KV GB/s",
