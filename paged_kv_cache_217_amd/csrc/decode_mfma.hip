@@ -184,45 +184,36 @@ void decode_partition_mfma(DecodeArgs a) {
     VT v[NVS];
   };
 
+  // Chunk ci through per-block buffer resources (size 0 when the block is
+  // absent: its loads give zeros), one constant lane offset each for K and V
+  // and a constant offset per row: no per-load address arithmetic.
+  const uint32_t k_lane = static_cast<uint32_t>(c * RB + 16 * g4);   // K row c, lane group g4
+  const uint32_t v_lane = static_cast<uint32_t>(4 * g4 * RB + VB * c);  // V row 4 g4, dims DPL c
   auto load = [&](Chunk& ch, int ci) {
-    const uint8_t* kb[BPC];
-    const uint8_t* vb[BPC];
-    bool have[BPC];
+    __amdgpu_buffer_rsrc_t rk[BPC], rv[BPC];
 #pragma unroll
     for (int i = 0; i < BPC; ++i) {
       const int blk = blk0 + ci * BPC + i;
-      have[i] = blk < blk1;
-      int p = have[i] ? bt[blk] : 0;
+      const bool have = blk < blk1;
+      int p = __builtin_amdgcn_readfirstlane(have ? bt[blk] : 0);
       if (p < 0 || p >= a.num_blocks) p = 0;
-      kb[i] = a.k_cache + p * block_stride + head_off;
-      vb[i] = a.v_cache + p * block_stride + head_off;
+      const int bytes = have ? static_cast<int>(tile_bytes) : 0;
+      rk[i] = tile_rsrc(a.k_cache + p * block_stride + head_off, bytes);
+      rv[i] = tile_rsrc(a.v_cache + p * block_stride + head_off, bytes);
     }
+    // K: token 16 rg + c is row (16 rg) % BS + c of block 16 rg / BS; load kl
+    // covers bytes 64 kl + 16 g4 of the row (bf16: dims 32 kl + 8 g4; FP8:
+    // 64 kl + 16 g4; FP4: the lane group's 32 dims)
 #pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) {
-      const int t = 16 * rg + c;                       // K: token c of row group rg
-      const int bi = t / BS;
+    for (int rg = 0; rg < NRG; ++rg)
 #pragma unroll
-      for (int kl = 0; kl < NKL; ++kl) {
-        if (!have[bi]) {
-          ch.k[rg][kl] = make_uint4(0, 0, 0, 0);
-        } else if constexpr (FP4) {
-          ld_stream(ch.k[rg][kl], kb[bi] + (t % BS) * RB + 16 * g4);
-        } else {
-          const int dim = FP8 ? 64 * kl + 16 * g4 : 32 * kl + 8 * g4;
-          ld_stream(ch.k[rg][kl], kb[bi] + ((t % BS) * D + dim) * EB);
-        }
-      }
-    }
+      for (int kl = 0; kl < NKL; ++kl)
+        ld_stream(ch.k[rg][kl], rk[16 * rg / BS], k_lane, ((16 * rg) % BS) * RB + 64 * kl);
+    // V: slot s is token 16 X + 4 g4 + (s & 3), X = 2 (s / 8) + (s % 8) / 4
 #pragma unroll
     for (int s = 0; s < NVS; ++s) {
-      const int t = v_tok(s);
-      const int bi = t / BS;
-      if (!have[bi])
-        ch.v[s] = VT{};
-      else if constexpr (FP4)
-        ld_stream(ch.v[s], vb[bi] + (t % BS) * RB + VB * c);
-      else
-        ld_stream(ch.v[s], vb[bi] + ((t % BS) * D + DPL * c) * EB);
+      const int X = 2 * (s >> 3) + ((s & 7) >> 2);
+      ld_stream(ch.v[s], rv[16 * X / BS], v_lane, ((16 * X) % BS + (s & 3)) * RB);
     }
   };
 
