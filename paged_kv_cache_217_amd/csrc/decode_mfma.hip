@@ -24,7 +24,8 @@
 //           8 token rows of DPL dims (whole rows per load instruction across
 //           16 lanes) and transposing 16-bit pairs with v_perm_b32.
 //   Every lane therefore owns one head's softmax state (its 4 k-group lanes
-//   share a max through two cross-lane exchanges) and that head's output
+//   share a max through two row-swap moves, v_permlane16/32_swap) and that
+//   head's output
 //   accumulator for D/4 dims.
 // P is fed to the matrix core as bf16 hi + lo parts (two MFMAs), which keeps
 // the weights to ~16 significant bits; the row sums use the fp32 weights.
@@ -59,13 +60,18 @@ namespace pkv {
 using namespace mfma;
 
 // Two waves per SIMD: the register budget is 256 per lane (arch + acc).
-template <int D, int BS, int FMT, int NW, bool SPLIT_P>
+// DEPTH chunk buffers rotate through the main loop: DEPTH - 1 chunks are in
+// flight while one is computed. With DEPTH = 4 a chunk is half as long, so the
+// four buffers take the registers of two full chunks.
+template <int D, int BS, int FMT, int NW, bool SPLIT_P, int DEPTH>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_partition_mfma(DecodeArgs a) {
   constexpr bool FP8 = FMT == kFmtFp8;
   constexpr bool FP4 = FMT == kFmtFp4;        // two E2M1 codes per byte, d = 128 only
   constexpr bool QNT = FMT != kFmtBf16;       // per-head scales
-  constexpr int CT = FP4 ? 128 : FP8 ? 64 : 32;   // tokens per chunk (16 KiB of K+V)
+  static_assert(DEPTH == 2 || (DEPTH == 4 && FMT != kFmtBf16), "pipeline depth");
+  // tokens per chunk: 16 KiB of K+V with two buffers, 8 KiB with four
+  constexpr int CT = (FP4 ? 128 : FP8 ? 64 : 32) / (DEPTH / 2);
   constexpr int NRG = CT / 16;                // 16-token row groups per chunk
   constexpr int NKS = CT / 32;                // 32-token PV k-steps per chunk
   constexpr int NKK = D / 32;                 // QK MFMA steps over d
@@ -269,8 +275,7 @@ void decode_partition_mfma(DecodeArgs a) {
     float mx = s[0];
 #pragma unroll
     for (int i = 1; i < 4 * RGS; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     m_true = fmaxf(m_true, mx);
     const bool need = mx > m_ref + kLazyRescale;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -346,25 +351,42 @@ void decode_partition_mfma(DecodeArgs a) {
     }
   };
 
-  // ---- main loop, next chunk's loads in flight while the current one is computed
+  // ---- main loop, later chunks' loads in flight while the current one is computed
   {
     const int first = wave_parts ? 0 : wave;
     const int stride = wave_parts ? 1 : NW;
-    Chunk A, B;
-    int ci = first;
-    if (ci < n_ch) load(A, ci);
-    for (; ci < n_ch; ci += 2 * stride) {
-      if (ci + stride < n_ch) load(B, ci + stride);
-      compute(A, ci);
-      if (ci + stride >= n_ch) break;
-      if (ci + 2 * stride < n_ch) load(A, ci + 2 * stride);
-      compute(B, ci + stride);
+    if constexpr (DEPTH == 2) {
+      Chunk A, B;
+      int ci = first;
+      if (ci < n_ch) load(A, ci);
+      for (; ci < n_ch; ci += 2 * stride) {
+        if (ci + stride < n_ch) load(B, ci + stride);
+        compute(A, ci);
+        if (ci + stride >= n_ch) break;
+        if (ci + 2 * stride < n_ch) load(A, ci + 2 * stride);
+        compute(B, ci + stride);
+      }
+    } else if (first < n_ch) {
+      // A chunk past the partition has only absent blocks (size-0 resources),
+      // so its loads return zeros without reading memory and every load can be
+      // issued unconditionally: the outstanding-load count stays static.
+      Chunk buf[DEPTH];
+#pragma unroll
+      for (int u = 0; u < DEPTH - 1; ++u) load(buf[u], first + u * stride);
+      for (int ci = first; ci < n_ch; ci += DEPTH * stride) {
+#pragma unroll
+        for (int u = 0; u < DEPTH; ++u) {
+          const int cu = ci + u * stride;
+          if (cu >= n_ch) break;
+          load(buf[(u + DEPTH - 1) % DEPTH], cu + (DEPTH - 1) * stride);
+          compute(buf[u], cu);
+        }
+      }
     }
   }
 
   // ---- wave totals for head c, rebased on the true max
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = sum_xor32(sum_xor16(l));
   const float f = m_true == -INFINITY ? 0.0f : fast_exp2(m_ref - m_true);
   l *= f;
   if (g4 == 0) {
@@ -434,9 +456,28 @@ void decode_partition_mfma(DecodeArgs a) {
 
 constexpr int kMfmaWaves = 4;
 
+// Pipeline depth: FP4 runs four half-size chunks (its per-byte conversion
+// and softmax work keeps a wave on a chunk long enough that one chunk in
+// flight does not cover the load latency: 97.6 -> 94.0 us on the 70B FP4
+// layer); bf16 and FP8 run two full chunks (FP8 measured no faster with four).
+// PKV_DECODE_DEPTH=2 or 4 forces the depth of the quantised formats, for
+// measurement.
+static int pipeline_depth(int fmt) {
+  static const int forced = [] {
+    const char* e = getenv("PKV_DECODE_DEPTH");
+    return e ? (e[0] == '4' ? 4 : 2) : 0;
+  }();
+  if (fmt == kFmtBf16) return 2;
+  return forced ? forced : (fmt == kFmtFp4 ? 4 : 2);
+}
+
 template <int D, int BS, int FMT>
 static hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  decode_partition_mfma<D, BS, FMT, kMfmaWaves, true><<<grid, kMfmaWaves * 64, 0, s>>>(a);
+  if (pipeline_depth(FMT) == 4)
+    decode_partition_mfma<D, BS, FMT, kMfmaWaves, true, FMT == kFmtBf16 ? 2 : 4>
+        <<<grid, kMfmaWaves * 64, 0, s>>>(a);
+  else
+    decode_partition_mfma<D, BS, FMT, kMfmaWaves, true, 2><<<grid, kMfmaWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
