@@ -182,6 +182,10 @@ SHAPES = [
     ([40, 97, 600], 64, 8, 128, 32, W.FP8, 64),
     ([1, 2, 31, 32, 33], 8, 4, 64, 16, W.FP8, 32),
     ([513, 66], 16, 16, 128, 16, W.FP8, 512),
+    # lengths ending inside either 16-token row group of a 32-token step, with
+    # NaN codes in the rest of the last block
+    ([5, 17, 20, 33, 47, 63], 16, 2, 128, 16, W.FP8, 0),
+    ([5, 17, 20, 33, 47, 63], 4, 4, 64, 32, W.FP8, 32),
 ]
 
 
