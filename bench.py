@@ -14,7 +14,8 @@ entry is for the dominant kernel (the decode partition kernel): its
 algorithmic bytes per launch over its average duration, measured with HIP
 events recorded on the stream it runs on, against MI355X's 8 TB/s HBM peak.
 cpu_baseline times the float64 oracle on a bounded sample of the same
-workload on this host's cores.
+workload in one process with one BLAS thread; cpu_baseline_procs times it in
+several processes (up to 16) over whole sequences of the same layer.
 """
 
 import argparse
@@ -69,6 +70,9 @@ def parse():
                     help="1: longest-first work list built once per step (pkv_decode_schedule)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the oracle CPU baseline (0 disables it)")
+    ap.add_argument("--cpu-procs", type=int, default=min(16, os.cpu_count() or 1),
+                    help="also time the oracle in this many processes (one BLAS thread each) "
+                         "over whole sequences, reported as cpu_baseline_procs (1 disables it)")
     ap.add_argument("--swap", type=int, default=0, metavar="N",
                     help="measure swapping N sequences of the 70B layer to host memory and back")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -104,8 +108,28 @@ def main():
     import numpy as np
     import torch
 
-    import paged_kv_cache_217_amd as pkv
     import workloads as W
+
+    w = W.ALL[args.workload]()
+    decode = not (args.copy_calibration or args.swap or w.Q > 1 or w.notes.get("prefix_len"))
+    # The processes of the multi-process oracle baseline are started here,
+    # before anything touches the GPU (libpkv is not loaded yet, and
+    # torch.cuda is first used below): they are new interpreters, and a
+    # process that has initialised the GPU must not start programs that way.
+    pool = None
+    if decode and args.cpu_seconds > 0 and args.cpu_procs > 1:
+        import multiprocessing as mp
+        pool = mp.get_context("spawn").Pool(args.cpu_procs)
+    try:
+        run(args, w, pool, np, torch, W)
+    finally:
+        if pool is not None:
+            pool.terminate()
+            pool.join()
+
+
+def run(args, w, pool, np, torch, W):
+    import paged_kv_cache_217_amd as pkv
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -117,8 +141,6 @@ def main():
     if args.swap:
         bench_swap(args, pkv, W, np, torch, dev)
         return
-
-    w = W.ALL[args.workload]()
     if w.Q > 1:
         bench_multi_query(args, w, pkv, W, np, torch, dev)
         return
@@ -287,6 +309,12 @@ def main():
     # ---------------------------------------------------------------- oracle on the CPU
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, caches[0], q[0], args.cpu_seconds)
+        if pool is not None:
+            try:
+                result["cpu_baseline_procs"] = cpu_baseline_procs(
+                    w, caches[0], q[0], args.cpu_seconds, args.cpu_procs, pool)
+            except Exception as e:           # the GPU figures stand without it
+                log(f"[bench] multi-process oracle baseline failed: {e!r}")
     print(json.dumps(result), flush=True)
 
 
@@ -596,25 +624,96 @@ def cpu_baseline(w, layer_cache, q0, budget):
     kb, vb, qb = W.bits(kc), W.bits(vc), W.bits(q0)
     ksn = None if ks is None else ks.cpu().numpy()
     vsn = None if vs is None else vs.cpu().numpy()
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info] + [1])
     done_tokens = 0
     n = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget and n < 64 * w.B:
-        b = n % w.B                      # whole sequences of layer 0, cycling if time remains
-        ref.decode_attention(qb[b:b + 1], kb, vb, w.block_tables[b:b + 1],
-                             w.context_lens[b:b + 1], w.scale, w.kv_dtype, ksn, vsn)
-        done_tokens += int(w.context_lens[b])
-        n += 1
-    dt = time.perf_counter() - t0
+    # one BLAS thread: the oracle's per-head products are matrix-vector
+    # products, which a larger BLAS pool measured no faster on
+    with threadpoolctl.threadpool_limits(1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget and n < 64 * w.B:
+            b = n % w.B                  # whole sequences of layer 0, cycling if time remains
+            ref.decode_attention(qb[b:b + 1], kb, vb, w.block_tables[b:b + 1],
+                                 w.context_lens[b:b + 1], w.scale, w.kv_dtype, ksn, vsn)
+            done_tokens += int(w.context_lens[b])
+            n += 1
+        dt = time.perf_counter() - t0
     kv = done_tokens * w.n_kv * w.d * w.p * 2
     log(f"[bench] oracle: {n} sequences in {dt:.1f}s")
-    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "sample": f"{n} whole sequences of layer 0 (sequence index mod {w.B}; {done_tokens} "
-                      f"tokens, all {w.n_q} query heads), numpy float64, 1 process, {dt:.1f} s; "
-                      f"host has {os.cpu_count()} logical CPUs"}
+                      f"tokens, all {w.n_q} query heads), numpy float64, 1 process, 1 BLAS "
+                      f"thread, {dt:.1f} s; host has {os.cpu_count()} logical CPUs"}
+
+
+def _oracle_worker(job):
+    """One process of the multi-process oracle baseline: whole sequences of the
+    shared layer, one BLAS thread, until the budget is spent."""
+    import numpy as np
+    import threadpoolctl
+
+    from oracle import paged as ref
+
+    d, seqs, budget = job
+    with threadpoolctl.threadpool_limits(1):
+        kb = np.load(d["k"], mmap_mode="r")
+        vb = np.load(d["v"], mmap_mode="r")
+        qb = np.load(d["q"])
+        bt = np.load(d["bt"])
+        cl = np.load(d["cl"])
+        ks = np.load(d["ks"]) if d.get("ks") else None
+        vs = np.load(d["vs"]) if d.get("vs") else None
+        tokens = 0
+        t0 = time.perf_counter()
+        for b in seqs:
+            if time.perf_counter() - t0 >= budget:
+                break
+            ref.decode_attention(qb[b:b + 1], kb, vb, bt[b:b + 1], cl[b:b + 1], d["scale"],
+                                 d["kv_dtype"], ks, vs)
+            tokens += int(cl[b])
+        return tokens, time.perf_counter() - t0
+
+
+def cpu_baseline_procs(w, layer_cache, q0, budget, procs, pool):
+    """The same oracle in `procs` processes (`pool`, started before the GPU was
+    touched), each with one BLAS thread, over whole sequences of layer 0
+    (sequence i goes to process i mod procs). The layer is shared through
+    read-only memory-mapped files."""
+    import shutil
+    import tempfile
+
+    import numpy as np
+
+    import workloads as W
+
+    kc, vc, ks, vs = layer_cache
+    root = tempfile.mkdtemp(prefix="pkv_oracle_", dir="/dev/shm" if os.path.isdir("/dev/shm")
+                            else None)
+    try:
+        d = {"scale": w.scale, "kv_dtype": w.kv_dtype}
+        arrays = {"k": W.bits(kc), "v": W.bits(vc), "q": W.bits(q0), "bt": w.block_tables,
+                  "cl": w.context_lens}
+        if ks is not None:
+            arrays["ks"] = ks.cpu().numpy()
+            arrays["vs"] = vs.cpu().numpy()
+        for name, arr in arrays.items():
+            d[name] = os.path.join(root, name + ".npy")
+            np.save(d[name], arr)
+        del arrays
+        seqs = [list(range(i, 64 * w.B, procs)) for i in range(procs)]
+        jobs = [(d, [b % w.B for b in s], budget) for s in seqs]
+        log(f"[bench] oracle in {procs} processes")
+        res = pool.map(_oracle_worker, jobs, chunksize=1)
+    finally:
+        shutil.rmtree(root, ignore_errors=True)
+    tokens = sum(r[0] for r in res)
+    dt = max(r[1] for r in res)
+    kv = tokens * w.n_kv * w.d * w.p * 2
+    log(f"[bench] oracle, {procs} processes: {tokens} tokens in {dt:.1f}s")
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": procs, "kind": "oracle",
+            "sample": f"whole sequences of layer 0 split over {procs} processes (one BLAS "
+                      f"thread each; {tokens} tokens, all {w.n_q} query heads), numpy float64, "
+                      f"{dt:.1f} s; host has {os.cpu_count()} logical CPUs"}
 
 
 if __name__ == "__main__":
