@@ -297,6 +297,9 @@ def run(args, w, pool, np, torch, W):
         "kernels_ms": {"kv_append": round(avg(t_append), 5),
                        "decode_partition": round(ms_part, 5),
                        "splitk_reduce": round(avg(t_reduce), 5) if split else None},
+        # spread of the per-launch event timings of the partition kernel
+        "decode_partition_ms_p10_p50_p90": [round(float(np.percentile(t_part, p)), 5)
+                                            for p in (10, 50, 90)],
         "roofline": {"bound": "hbm", "kernel": "decode_partition",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
