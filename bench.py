@@ -150,7 +150,6 @@ def run(args, w, pool, np, torch, W):
     layers = args.layers or w.layers
     B, n_q, n_kv, d, bs = w.B, w.n_q, w.n_kv, w.d, w.bs
     max_ctx = int(w.context_lens.max())
-    fp8 = w.kv_dtype in (W.FP8, W.FP4)          # quantised: per-head scales
     log(f"[bench] workload {w.name}: B={B} n_q={n_q} n_kv={n_kv} d={d} bs={bs} "
         f"{w.kv_dtype} layers={layers} tokens={w.total_tokens} pool={w.num_blocks} blocks/layer")
 
@@ -254,15 +253,9 @@ def run(args, w, pool, np, torch, W):
     ms_part = avg(t_part)
 
     # ---------------------------------------------------------------- accounting
-    p = w.p
     tokens = w.total_tokens
-    kv_bytes_layer = int(tokens * n_kv * d * p * 2)
-    nP = [max(1, -(-int(c) // P)) if c > 0 else 0 for c in w.context_lens]
-    part_bytes = (kv_bytes_layer                                  # K and V
-                  + B * n_q * d * 2                               # q
-                  + sum(-(-int(c) // bs) for c in w.context_lens) * 4   # block-table entries
-                  + (sum(nP) * n_q * (d + 2) * 4 if split else B * n_q * d * 4)  # partials/out
-                  + (2 * n_kv * 4 if fp8 else 0))                 # FP8 / FP4 scales
+    kv_bytes_layer = kv_bytes(w)
+    part_bytes = partition_bytes(w, P)
     achieved = part_bytes / (ms_part * 1e-3) / 1e9
     kv_gbs = kv_bytes_layer * layers / (ms_step * 1e-3) / 1e9
     tok_s = B / (ms_step * 1e-3)
@@ -319,6 +312,29 @@ def run(args, w, pool, np, torch, W):
             except Exception as e:           # the GPU figures stand without it
                 log(f"[bench] multi-process oracle baseline failed: {e!r}")
     print(json.dumps(result), flush=True)
+
+
+def kv_bytes(w):
+    """K and V bytes one layer's attention reads: every attended token's K and
+    V rows of every KV head (2 * n_kv * d_head * bytes per element)."""
+    return int(w.total_tokens * w.n_kv * w.d * w.p * 2)
+
+
+def partition_bytes(w, P):
+    """Algorithmic bytes of one launch of the decode partition kernel over the
+    workload's batch with partition size P: the K/V it reads, the queries, the
+    block-table entries of the attended blocks, the FP8/FP4 scales, and what it
+    writes (the output in fp32 in a single pass, else (m, l, o) per
+    partition)."""
+    ctx = [int(c) for c in w.context_lens]
+    max_ctx = max(ctx) if ctx else 0
+    split = -(-max_ctx // P) > 1
+    n_part = sum(-(-c // P) for c in ctx if c > 0)
+    return (kv_bytes(w)
+            + w.B * w.n_q * w.d * 2                                    # q, bf16
+            + sum(-(-c // w.bs) for c in ctx) * 4                      # block-table entries
+            + (n_part * w.n_q * (w.d + 2) * 4 if split else w.B * w.n_q * w.d * 4)
+            + (2 * w.n_kv * 4 if w.kv_dtype != "bf16" else 0))         # per-head scales
 
 
 def bench_swap(args, pkv, W, np, torch, dev):

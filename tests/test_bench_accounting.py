@@ -1,0 +1,54 @@
+"""The algorithmic byte counts behind bench.py's roofline, pinned on the CPU.
+
+The KV term must reproduce the pages' closed form for KV bytes per token,
+2 * L * n_kv * d_head * p ([SMTS] "Quantifying the KV-Cache Memory Wall";
+[MTKV] "The Anatomy of the KV-Cache Memory Wall"; [LLMI] "5. Mathematics:
+Sizing the KV Cache"): 327,680 B per token at L = 80, n_kv = 8, d = 128,
+2-byte elements. The partition kernel's launch total must be that term plus
+exactly the queries, table entries, scales and outputs it moves.
+"""
+
+import bench
+import workloads as W
+from oracle import sizing
+
+
+def test_70b_step_reads_the_closed_form_kv_bytes():
+    w = W.gqa_70b()
+    per_token = sizing.kv_bytes_per_token(80, 8, 128, 2)
+    assert per_token == 327_680
+    # one decode step attends 64 x 8192 tokens in each of the 80 layers
+    assert bench.kv_bytes(w) * w.layers == 64 * 8192 * per_token == 171_798_691_840
+
+
+def test_70b_layer_launch_bytes():
+    w = W.gqa_70b()
+    kv = 64 * 8192 * 8 * 128 * 2 * 2            # K and V of one layer
+    q = 64 * 64 * 128 * 2                        # bf16 queries
+    table = 64 * (8192 // 16) * 4                # one int32 entry per attended block
+    out = 64 * 64 * 128 * 4                      # fp32 output, single pass
+    assert bench.partition_bytes(w, 8192) == kv + q + table + out == 2_150_760_448
+
+
+def test_split_launch_writes_partials_instead_of_the_output():
+    w = W.gqa_70b()
+    single = bench.partition_bytes(w, 8192)
+    split = bench.partition_bytes(w, 4096)      # 2 partitions of every sequence
+    out = 64 * 64 * 128 * 4
+    partials = 64 * 2 * 64 * (128 + 2) * 4      # (m, l, o) per partition and head
+    assert split - single == partials - out
+
+
+def test_quantised_launch_counts_bytes_per_element_and_scales():
+    w = W.gqa_70b_fp8()
+    ctx = [int(c) for c in w.context_lens]
+    kv = sum(ctx) * 8 * 128 * 1 * 2
+    assert bench.kv_bytes(w) == kv
+    P = 16384
+    n_part = sum(-(-c // P) for c in ctx)
+    expect = (kv + w.B * 64 * 128 * 2 + sum(-(-c // 32) for c in ctx) * 4
+              + n_part * 64 * 130 * 4 + 2 * 8 * 4)
+    assert bench.partition_bytes(w, P) == expect
+    # FP4: half a byte per element
+    w4 = W.gqa_70b_fp4(layers=1)
+    assert bench.kv_bytes(w4) * 4 == bench.kv_bytes(W.gqa_70b(layers=1))
