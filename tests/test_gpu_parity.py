@@ -452,6 +452,27 @@ def test_full_table_row_and_last_pool_block(pkv):
         check_close(out, expect, W.FP8, f"edge P={P} row={row}")
 
 
+@pytest.mark.parametrize("n_q, dt", [(8, W.BF16), (64, W.FP8)])
+def test_million_token_context(pkv, n_q, dt):
+    """One sequence of 2^20 tokens (the 1M-token contexts [MTKV] "The Anatomy of
+    the KV-Cache Memory Wall" sizes) beside a short one, one KV head: split-K at
+    the library's partition and the reduce over its partials; with 64 query
+    heads the decode runs on the multi-query kernel."""
+    ctx = 1 << 20
+    w = W.custom("million", [ctx, 77], n_q, 1, 128, 32, dt, seed=54)
+    kc, vc, ks, vs = W.make_cache(w)
+    q = W.make_query(w)
+    kd, vd, qd, bt, cl, ksd, vsd = to_dev(w, kc, vc, q, ks, vs)
+    out = pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, ctx, k_scale=ksd,
+                                     v_scale=vsd)
+    torch.cuda.synchronize()
+    expect = ref.decode_attention(W.bits(q), W.bits(kc), W.bits(vc), w.block_tables,
+                                  w.context_lens, w.scale, dt,
+                                  None if ks is None else ks.numpy(),
+                                  None if vs is None else vs.numpy())
+    check_close(out, expect, dt, f"1M tokens n_q={n_q} {dt}")
+
+
 def test_many_short_sequences_scheduled(pkv):
     """4096 sequences of 1..64 tokens through the schedule, split-K and single pass."""
     rng = np.random.default_rng(52)
