@@ -337,6 +337,25 @@ def partition_bytes(w, P):
             + (2 * w.n_kv * 4 if w.kv_dtype != "bf16" else 0))         # per-head scales
 
 
+def multi_query_work(w, P_max):
+    """Algorithmic work of one multi-token-query attention call (the kernel and,
+    with P_max > 1, the reduce): every (sequence, KV head) reads its context's K
+    and V once, plus the bf16 queries, the fp32 outputs, the table entries of
+    the attended blocks and, when split, the partials written and read back.
+    Query i of a sequence with c tokens and q new ones sees c - q + i + 1
+    tokens, and each visible (query row, token) costs 4 d flops (2 d for the
+    score, 2 d for the weighted value). Returns (flops, bytes)."""
+    ctx = [int(c) for c in w.context_lens]
+    ql = [int(x) for x in w.query_lens]
+    visible = sum(c * q - q * (q - 1) // 2 for c, q in zip(ctx, ql))
+    flops = 4 * w.d * w.n_q * visible
+    nbytes = (kv_bytes(w) + w.B * w.Q * w.n_q * w.d * (2 + 4)
+              + sum(-(-c // w.bs) for c in ctx) * 4)
+    if P_max > 1:
+        nbytes += 2 * w.B * w.Q * w.n_q * P_max * (w.d + 2) * 4
+    return flops, nbytes
+
+
 def bench_swap(args, pkv, W, np, torch, dev):
     """Swap args.swap sequences of one 70B-GQA layer pool (8192 tokens each,
     512 blocks of 8 heads x 16 tokens x 128 dims) to pinned host memory and
@@ -574,16 +593,8 @@ def bench_multi_query(args, w, pkv, W, np, torch, dev):
     avg = lambda x: sum(x) / len(x)
     ms_att = avg(t_att)
 
-    # algorithmic work of one attention call: every (sequence, KV head) reads its
-    # context's K and V once; each live query row costs 4 d flops per visible token
-    kv_bytes_layer = w.total_tokens * n_kv * d * w.p * 2
-    visible = sum(int(w.context_lens[b]) * int(ql[b]) - int(ql[b]) * (int(ql[b]) - 1) // 2
-                  for b in range(B))
-    flops = 4.0 * d * n_q * visible
-    att_bytes = (kv_bytes_layer + B * Q * n_q * d * (2 + 4)
-                 + sum(-(-int(c) // bs) for c in w.context_lens) * 4)
-    if P_max > 1:
-        att_bytes += 2 * B * Q * n_q * P_max * (d + 2) * 4
+    kv_bytes_layer = kv_bytes(w)
+    flops, att_bytes = multi_query_work(w, P_max)
     intensity = flops / att_bytes
     # 128 or more (query, head) rows per KV head run on the LDS-shared kernel
     kname = "multi_query_lds_mfma" if Q * (n_q // n_kv) >= 128 else "multi_query_partition_mfma"

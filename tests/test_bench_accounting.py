@@ -52,3 +52,24 @@ def test_quantised_launch_counts_bytes_per_element_and_scales():
     # FP4: half a byte per element
     w4 = W.gqa_70b_fp4(layers=1)
     assert bench.kv_bytes(w4) * 4 == bench.kv_bytes(W.gqa_70b(layers=1))
+
+
+def test_prompt_chunk_flops_count_every_visible_pair_once():
+    w = W.chunked_prefill_70b()
+    # 512 new tokens at the end of each of the 4096/16384/32768/65536-token
+    # contexts: query i sees c - 512 + i + 1 tokens
+    visible = sum(sum(c - 512 + i + 1 for i in range(512)) for c in (4096, 16384, 32768, 65536))
+    flops, _ = bench.multi_query_work(w, 1)
+    assert flops == 4 * 128 * 64 * visible == 1_975_718_510_592
+
+
+def test_verification_bytes_read_the_context_once():
+    w = W.spec_verify_70b()
+    _, single = bench.multi_query_work(w, 1)
+    kv = 64 * 8192 * 8 * 128 * 2 * 2
+    qo = 64 * 4 * 64 * 128 * (2 + 4)              # bf16 queries in, fp32 outputs out
+    assert single == kv + qo + 64 * 512 * 4 == 2_160_197_632
+    _, split = bench.multi_query_work(w, 2)
+    assert split - single == 2 * 64 * 4 * 64 * 2 * 130 * 4
+    flops, _ = bench.multi_query_work(w, 1)
+    assert flops == 4 * 128 * 64 * 64 * (4 * 8192 - 6)
