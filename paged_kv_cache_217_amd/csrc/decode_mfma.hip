@@ -103,7 +103,10 @@ void decode_partition_mfma(DecodeArgs a) {
   // dispatched first and the short tail of the launch is made of first
   // partitions
   // With a schedule, x = item * (KV heads x tiles) + head slot, and the item
-  // names (sequence, partition) in longest-first order.
+  // names (sequence, partition) in longest-first order. Workgroups go to the
+  // 8 XCDs round-robin, so with 8 KV heads head g runs on XCD g and the 8
+  // XCDs read the 8 head tiles of the same blocks at about the same time;
+  // placing a sequence's heads on one XCD instead measured slower.
   const int G = a.n_q / a.n_kv;
   const int tiles = (G + 15) / 16;
   int hx, b, pz;
