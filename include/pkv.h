@@ -76,6 +76,45 @@ const char* pkv_status_string(pkv_status s);
 const char* pkv_version(void);
 
 /* ---------------------------------------------------------------------------
+ * Debug mode: checks of the caller errors the interface leaves unspecified
+ * because their data lives in device memory. Normal mode never reads device
+ * data back and stays memory-safe for any such values, but the results are
+ * unspecified.
+ *
+ * pkv_set_debug(1) turns the mode on for the process (0 turns it off). It
+ * allocates one int32 flag on the current device, and on each further device
+ * at its first debug call. Returns PKV_ERR_HIP if that allocation fails.
+ *
+ * While it is on, each entry point that takes device data and a stream:
+ *   1. validates its host arguments as always;
+ *   2. synchronises `stream` and reports a flag raised by an earlier call's
+ *      checks on this device as PKV_ERR_INVALID_ARG, clearing the flag and
+ *      enqueuing nothing;
+ *   3. enqueues checks of its own device inputs ahead of its work. The work
+ *      still runs, with its normal-mode behaviour.
+ * The checks:
+ *   - decode, partials, multi-token, shared-prefix and gather calls: every
+ *     live table entry (the first cdiv(len, block_size) of a row) names a
+ *     block in [0, num_blocks); every length lies in [0, the max length
+ *     passed]; every query count lies in [0, min(Q, length)];
+ *   - kv_append: every non-negative slot lies in the pool
+ *     (< num_blocks * block_size) and appears once;
+ *   - copy_blocks: ids in the pool, distinct destinations, no destination
+ *     that is also a source.
+ * Swap ids outside the pool are not errors (see the swap calls).
+ *
+ * pkv_debug_check(stream) does step 2 alone: PKV_OK, PKV_ERR_INVALID_ARG (a
+ * raised flag, now cleared) or PKV_ERR_HIP. With the mode off it returns
+ * PKV_OK at once.
+ *
+ * The mode synchronises at every call. It is for development, not for timing
+ * or HIP graph capture. The switch is process-wide and not thread-safe: set it
+ * before other threads call the library.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_set_debug(int32_t enable);
+pkv_status pkv_debug_check(void* stream);
+
+/* ---------------------------------------------------------------------------
  * Slot mapping ([LLMI] "PagedAttention & Memory Management (vLLM)": logical
  * block pos / block_size of a sequence maps through its block-table row to a
  * physical block; the token sits at offset pos % block_size).

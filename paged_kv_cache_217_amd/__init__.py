@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     cache_desc,
     cascade_decode_attention,
     copy_blocks,
+    debug_check,
     decode_schedule,
     decode_workspace_bytes,
     default_partition_size,
@@ -25,6 +26,7 @@ from ._lib import (  # noqa: F401
     paged_decode_partials,
     paged_multi_query_attention,
     partial_views,
+    set_debug,
     slot_mapping,
     splitk_reduce,
     status_string,

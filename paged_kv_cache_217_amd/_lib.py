@@ -55,6 +55,8 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
     "pkv_version": (ctypes.c_char_p, []),
+    "pkv_set_debug": (_i32, [_i32]),
+    "pkv_debug_check": (_i32, [_vp]),
     "pkv_slot_mapping": (_i32, [_vp, _i32, _vp, _i32, _i32, _vp, _vp]),
     "pkv_kv_append": (_i32, [ctypes.POINTER(CacheDesc), _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                              _vp]),
@@ -407,6 +409,16 @@ def copy_blocks(k_cache, v_cache, pairs, stream=None):
     n = pairs.numel() // 2
     _check(lib().pkv_copy_blocks(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(pairs),
                                  n, _stream(stream)), "pkv_copy_blocks")
+
+
+def set_debug(enable):
+    """Turn the library's debug mode on or off (see pkv_set_debug)."""
+    _check(lib().pkv_set_debug(1 if enable else 0), "pkv_set_debug")
+
+
+def debug_check(stream=None):
+    """Raise PkvError if an earlier call's debug checks found a caller error."""
+    _check(lib().pkv_debug_check(_stream(stream)), "pkv_debug_check")
 
 
 def swap_bytes(k_cache, n_blocks):

@@ -21,6 +21,53 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 pkv_status from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
+// ------------------------------------------------------------ debug mode
+// Process-wide switch (set before use; not thread-safe). When on, calls that
+// take device data first report a caller error raised by an earlier call's
+// checks (synchronising the stream to read the flag), then enqueue the checks
+// of their own device inputs ahead of the work. One int32 flag per device,
+// allocated on first use.
+constexpr int kMaxDevices = 64;
+bool g_debug = false;
+int* g_flag[kMaxDevices] = {};
+
+// The current device's flag (allocated and cleared on first use), or null
+// when debug mode is off or the allocation failed.
+int* debug_flag() {
+  if (!g_debug) return nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (!g_flag[dev]) {
+    int* f = nullptr;
+    if (hipMalloc(&f, sizeof(int)) != hipSuccess) return nullptr;
+    if (hipMemset(f, 0, sizeof(int)) != hipSuccess) return nullptr;
+    g_flag[dev] = f;
+  }
+  return g_flag[dev];
+}
+
+// Reports (and clears) a flag raised by earlier checks on this device.
+pkv_status debug_take(hipStream_t s) {
+  if (!g_debug) return PKV_OK;
+  int* f = debug_flag();
+  if (!f) return PKV_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return PKV_ERR_HIP;
+  int h = 0;
+  if (hipMemcpy(&h, f, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return PKV_ERR_HIP;
+  if (h == 0) return PKV_OK;
+  if (hipMemset(f, 0, sizeof(int)) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_ERR_INVALID_ARG;
+}
+
+// Live block-table entries and lengths of a call (debug mode only).
+pkv_status debug_tables(hipStream_t s, const int32_t* tables, int max_blocks,
+                        const int32_t* lens, int fixed_len, int max_len, const int32_t* qlens,
+                        int Q, int B, const pkv_cache_desc* d) {
+  if (!g_debug) return PKV_OK;
+  return from_hip(pkv::launch_check_tables(tables, max_blocks, lens, fixed_len, max_len, qlens, Q,
+                                           B, d->block_size, d->num_blocks, debug_flag(), s));
+}
+
 pkv_status check_desc(const pkv_cache_desc* d) {
   if (!d || d->num_blocks <= 0 || d->n_kv <= 0) return PKV_ERR_INVALID_ARG;
   if (d->kv_dtype != PKV_BF16 && d->kv_dtype != PKV_FP8_E4M3 && d->kv_dtype != PKV_FP4_E2M1)
@@ -214,12 +261,25 @@ const char* pkv_status_string(pkv_status s) {
 
 const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
 
+pkv_status pkv_set_debug(int32_t enable) {
+  g_debug = enable != 0;
+  if (g_debug && !debug_flag()) {
+    g_debug = false;
+    return PKV_ERR_HIP;
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_debug_check(void* stream) { return debug_take(as_stream(stream)); }
+
 pkv_status pkv_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
                             const int32_t* positions, int32_t B, int32_t block_size,
                             int64_t* slots_out, void* stream) {
   if (B < 0 || max_blocks_per_seq <= 0 || block_size <= 0) return PKV_ERR_INVALID_ARG;
   if (B == 0) return PKV_OK;
   if (!block_tables || !positions || !slots_out) return PKV_ERR_INVALID_ARG;
+  const pkv_status pend = debug_take(as_stream(stream));
+  if (pend != PKV_OK) return pend;
   return from_hip(pkv::launch_slot_mapping(block_tables, max_blocks_per_seq, positions, B,
                                            block_size, slots_out, as_stream(stream)));
 }
@@ -235,6 +295,14 @@ pkv_status pkv_kv_append(const pkv_cache_desc* desc, void* k_cache, void* v_cach
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
     return PKV_ERR_INVALID_ARG;
   if (desc->kv_dtype != PKV_BF16 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (g_debug) {
+    st = debug_take(as_stream(stream));
+    if (st != PKV_OK) return st;
+    st = from_hip(pkv::launch_check_slots(
+        slot_mapping, T, static_cast<int64_t>(desc->num_blocks) * desc->block_size, debug_flag(),
+        as_stream(stream)));
+    if (st != PKV_OK) return st;
+  }
   return from_hip(pkv::launch_kv_append(*desc, k_cache, v_cache, k_new, v_new, slot_mapping, T,
                                         k_scale, v_scale, as_stream(stream)));
 }
@@ -273,6 +341,13 @@ pkv_status pkv_paged_decode_attention(const pkv_cache_desc* desc, void* out, int
   if (!out) return PKV_ERR_INVALID_ARG;
   st = attach_schedule(&a, schedule);
   if (st != PKV_OK) return st;
+  if (g_debug) {
+    st = debug_take(as_stream(stream));
+    if (st == PKV_OK)
+      st = debug_tables(as_stream(stream), block_tables, max_blocks_per_seq, context_lens, 0,
+                        max_context_len, nullptr, 0, B, desc);
+    if (st != PKV_OK) return st;
+  }
   a.out = out;
   a.out_dtype = out_dtype;
   // With more than 16 query heads per KV head the partition kernel would run
@@ -335,6 +410,13 @@ pkv_status pkv_paged_decode_partials(const pkv_cache_desc* desc, const void* q,
   a.ws_o = w.o;
   a.write_partials = true;
   a.wave_partitions = a.schedule == nullptr && use_wave_partitions(a.partition);
+  if (g_debug) {
+    st = debug_take(as_stream(stream));
+    if (st == PKV_OK)
+      st = debug_tables(as_stream(stream), block_tables, max_blocks_per_seq, context_lens, 0,
+                        max_context_len, nullptr, 0, B, desc);
+    if (st != PKV_OK) return st;
+  }
   return from_hip(pkv::launch_decode_partition(a, as_stream(stream)));
 }
 
@@ -348,6 +430,8 @@ pkv_status pkv_splitk_reduce(void* out, int32_t out_dtype, const float* m, const
   if (max_partitions > kMaxReducePartitions) return PKV_ERR_UNSUPPORTED;
   if (B == 0) return PKV_OK;
   if (!out || !m || !l || !o || !context_lens) return PKV_ERR_INVALID_ARG;
+  const pkv_status pend = debug_take(as_stream(stream));
+  if (pend != PKV_OK) return pend;
   return from_hip(pkv::launch_splitk_reduce(out, out_dtype, m, l, o, context_lens, B, n_q,
                                             d_head, max_partitions, partition_size,
                                             as_stream(stream)));
@@ -400,6 +484,13 @@ pkv_status pkv_paged_multi_query_attention(const pkv_cache_desc* desc, void* out
   a.out = out;
   a.out_dtype = out_dtype;
   const hipStream_t s = as_stream(stream);
+  if (g_debug) {
+    st = debug_take(s);
+    if (st == PKV_OK)
+      st = debug_tables(s, block_tables, max_blocks_per_seq, context_lens, 0, max_context_len,
+                        query_lens, Q, B, desc);
+    if (st != PKV_OK) return st;
+  }
   if (a.P_max == 1) {
     a.write_partials = false;
     return from_hip(pkv::launch_multi_query_partition(a, s));
@@ -513,6 +604,16 @@ pkv_status pkv_cascade_decode_attention(
   if (need > 0 && !aligned16(workspace)) return PKV_ERR_INVALID_ARG;
   const hipStream_t s = as_stream(stream);
   char* ws = static_cast<char*>(workspace);
+  if (g_debug) {
+    st = debug_take(s);
+    if (st == PKV_OK && prefix_len > 0)
+      st = debug_tables(s, prefix_table, prefix_len / desc->block_size, nullptr, prefix_len,
+                        prefix_len, nullptr, 0, 1, desc);
+    if (st == PKV_OK)
+      st = debug_tables(s, block_tables, max_blocks_per_seq, suffix_lens, 0, max_suffix_len,
+                        nullptr, 0, B, desc);
+    if (st != PKV_OK) return st;
+  }
 
   Workspace wp{}, wsuf{};
   if (pl.Pp_max > 0) {
@@ -604,6 +705,8 @@ pkv_status pkv_swap_out(const pkv_cache_desc* desc, const void* k_cache, const v
   pkv_status st = check_swap(desc, k_cache, v_cache, block_ids, n_blocks, staging, host);
   if (st != PKV_OK || n_blocks == 0) return st;
   const hipStream_t s = as_stream(stream);
+  st = debug_take(s);
+  if (st != PKV_OK) return st;
   hipError_t e = pkv::launch_swap_pack(*desc, k_cache, v_cache, block_ids, n_blocks, staging, s);
   if (e != hipSuccess) return PKV_ERR_HIP;
   return from_hip(hipMemcpyAsync(host, staging, pkv_swap_bytes(desc, n_blocks),
@@ -616,6 +719,8 @@ pkv_status pkv_swap_in(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
   pkv_status st = check_swap(desc, k_cache, v_cache, block_ids, n_blocks, staging, host);
   if (st != PKV_OK || n_blocks == 0) return st;
   const hipStream_t s = as_stream(stream);
+  st = debug_take(s);
+  if (st != PKV_OK) return st;
   hipError_t e = hipMemcpyAsync(staging, host, pkv_swap_bytes(desc, n_blocks),
                                 hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return PKV_ERR_HIP;
@@ -640,6 +745,8 @@ pkv_status pkv_decode_schedule(const int32_t* context_lens, int32_t B, int32_t m
   const int64_t P_max = std::max<int64_t>(1, cdiv(max_context_len, partition_size));
   if (P_max > kMaxReducePartitions) return PKV_ERR_UNSUPPORTED;
   if (schedule_bytes_ < schedule_bytes(B, P_max)) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  const pkv_status pend = debug_take(as_stream(stream));
+  if (pend != PKV_OK) return pend;
   return from_hip(pkv::launch_decode_schedule(context_lens, B, partition_size,
                                               static_cast<int>(P_max),
                                               static_cast<int32_t*>(schedule), as_stream(stream)));
@@ -653,6 +760,13 @@ pkv_status pkv_copy_blocks(const pkv_cache_desc* desc, void* k_cache, void* v_ca
   if (n_pairs == 0) return PKV_OK;
   if (!k_cache || !v_cache || !pairs) return PKV_ERR_INVALID_ARG;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
+  if (g_debug) {
+    st = debug_take(as_stream(stream));
+    if (st == PKV_OK)
+      st = from_hip(pkv::launch_check_pairs(pairs, n_pairs, desc->num_blocks, debug_flag(),
+                                            as_stream(stream)));
+    if (st != PKV_OK) return st;
+  }
   return from_hip(pkv::launch_copy_blocks(*desc, k_cache, v_cache, pairs, n_pairs,
                                           as_stream(stream)));
 }
@@ -667,6 +781,14 @@ pkv_status pkv_gather_kv(const pkv_cache_desc* desc, void* k_out, void* v_out,
   if (!k_out || !v_out || !k_cache || !v_cache || !block_table_row) return PKV_ERR_INVALID_ARG;
   if (!aligned16(k_out) || !aligned16(v_out) || !aligned16(k_cache) || !aligned16(v_cache))
     return PKV_ERR_INVALID_ARG;
+  if (g_debug) {
+    st = debug_take(as_stream(stream));
+    if (st == PKV_OK)
+      st = debug_tables(as_stream(stream), block_table_row,
+                        static_cast<int>(cdiv(context_len, desc->block_size)), nullptr,
+                        context_len, context_len, nullptr, 0, 1, desc);
+    if (st != PKV_OK) return st;
+  }
   return from_hip(pkv::launch_gather(*desc, k_out, v_out, k_cache, v_cache, block_table_row,
                                      context_len, as_stream(stream)));
 }

@@ -390,3 +390,8 @@ def test_block_manager_errors():
     with pytest.raises(pkv.PkvError):
         bm.export_table([1], 0)             # one block does not fit in zero columns
     assert bm.seq_len(99) == -1 and bm.ref_count(7) == -1
+
+
+def test_debug_check_is_ok_while_debug_mode_is_off():
+    """With debug mode off (the default) the check makes no HIP call and returns OK."""
+    assert pkv.lib().pkv_debug_check(None) == _lib.PKV_OK
