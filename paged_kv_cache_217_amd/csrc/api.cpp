@@ -9,6 +9,7 @@
 
 #include "pkv.h"
 #include "pkv_internal.h"
+#include "debug_checks.h"
 
 namespace {
 

@@ -7,7 +7,7 @@
 // run ahead of the work on the caller's stream and raise a per-device flag for
 // the caller errors the interface names; the next call reports it. They only
 // read within the arrays the call describes.
-#include "pkv_internal.h"
+#include "debug_checks.h"
 
 namespace pkv {
 

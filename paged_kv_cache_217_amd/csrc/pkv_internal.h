@@ -81,16 +81,6 @@ hipError_t launch_swap_unpack(const pkv_cache_desc& d, void* k_cache, void* v_ca
                               const int32_t* block_ids, int n, const void* staging,
                               hipStream_t stream);
 
-// Debug-mode checks of caller data in device memory; each raises *flag on a
-// violation and reads only within the arrays described.
-hipError_t launch_check_tables(const int32_t* tables, int max_blocks, const int32_t* lens,
-                               int fixed_len, int max_len, const int32_t* qlens, int Q, int B,
-                               int bs, int num_blocks, int* flag, hipStream_t stream);
-hipError_t launch_check_slots(const int64_t* slots, int T, int64_t pool_slots, int* flag,
-                              hipStream_t stream);
-hipError_t launch_check_pairs(const int32_t* pairs, int n, int num_blocks, int* flag,
-                              hipStream_t stream);
-
 // Whether the decode kernels were built for this (d, bs, G, dtype) combination.
 bool decode_supported(int d, int bs, int G, int kv_dtype);
 
