@@ -465,6 +465,15 @@ int32_t pkv_bm_num_cached(const pkv_bm* bm);
 int32_t pkv_bm_num_evictable(const pkv_bm* bm);
 int32_t pkv_bm_num_free(const pkv_bm* bm);
 int32_t pkv_bm_ref_count(const pkv_bm* bm, int32_t block);
+/* Invariant check of the manager's state, O(blocks + table entries + cache):
+ * the free pool holds distinct, unreferenced, uncached blocks of the pool;
+ * a block's count equals its number of occurrences in resident sequences;
+ * each block is free, referenced, or cached with count 0; a resident
+ * sequence holds cdiv(length, block_size) blocks and a swapped one none; the
+ * radix cache's keys, parents and child counts agree with its child map; the
+ * evictable set is exactly the cached leaves with count 0. PKV_OK, or
+ * PKV_ERR_INVALID_ARG if any fails (or bm is NULL). Changes nothing. */
+pkv_status pkv_bm_check(const pkv_bm* bm);
 
 #ifdef __cplusplus
 }

@@ -105,6 +105,7 @@ SIGNATURES = {
     "pkv_bm_seq_len": (ctypes.c_int64, [_vp, ctypes.c_int64]),
     "pkv_bm_num_free": (_i32, [_vp]),
     "pkv_bm_ref_count": (_i32, [_vp, _i32]),
+    "pkv_bm_check": (_i32, [_vp]),
 }
 
 _lib = None
@@ -498,6 +499,10 @@ class BlockManager:
         _check(lib().pkv_bm_append_slot(self._h, seq, ctypes.byref(slot), ctypes.byref(src),
                                         ctypes.byref(dst)), "pkv_bm_append_slot")
         return slot.value, src.value, dst.value
+
+    def check(self):
+        """Raise PkvError if the manager's invariants do not hold (pkv_bm_check)."""
+        _check(lib().pkv_bm_check(self._h), "pkv_bm_check")
 
     def fork(self, parent, child):
         _check(lib().pkv_bm_fork(self._h, parent, child), "pkv_bm_fork")

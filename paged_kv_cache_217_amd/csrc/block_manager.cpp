@@ -350,6 +350,67 @@ int32_t pkv_bm_num_free(const pkv_bm* bm) {
   return bm ? static_cast<int32_t>(bm->free_pool.size()) : -1;
 }
 
+pkv_status pkv_bm_check(const pkv_bm* bm) {
+  if (!bm) return PKV_ERR_INVALID_ARG;
+  const int32_t nb = static_cast<int32_t>(bm->ref.size());
+  const int64_t bs = bm->block_size;
+  constexpr pkv_status kBad = PKV_ERR_INVALID_ARG;
+  // free pool: distinct pool blocks, unreferenced and not cached
+  std::vector<char> in_free(nb, 0);
+  for (int32_t b : bm->free_pool) {
+    if (b < 0 || b >= nb || in_free[b] || bm->ref[b] != 0 || bm->cached(b)) return kBad;
+    in_free[b] = 1;
+  }
+  // counts: each block's count is its number of occurrences in resident
+  // sequences; a sequence's blocks cover its length exactly
+  std::vector<int64_t> uses(nb, 0);
+  for (const auto& kv : bm->seqs) {
+    const auto& sq = kv.second;
+    if (sq.len < 0) return kBad;
+    if (sq.swapped) {
+      if (!sq.blocks.empty()) return kBad;
+      continue;
+    }
+    if (static_cast<int64_t>(sq.blocks.size()) != (sq.len + bs - 1) / bs) return kBad;
+    for (int32_t b : sq.blocks) {
+      if (b < 0 || b >= nb) return kBad;
+      uses[b] += 1;
+    }
+  }
+  // every block is free, referenced, or cached and idle: exactly one
+  for (int32_t b = 0; b < nb; ++b) {
+    if (bm->ref[b] < 0 || bm->ref[b] != uses[b]) return kBad;
+    if (bm->ref[b] == 0 && !in_free[b] && !bm->cached(b)) return kBad;
+  }
+  // radix cache: keys and parents agree with the child map, child counts
+  // are exact, and the evictable set is the idle cached leaves
+  std::vector<int32_t> kids(nb, 0);
+  int32_t n_cached = 0, n_idle_leaves = 0;
+  for (int32_t b = 0; b < nb; ++b) {
+    if (!bm->cached(b)) continue;
+    n_cached += 1;
+    const int32_t parent = bm->cached_parent[b];
+    if (parent < -1 || parent >= nb || (parent >= 0 && !bm->cached(parent))) return kBad;
+    if (bm->cached_key[b].parent != parent ||
+        static_cast<int64_t>(bm->cached_key[b].tokens.size()) != bs)
+      return kBad;
+    auto it = bm->children.find(bm->cached_key[b]);
+    if (it == bm->children.end() || it->second != b) return kBad;
+    if (parent >= 0) kids[parent] += 1;
+  }
+  if (n_cached != bm->n_cached || static_cast<int32_t>(bm->children.size()) != n_cached)
+    return kBad;
+  for (int32_t b = 0; b < nb; ++b) {
+    if (bm->cached(b) && kids[b] != bm->n_children[b]) return kBad;
+    if (bm->idle_leaf(b)) {
+      n_idle_leaves += 1;
+      if (!bm->evictable.count({bm->stamp[b], b})) return kBad;
+    }
+  }
+  if (static_cast<int32_t>(bm->evictable.size()) != n_idle_leaves) return kBad;
+  return PKV_OK;
+}
+
 int32_t pkv_bm_ref_count(const pkv_bm* bm, int32_t block) {
   if (!bm || block < 0 || block >= static_cast<int32_t>(bm->ref.size())) return -1;
   return bm->ref[block];

@@ -90,6 +90,7 @@ int main() {
         if (pkv_bm_free(bm, live[i]) != PKV_OK) return fail("free");
         live.erase(live.begin() + static_cast<long>(i));
       }
+      if (pkv_bm_check(bm) != PKV_OK) return fail("pkv_bm_check");
       // every block is free, referenced or cached and idle; counts never negative
       int referenced = 0;
       for (int b = 0; b < nb; ++b) {

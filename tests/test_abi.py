@@ -200,6 +200,7 @@ def test_block_manager_matches_the_model_on_random_operations():
                 model.free(seq)
                 lib_bm.free(seq)
             assert lib_bm.num_free() == len(model.free_pool)
+            lib_bm.check()
         for blk in range(nb):
             assert lib_bm.ref_count(blk) == model.ref[blk]
         mb = max([len(t) for t in model.tables.values()] + [1])
@@ -264,6 +265,7 @@ def test_block_manager_with_swaps_matches_the_model():
                 model.free(seq)
                 lib_bm.free(seq)
             assert lib_bm.num_free() == len(model.free_pool)
+            lib_bm.check()
         for blk in range(nb):
             assert lib_bm.ref_count(blk) == model.ref[blk]
         for s in resident + swapped:
@@ -373,6 +375,7 @@ def test_block_manager_prefix_cache_matches_the_model():
             assert lib_bm.num_free() == len(model.free_pool)
             assert lib_bm.num_cached() == len(model.node_of)
             assert lib_bm.num_evictable() == len(model._evictable())
+            lib_bm.check()
         for blk in range(nb):
             assert lib_bm.ref_count(blk) == model.ref[blk]
         mb = max([len(t) for t in model.tables.values()] + [1])

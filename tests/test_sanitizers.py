@@ -27,3 +27,20 @@ def test_block_manager_under_asan_and_ubsan(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
     assert r.returncode == 0, r.stderr[-2000:]
     assert "block manager: ok" in r.stdout
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_block_manager_check_detects_planted_corruption(tmp_path):
+    """pkv_bm_check passes a state built through the ABI and rejects each of a
+    list of corruptions planted in copies of it (the driver includes the
+    manager's source to reach the opaque state)."""
+    exe = tmp_path / "bm_check"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-omit-frame-pointer", "-fno-sanitize-recover=all", f"-I{ROOT}/include",
+           os.path.join(ROOT, "tests", "native", "bm_check_mutations.cpp"), "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "every planted corruption detected" in r.stdout
