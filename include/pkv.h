@@ -82,8 +82,9 @@ const char* pkv_version(void);
  * unspecified.
  *
  * pkv_set_debug(1) turns the mode on for the process (0 turns it off). It
- * allocates one int32 flag on the current device, and on each further device
- * at its first debug call. Returns PKV_ERR_HIP if that allocation fails.
+ * allocates one int32 flag on the current device (kept until the process
+ * ends) and clears it, and allocates one on each further device at its first
+ * debug call. Returns PKV_ERR_HIP, with the mode left off, if that fails.
  *
  * While it is on, each entry point that takes device data and a stream:
  *   1. validates its host arguments as always;

@@ -264,7 +264,10 @@ const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
 
 pkv_status pkv_set_debug(int32_t enable) {
   g_debug = enable != 0;
-  if (g_debug && !debug_flag()) {
+  if (!g_debug) return PKV_OK;
+  int* f = debug_flag();
+  // a fresh start on this device: nothing pending from an earlier session
+  if (!f || hipMemset(f, 0, sizeof(int)) != hipSuccess) {
     g_debug = false;
     return PKV_ERR_HIP;
   }
