@@ -73,3 +73,15 @@ def test_verification_bytes_read_the_context_once():
     assert split - single == 2 * 64 * 4 * 64 * 2 * 130 * 4
     flops, _ = bench.multi_query_work(w, 1)
     assert flops == 4 * 128 * 64 * 64 * (4 * 8192 - 6)
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    """The library has no multi-GPU path: --gpus N > 1 stops before any work."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
