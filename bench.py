@@ -260,12 +260,7 @@ def run(args, w, pool, np, torch, W):
     kv_gbs = kv_bytes_layer * layers / (ms_step * 1e-3) / 1e9
     tok_s = B / (ms_step * 1e-3)
 
-    traffic = None
-    if os.path.exists(COUNTERS):
-        c = json.load(open(COUNTERS))
-        if c.get("kernel_hash") == kernel_hash() and c.get("workload") == w.name \
-                and c.get("partition") == P:
-            traffic = c.get("traffic_bytes_per_launch")
+    traffic = counter_traffic(w.name, P)
 
     result = {
         "metric": METRIC,
@@ -312,6 +307,21 @@ def run(args, w, pool, np, torch, W):
             except Exception as e:           # the GPU figures stand without it
                 log(f"[bench] multi-process oracle baseline failed: {e!r}")
     print(json.dumps(result), flush=True)
+
+
+def counter_traffic(name, P):
+    """HBM bytes per launch of the partition kernel for workload `name` at
+    partition size P, from the committed rocprofv3 counters, or None when
+    none were taken for it or the kernel sources changed since."""
+    if not os.path.exists(COUNTERS):
+        return None
+    c = json.load(open(COUNTERS))
+    if c.get("kernel_hash") != kernel_hash():
+        return None
+    if c.get("workload") == name and c.get("partition") == P:
+        return c.get("traffic_bytes_per_launch")
+    e = c.get("workloads", {}).get(name, {})
+    return e.get("traffic_bytes_per_launch") if e.get("partition") == P else None
 
 
 def kv_bytes(w):

@@ -85,3 +85,22 @@ def test_more_than_one_gpu_exits_with_a_message():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_counter_traffic_is_reported_only_for_measured_configurations():
+    """While the kernel sources match the committed counters, each decode
+    workload at its bench partition has HBM traffic close to its algorithmic
+    bytes (no re-reads); other partitions, and changed sources, give None."""
+    cases = [(W.gqa_70b(), 8192, 0.01), (W.gqa_70b_fp4(), 8192, 0.01),
+             (W.gqa_70b_fp8(), 16384, 0.01), (W.mha_7b(), 8192, 0.01),
+             (W.long_shared_prefix(), 512, 0.03)]       # prefix blocks shared: cache hits
+    current = bench.counter_traffic(cases[0][0].name, 8192) is not None
+    for w, P, tol in cases:
+        t = bench.counter_traffic(w.name, P)
+        if not current:
+            assert t is None
+            continue
+        algo = bench.partition_bytes(w, P)
+        assert abs(t["total"] - algo) <= tol * algo, (w.name, t["total"], algo)
+        assert t["total"] == t["read"] + t["written"]
+        assert bench.counter_traffic(w.name, P // 2) is None
