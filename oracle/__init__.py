@@ -29,9 +29,13 @@ Modules:
 
 Pin status (what each function is checked against in tests/, CPU only):
   every public function has at least one pin that is not a retyping of its
-  own formula (closed forms, special cases with known answers, library
-  routines, exhaustive comparison, invariants). No function is
-  "parity unpinned".
+  own formula: closed forms, values the pages print, special cases with known
+  answers, library routines (torch's bfloat16 / float8 conversions and
+  scaled_dot_product_attention), exhaustive comparison and invariants. No
+  function is "parity unpinned". Outputs at sizes the brute-force pins cannot
+  reach come from `paged.decode_attention` itself, which those pins cover.
+  tests/test_oracle_mutations.py plants 33 plausible mistakes in these
+  modules, one at a time, and requires the pins to fail on each.
 """
 
 from . import bf16, fp8_e4m3, fp4_e2m1, paged, block_manager, sizing  # noqa: F401

@@ -165,34 +165,6 @@ def decode_attention(q_bits, k_cache, v_cache, block_tables, context_lens, scale
     return out
 
 
-def decode_attention_heads(q_bits, k_cache, v_cache, block_tables, context_lens, scale,
-                           pairs, kv_dtype=BF16, k_scale=None, v_scale=None):
-    """Same as `decode_attention` for a list of (b, h) pairs only.
-
-    Used where the full batch is too large for the oracle: the listed outputs
-    are computed one by one. Returns float64 [len(pairs), d].
-    """
-    n_q, d = q_bits.shape[1], q_bits.shape[2]
-    G = n_q // k_cache.shape[1]
-    out = np.zeros((len(pairs), d))
-    cache = {}
-    for i, (b, h) in enumerate(pairs):
-        g = h // G
-        key = (b, g)
-        if key not in cache:
-            ctx = int(context_lens[b])
-            kr = gather(k_cache[:, g:g + 1], block_tables[b], ctx)
-            vr = gather(v_cache[:, g:g + 1], block_tables[b], ctx)
-            ks = None if k_scale is None else np.asarray(k_scale)[g:g + 1]
-            vs = None if v_scale is None else np.asarray(v_scale)[g:g + 1]
-            cache = {key: (dequantize(kr, kv_dtype, ks)[:, 0, :],
-                           dequantize(vr, kv_dtype, vs)[:, 0, :])}
-        kd, vd = cache[key]
-        q = _bf16.to_f64(q_bits[b, h])
-        out[i], _ = attention_one(q, kd, vd, scale)
-    return out
-
-
 # --------------------------------------------------------------------------
 # 3. split-K partials and their log-sum-exp merge
 # --------------------------------------------------------------------------

@@ -16,3 +16,13 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_sessionstart(session):
+    # A planted oracle mistake, for tests/test_oracle_mutations.py only: that
+    # test runs the oracle's CPU pins in a pytest process of its own with
+    # ORACLE_MUTANT naming the mistake, and expects them to fail.
+    name = os.environ.get("ORACLE_MUTANT")
+    if name:
+        import oracle_mutants
+        oracle_mutants.apply(name)

@@ -70,9 +70,47 @@ def test_encoder_matches_torch_on_every_bf16_pattern(scale):
 
 
 def test_encoder_division_is_binary32():
-    # x / s is rounded to float32 before encoding: a quotient that is a tie only in
-    # float64 must follow the float32 result.
-    x = np.float32(1.0000001)
-    s = np.float32(0.94117647)
-    q32 = np.float32(x / s)
-    assert fp8.quantize_f32_div(np.array([x]), s)[0] == fp8.encode(np.array([q32]))[0]
+    # The quotient is rounded to binary32 before it is encoded. Here the float32
+    # quotient is exactly 19/1024, the midpoint of codes 0x09 (9/512) and 0x0A
+    # (10/512), which ties to the even code 0x0A; the float64 quotient lies just
+    # below the midpoint and would give 0x09.
+    x = np.float32(0.019002437591552734)
+    s = np.float32(1.024131417274475)
+    q32 = np.divide(x, s, dtype=np.float32)
+    assert q32 == np.float32(19 / 1024)
+    assert float(x) / float(s) < 19 / 1024
+    assert fp8.quantize_f32_div(np.array([x]), s)[0] == 0x0A
+    tq = torch.tensor([x]) / torch.tensor([s])            # torch's binary32 division and cast
+    assert tq.to(torch.float8_e4m3fn).view(torch.uint8).item() == 0x0A
+
+
+def test_fp8_decode_attention_equals_dense_reference():
+    # paged FP8 attention against a dense float64 computation whose values are
+    # decoded by torch's float8_e4m3fn conversion and scaled per KV head
+    from oracle import paged
+    rng = np.random.default_rng(21711)
+    nb, n_kv, bs, d, n_q = 6, 2, 4, 8, 4
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    k = rng.choice(finite, size=(nb, n_kv, bs, d)).astype(np.uint8)
+    v = rng.choice(finite, size=(nb, n_kv, bs, d)).astype(np.uint8)
+    ks = np.array([0.007, 0.011], dtype=np.float32)
+    vs = np.array([0.25, 2.0], dtype=np.float32)
+    qf = rng.standard_normal((1, n_q, d)).astype(np.float32)
+    q = torch.from_numpy(qf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    table = np.array([[4, 1, 5]], dtype=np.int32)
+    out = paged.decode_attention(q, k, v, table, np.array([10], np.int32), 0.3, paged.FP8, ks, vs)
+
+    def torch_decode(codes):
+        return torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+
+    kd = np.concatenate([k[b] for b in (4, 1, 5)], axis=1)[:, :10]
+    vd = np.concatenate([v[b] for b in (4, 1, 5)], axis=1)[:, :10]
+    kf = torch_decode(kd) * ks.astype(np.float64)[:, None, None]
+    vf = torch_decode(vd) * vs.astype(np.float64)[:, None, None]
+    qd = torch.from_numpy(qf).to(torch.bfloat16).double().numpy()[0]
+    for h in range(n_q):
+        g = h // 2
+        sc = 0.3 * kf[g] @ qd[h]
+        w = np.exp(sc - sc.max())
+        w /= w.sum()
+        assert np.allclose(out[0, h], w @ vf[g], rtol=1e-12, atol=1e-12)
