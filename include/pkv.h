@@ -35,8 +35,9 @@
  * head) tile of block_size * d_head elements is contiguous.
  *
  * Supported geometry: block_size in {16, 32}; d_head in {64, 128} (FP4:
- * 128); n_q = G * n_kv with G in {1, 2, 4, 8, 16} or any multiple of 16.
- * Anything else returns PKV_ERR_UNSUPPORTED.
+ * 128); n_q = G * n_kv for any G >= 1, from MHA (G = 1) to MQA (n_kv = 1).
+ * Other block sizes, widths or element types return PKV_ERR_UNSUPPORTED; an
+ * n_q that is not a multiple of n_kv returns PKV_ERR_INVALID_ARG.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -292,9 +293,16 @@ pkv_status pkv_paged_multi_query_attention(const pkv_cache_desc* desc, void* out
  * Passing it as `schedule` to pkv_paged_decode_attention / _partials makes
  * the partition kernel take its work in that order. The call must use the
  * same context_lens contents, B, max_context_len and resolved partition size
- * the schedule was built with (results are unspecified otherwise); NULL keeps
- * the static grid order. partition_size must be > 0 (resolve 0 with
- * pkv_default_partition_size first). B above 65535 is unsupported.
+ * the schedule was built with; NULL keeps the static grid order.
+ * partition_size must be > 0 (resolve 0 with pkv_default_partition_size
+ * first). B above 65535 is unsupported.
+ * A schedule whose recorded partition size, B or partition count differs from
+ * the call's is not followed: the partition kernel computes nothing and the
+ * results are unspecified, but nothing outside the call's arrays is read or
+ * written; items naming a sequence or partition outside the call are
+ * skipped. Debug mode (pkv_set_debug) checks the schedule ahead of the work
+ * and reports such a mismatch, an item count other than the call's number of
+ * partitions, or an item outside the call, as PKV_ERR_INVALID_ARG.
  * ------------------------------------------------------------------------- */
 size_t pkv_decode_schedule_bytes(int32_t B, int32_t max_context_len, int32_t partition_size);
 

@@ -161,6 +161,42 @@ def _need(t, dtype, what, device=True):
         raise ValueError(f"{what} must be a GPU tensor")
 
 
+def _check_out(out, shape, device):
+    """A caller's output tensor must be exactly what the kernel writes."""
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("output dtype must be float32 or bfloat16")
+    if not out.is_contiguous() or not out.is_cuda or out.device != device:
+        raise ValueError("out must be a contiguous tensor on the inputs' GPU")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must have shape {tuple(shape)}, got {tuple(out.shape)}")
+
+
+def _check_scales(k_scale, v_scale, n_kv, device):
+    for s, name in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if s is None:
+            raise ValueError("FP8 and FP4 caches need k_scale and v_scale")
+        _need(s, torch.float32, name)
+        if s.numel() != n_kv or s.device != device:
+            raise ValueError(f"{name} must hold one float32 per KV head ({n_kv}) on the "
+                             "caches' GPU")
+
+
+def _check_workspace(ws, device):
+    _need(ws, torch.uint8, "workspace")
+    if ws.device != device:
+        raise ValueError("workspace must be on the inputs' GPU")
+
+
+def _check_caches(k_cache, v_cache):
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    for c in (k_cache, v_cache):
+        if not c.is_contiguous() or not c.is_cuda:
+            raise ValueError("caches must be contiguous GPU tensors")
+    if v_cache.device != k_cache.device:
+        raise ValueError("k_cache and v_cache must be on one GPU")
+
+
 def kv_dtype_of(cache):
     if cache.dtype == torch.bfloat16:
         return PKV_BF16
@@ -197,8 +233,14 @@ def slot_mapping(block_tables, positions, block_size, out=None, stream=None):
     _need(block_tables, torch.int32, "block_tables")
     _need(positions, torch.int32, "positions")
     B = positions.numel()
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks] with B = positions.numel()")
     if out is None:
         out = torch.empty(B, dtype=torch.int64, device=positions.device)
+    else:
+        _need(out, torch.int64, "out")
+        if out.numel() != B:
+            raise ValueError("out must hold one slot per position")
     _check(lib().pkv_slot_mapping(_ptr(block_tables), block_tables.shape[1], _ptr(positions), B,
                                   block_size, _ptr(out), _stream(stream)), "pkv_slot_mapping")
     return out
@@ -207,12 +249,15 @@ def slot_mapping(block_tables, positions, block_size, out=None, stream=None):
 def kv_append(k_cache, v_cache, k_new, v_new, slots, k_scale=None, v_scale=None, stream=None):
     """Store k_new/v_new (bf16 [T, n_kv, d]) at `slots` (int64 [T]) in the caches, in place."""
     desc = cache_desc(k_cache)
+    _check_caches(k_cache, v_cache)
     _need(k_new, torch.bfloat16, "k_new")
     _need(v_new, torch.bfloat16, "v_new")
     _need(slots, torch.int64, "slot_mapping")
     T = slots.numel()
     if k_new.shape != (T, desc.n_kv, desc.d_head) or v_new.shape != k_new.shape:
         raise ValueError("k_new/v_new must be [T, n_kv, d_head]")
+    if desc.kv_dtype in (PKV_FP8_E4M3, PKV_FP4_E2M1):
+        _check_scales(k_scale, v_scale, desc.n_kv, k_cache.device)
     _check(lib().pkv_kv_append(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(k_new),
                                _ptr(v_new), _ptr(slots), T, _ptr(k_scale), _ptr(v_scale),
                                _stream(stream)), "pkv_kv_append")
@@ -243,20 +288,18 @@ def _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_s
     _need(q, torch.bfloat16, "q")
     _need(block_tables, torch.int32, "block_tables")
     _need(context_lens, torch.int32, "context_lens")
-    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
-        raise ValueError("k_cache and v_cache must match")
-    for c in (k_cache, v_cache):
-        if not c.is_contiguous() or not c.is_cuda:
-            raise ValueError("caches must be contiguous GPU tensors")
+    _check_caches(k_cache, v_cache)
     desc = cache_desc(k_cache)
+    if q.dim() != 3 or block_tables.dim() != 2:
+        raise ValueError("q must be [B, n_q, d_head] and block_tables [B, max_blocks]")
     B, n_q, d = q.shape
     if d != desc.d_head or block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("q / block_tables / context_lens shapes disagree with the cache")
+    for t in (q, block_tables, context_lens):
+        if t.device != k_cache.device:
+            raise ValueError("every input must be on the caches' GPU")
     if desc.kv_dtype in (PKV_FP8_E4M3, PKV_FP4_E2M1):
-        for s in (k_scale, v_scale):
-            if s is None:
-                raise ValueError("FP8 and FP4 caches need k_scale and v_scale")
-            _need(s, torch.float32, "scale")
+        _check_scales(k_scale, v_scale, desc.n_kv, k_cache.device)
     return desc, B, n_q, d
 
 
@@ -282,9 +325,13 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
                                      k_scale, v_scale)
     if out is None:
         out = torch.empty((B, n_q, d), dtype=out_dtype, device=q.device)
+    _check_out(out, (B, n_q, d), q.device)
     P = _resolve_partition(k_cache, B, n_q, max_context_len, partition_size)
     if workspace is None:
         workspace, _ = make_workspace(k_cache, B, n_q, max_context_len, P)
+    _check_workspace(workspace, q.device)
+    if schedule is not None:
+        _need(schedule, torch.int32, "schedule")
     _check(lib().pkv_paged_decode_attention(
         ctypes.byref(desc), _ptr(out), _out_code(out.dtype), _ptr(q), _ptr(k_cache),
         _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, n_q,
@@ -317,10 +364,12 @@ def paged_multi_query_attention(q, query_lens, k_cache, v_cache, block_tables, c
         raise ValueError("query_lens must hold one length per sequence")
     if out is None:
         out = torch.empty((B, Q, n_q, d), dtype=out_dtype, device=q.device)
+    _check_out(out, (B, Q, n_q, d), q.device)
     P = int(partition_size) or multi_query_partition_size(k_cache, B, Q, n_q, max_context_len)
     if workspace is None:
         nbytes = int(lib().pkv_multi_query_workspace_bytes(B, Q, n_q, d, int(max_context_len), P))
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q.device)
     _check(lib().pkv_paged_multi_query_attention(
         ctypes.byref(desc), _ptr(out), _out_code(out.dtype), _ptr(q), Q, _ptr(query_lens),
         _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
@@ -340,13 +389,17 @@ def cascade_decode_attention(q, k_cache, v_cache, prefix_table, prefix_len, bloc
                                      k_scale, v_scale)
     if prefix_len:
         _need(prefix_table, torch.int32, "prefix_table")
+        if prefix_table.numel() * desc.block_size < int(prefix_len):
+            raise ValueError("prefix_table must hold prefix_len / block_size entries")
     if out is None:
         out = torch.empty((B, n_q, d), dtype=out_dtype, device=q.device)
+    _check_out(out, (B, n_q, d), q.device)
     if workspace is None:
         nbytes = int(lib().pkv_cascade_workspace_bytes(
             ctypes.byref(desc), B, n_q, int(prefix_len), int(prefix_partition),
             int(max_suffix_len), int(suffix_partition)))
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q.device)
     _check(lib().pkv_cascade_decode_attention(
         ctypes.byref(desc), _ptr(out), _out_code(out.dtype), _ptr(q), _ptr(k_cache),
         _ptr(v_cache), _ptr(prefix_table) if prefix_len else None, int(prefix_len),
@@ -378,6 +431,9 @@ def paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale
     P = int(partition_size)
     if workspace is None:
         workspace, _ = make_workspace(k_cache, B, n_q, max_context_len, P)
+    _check_workspace(workspace, q.device)
+    if schedule is not None:
+        _need(schedule, torch.int32, "schedule")
     _check(lib().pkv_paged_decode_partials(
         ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), B, n_q, int(max_context_len), float(scale),
@@ -391,12 +447,21 @@ def paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale
 def splitk_reduce(m, l, o, context_lens, partition_size, out=None, out_dtype=torch.float32,
                   stream=None):
     """Log-sum-exp merge of partials m, l [B, n_q, P_max], o [B, n_q, P_max, d]."""
+    if o.dim() != 4:
+        raise ValueError("o must be [B, n_q, P_max, d]")
     B, n_q, P_max, d = o.shape
     for t, name in ((m, "m"), (l, "l"), (o, "o")):
         _need(t, torch.float32, name)
+        if t.device != o.device:
+            raise ValueError("m, l and o must be on one GPU")
+    if tuple(m.shape) != (B, n_q, P_max) or tuple(l.shape) != (B, n_q, P_max):
+        raise ValueError("m and l must be [B, n_q, P_max] with o [B, n_q, P_max, d]")
     _need(context_lens, torch.int32, "context_lens")
+    if context_lens.numel() != B:
+        raise ValueError("context_lens must hold one length per sequence")
     if out is None:
         out = torch.empty((B, n_q, d), dtype=out_dtype, device=o.device)
+    _check_out(out, (B, n_q, d), o.device)
     _check(lib().pkv_splitk_reduce(_ptr(out), _out_code(out.dtype), _ptr(m), _ptr(l), _ptr(o),
                                    _ptr(context_lens), B, n_q, d, P_max, int(partition_size),
                                    _stream(stream)), "pkv_splitk_reduce")
@@ -406,7 +471,10 @@ def splitk_reduce(m, l, o, context_lens, partition_size, out=None, out_dtype=tor
 def copy_blocks(k_cache, v_cache, pairs, stream=None):
     """Copy blocks src -> dst in both caches; pairs is int32 [n, 2] on the GPU."""
     desc = cache_desc(k_cache)
+    _check_caches(k_cache, v_cache)
     _need(pairs, torch.int32, "pairs")
+    if pairs.numel() % 2:
+        raise ValueError("pairs must be int32 [n, 2]")
     n = pairs.numel() // 2
     _check(lib().pkv_copy_blocks(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(pairs),
                                  n, _stream(stream)), "pkv_copy_blocks")

@@ -5,7 +5,6 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
 
 #include "pkv.h"
 #include "pkv_internal.h"
@@ -67,6 +66,13 @@ pkv_status debug_tables(hipStream_t s, const int32_t* tables, int max_blocks,
   if (!g_debug) return PKV_OK;
   return from_hip(pkv::launch_check_tables(tables, max_blocks, lens, fixed_len, max_len, qlens, Q,
                                            B, d->block_size, d->num_blocks, debug_flag(), s));
+}
+
+// The longest-first schedule a call follows, if any (debug mode only).
+pkv_status debug_schedule(hipStream_t s, const pkv::DecodeArgs& a) {
+  if (!g_debug || a.schedule == nullptr) return PKV_OK;
+  return from_hip(pkv::launch_check_schedule(a.schedule, a.context_lens, a.B, a.partition,
+                                             a.P_max, debug_flag(), s));
 }
 
 pkv_status check_desc(const pkv_cache_desc* d) {
@@ -145,16 +151,8 @@ int32_t pick_partition_units(int64_t units, int32_t max_ctx, int64_t row_bytes) 
 }
 
 // Partials mode runs one wave per partition when partitions are short (each
-// wave then keeps a long load pipeline instead of a few chunks);
-// PKV_WAVE_PARTITIONS=0/1 overrides the choice (for measurement).
-bool use_wave_partitions(int32_t partition) {
-  static const int forced = [] {
-    const char* e = getenv("PKV_WAVE_PARTITIONS");
-    return e ? (e[0] == '1' ? 1 : 0) : -1;
-  }();
-  if (forced >= 0) return forced == 1;
-  return partition <= 1024;
-}
+// wave then keeps a long load pipeline instead of a few chunks).
+bool use_wave_partitions(int32_t partition) { return partition <= 1024; }
 
 size_t schedule_bytes(int64_t B, int64_t P_max) {
   return pkv::kScheduleHeader * sizeof(int32_t) + static_cast<size_t>(B * P_max) * 2 * sizeof(int32_t);
@@ -350,6 +348,7 @@ pkv_status pkv_paged_decode_attention(const pkv_cache_desc* desc, void* out, int
     if (st == PKV_OK)
       st = debug_tables(as_stream(stream), block_tables, max_blocks_per_seq, context_lens, 0,
                         max_context_len, nullptr, 0, B, desc);
+    if (st == PKV_OK) st = debug_schedule(as_stream(stream), a);
     if (st != PKV_OK) return st;
   }
   a.out = out;
@@ -419,6 +418,7 @@ pkv_status pkv_paged_decode_partials(const pkv_cache_desc* desc, const void* q,
     if (st == PKV_OK)
       st = debug_tables(as_stream(stream), block_tables, max_blocks_per_seq, context_lens, 0,
                         max_context_len, nullptr, 0, B, desc);
+    if (st == PKV_OK) st = debug_schedule(as_stream(stream), a);
     if (st != PKV_OK) return st;
   }
   return from_hip(pkv::launch_decode_partition(a, as_stream(stream)));

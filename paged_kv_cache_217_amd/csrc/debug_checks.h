@@ -19,4 +19,10 @@ hipError_t launch_check_slots(const int64_t* slots, int T, int64_t pool_slots, i
 hipError_t launch_check_pairs(const int32_t* pairs, int n, int num_blocks, int* flag,
                               hipStream_t stream);
 
+// Longest-first schedule: header (partition size, B, partition count) equal
+// to the call's, item count equal to the call's number of partitions, every
+// item a (sequence, partition) of the call.
+hipError_t launch_check_schedule(const int32_t* sched, const int32_t* lens, int B, int P,
+                                 int P_max, int* flag, hipStream_t stream);
+
 }  // namespace pkv

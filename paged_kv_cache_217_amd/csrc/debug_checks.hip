@@ -83,7 +83,49 @@ __global__ void check_pairs_kernel(const int32_t* __restrict__ pairs, int n, int
   }
 }
 
+// One workgroup. The header is read first; only if it names this call's
+// geometry (so the buffer holds B * P_max item slots) are the items read.
+// A sequence owns cdiv(len, P) partitions (at most P_max); in a single pass
+// (P_max == 1) every sequence, empty or not, has its one item.
+__global__ void check_schedule_kernel(const int32_t* __restrict__ sched,
+                                      const int32_t* __restrict__ lens, int B, int P, int P_max,
+                                      int* flag) {
+  __shared__ int total;
+  __shared__ int ok;
+  if (threadIdx.x == 0) {
+    total = 0;
+    ok = sched[1] == P && sched[2] == B && sched[3] == P_max;
+    if (!ok) raise(flag);
+  }
+  __syncthreads();
+  if (!ok) return;
+  auto parts = [&](int b) -> int {
+    const int len = lens[b];
+    const int np = len > 0 ? min((len + P - 1) / P, P_max) : 0;
+    return P_max == 1 ? 1 : np;
+  };
+  int mine = 0;
+  for (int b = threadIdx.x; b < B; b += blockDim.x) mine += parts(b);
+  atomicAdd(&total, mine);
+  __syncthreads();
+  const int n = sched[0];
+  if (threadIdx.x == 0 && n != total) raise(flag);
+  const int cap = min(n, B * P_max);
+  const int2* items = reinterpret_cast<const int2*>(sched + 8);
+  for (int i = threadIdx.x; i < cap; i += blockDim.x) {
+    const int2 it = items[i];
+    if (it.x < 0 || it.x >= B || it.y < 0 || it.y >= parts(it.x)) raise(flag);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_check_schedule(const int32_t* sched, const int32_t* lens, int B, int P,
+                                 int P_max, int* flag, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  check_schedule_kernel<<<1, 1024, 0, s>>>(sched, lens, B, P, P_max, flag);
+  return hipGetLastError();
+}
 
 hipError_t launch_check_tables(const int32_t* tables, int max_blocks, const int32_t* lens,
                                int fixed_len, int max_len, const int32_t* qlens, int Q, int B,

@@ -1,16 +1,22 @@
 // Paged decode attention, partition kernel on the gfx950 matrix cores.
 //
-// Same computation as the VALU partition kernel (see decode_attention.hip and
-// [MTKV] "Architecting Multi-Tier Disaggregated KV-Cache Hierarchies for
-// Terabyte-Scale LLM Inference", section "High-Throughput Paged Attention
-// Kernel Integration"): per (sequence, KV head, partition), online softmax of
-// scale * q . k over the partition's tokens for all query heads of the group,
+// What is computed follows [MTKV] "Architecting Multi-Tier Disaggregated
+// KV-Cache Hierarchies for Terabyte-Scale LLM Inference", section
+// "High-Throughput Paged Attention Kernel Integration": per (sequence, KV
+// head, partition), online softmax of scale * q . k over the partition's
+// tokens for all query heads of the group (query head h reads KV head h / G),
 // accumulating the weighted sum of V, with the K/V tiles fetched through the
-// block table.
+// block table; the weights are the softmax of [MTKV] "Mathematical
+// Formulation of Block Salience". The page's kernel runs one program per
+// (sequence, query head) and so reads every KV byte G times; here one
+// workgroup serves all query heads of a KV head (up to 16 per head tile), so
+// each byte of the partition is read once, and short batches are split over
+// the context (split-K) and merged by the log-sum-exp reduce.
 //
 // Why MFMA: with G = 8 query heads per KV head every bf16 K/V element feeds
 // 8 fp32 FMAs plus a conversion; on the vector ALU that is ~80% of its issue
-// rate at 70% of HBM bandwidth. v_mfma_f32_16x16x32_bf16 consumes the bf16
+// rate at 70% of HBM bandwidth (a vector-ALU form of this kernel measured
+// 944 us on the 70B layer against 368 us for the first matrix-core form). v_mfma_f32_16x16x32_bf16 consumes the bf16
 // tiles as loaded (no conversion) and does the contraction of 16 heads in one
 // instruction; heads beyond G are zero columns.
 //
@@ -113,8 +119,12 @@ void decode_partition_mfma(DecodeArgs a) {
   if (a.schedule != nullptr) {
     const int hxn = a.n_kv * tiles;
     const int item = blockIdx.x / hxn;
+    // a list built for another geometry is not followed (and its items may lie
+    // past the caller's buffer)
+    if (a.schedule[1] != a.partition || a.schedule[2] != a.B || a.schedule[3] != a.P_max) return;
     if (item >= a.schedule[0]) return;                 // past the list: nothing to do
     const int2 it = reinterpret_cast<const int2*>(a.schedule + kScheduleHeader)[item];
+    if (it.x < 0 || it.x >= a.B || it.y < 0 || it.y >= a.P_max) return;
     hx = blockIdx.x % hxn;
     b = it.x;
     pz = it.y;
@@ -463,24 +473,10 @@ constexpr int kMfmaWaves = 4;
 // and softmax work keeps a wave on a chunk long enough that one chunk in
 // flight does not cover the load latency: 97.6 -> 94.0 us on the 70B FP4
 // layer); bf16 and FP8 run two full chunks (FP8 measured no faster with four).
-// PKV_DECODE_DEPTH=2 or 4 forces the depth of the quantised formats, for
-// measurement.
-static int pipeline_depth(int fmt) {
-  static const int forced = [] {
-    const char* e = getenv("PKV_DECODE_DEPTH");
-    return e ? (e[0] == '4' ? 4 : 2) : 0;
-  }();
-  if (fmt == kFmtBf16) return 2;
-  return forced ? forced : (fmt == kFmtFp4 ? 4 : 2);
-}
-
 template <int D, int BS, int FMT>
 static hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  if (pipeline_depth(FMT) == 4)
-    decode_partition_mfma<D, BS, FMT, kMfmaWaves, true, FMT == kFmtBf16 ? 2 : 4>
-        <<<grid, kMfmaWaves * 64, 0, s>>>(a);
-  else
-    decode_partition_mfma<D, BS, FMT, kMfmaWaves, true, 2><<<grid, kMfmaWaves * 64, 0, s>>>(a);
+  constexpr int depth = FMT == kFmtFp4 ? 4 : 2;
+  decode_partition_mfma<D, BS, FMT, kMfmaWaves, true, depth><<<grid, kMfmaWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -23,7 +23,6 @@
 // position are not read at all. Rows that see no token of a partition emit
 // an empty partial (l = 0, o = 0) and the reduce skips them.
 #include <float.h>
-#include <stdlib.h>
 
 #include "mfma_common.h"
 #include "pkv_device.h"
@@ -484,23 +483,6 @@ void multi_query_partition_mfma(DecodeArgs a) {
   }
 }
 
-// Row tiles per wave, waves per tile set and waves per set, for a launch of
-// `tiles` row tiles per KV head; PKV_MQ_GROUP="TRS" (e.g. "214") overrides it
-// (for measurement).
-struct Group {
-  int TPW, R, S;
-};
-
-static Group pick_group(int tiles) {
-  static const int forced = [] {
-    const char* e = getenv("PKV_MQ_GROUP");
-    return e && e[0] && e[1] && e[2] ? (e[0] - '0') * 100 + (e[1] - '0') * 10 + (e[2] - '0')
-                                     : 0;
-  }();
-  if (forced == 114 || forced == 124 || forced == 214) return {forced / 100, forced / 10 % 10, forced % 10};
-  return tiles >= 2 ? Group{2, 1, 4} : Group{1, 1, 4};
-}
-
 template <int D, int BS, int FMT, int TPW, int R, int S>
 static hipError_t launch_g(const DecodeArgs& a, int tiles, hipStream_t s) {
   constexpr int tpg = TPW * R;
@@ -509,11 +491,11 @@ static hipError_t launch_g(const DecodeArgs& a, int tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Two or more row tiles per KV head: each wave applies every K/V chunk to two
+// tiles (one 4-wave workgroup per pair); a single tile runs one per wave.
 template <int D, int BS, int FMT>
 static hipError_t launch_mq(const DecodeArgs& a, int tiles, hipStream_t s) {
-  const Group gr = pick_group(tiles);
-  if (gr.TPW == 2) return launch_g<D, BS, FMT, 2, 1, 4>(a, tiles, s);
-  if (gr.R == 2) return launch_g<D, BS, FMT, 1, 2, 4>(a, tiles, s);
+  if (tiles >= 2) return launch_g<D, BS, FMT, 2, 1, 4>(a, tiles, s);
   return launch_g<D, BS, FMT, 1, 1, 4>(a, tiles, s);
 }
 
@@ -528,21 +510,11 @@ static hipError_t launch_mq_fmt(const DecodeArgs& a, int tiles, hipStream_t s) {
 
 // Many rows per KV head (128 or more) share each K/V chunk through LDS
 // (multi_query_lds.hip); fewer stream it into registers here.
-// PKV_MQ_KERNEL=reg / lds forces one of the two (for measurement).
-static int forced_mq_kernel() {
-  static const int v = [] {
-    const char* e = getenv("PKV_MQ_KERNEL");
-    return e ? (e[0] == 'l' ? 2 : e[0] == 'r' ? 1 : 0) : 0;
-  }();
-  return v;
-}
-
 hipError_t launch_multi_query_partition(const DecodeArgs& a, hipStream_t s) {
   if (a.kv_dtype == PKV_FP4_E2M1 && a.d != 128) return hipErrorInvalidValue;
   const int G = a.n_q / a.n_kv;
   const int tiles = (a.Q * G + 15) / 16;
-  const int forced = forced_mq_kernel();
-  if (forced == 2 || (forced == 0 && tiles >= 8)) return launch_multi_query_lds(a, s);
+  if (tiles >= 8) return launch_multi_query_lds(a, s);
   if (a.d == 128)
     return a.bs == 16 ? launch_mq_fmt<128, 16>(a, tiles, s) : launch_mq_fmt<128, 32>(a, tiles, s);
   return a.bs == 16 ? launch_mq_fmt<64, 16>(a, tiles, s) : launch_mq_fmt<64, 32>(a, tiles, s);

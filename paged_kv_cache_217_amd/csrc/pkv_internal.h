@@ -19,7 +19,7 @@ struct DecodeArgs {
   const uint8_t* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  const float* k_scale;       // FP8 only
+  const float* k_scale;       // FP8 / FP4 only
   const float* v_scale;
   float* ws_m;                // [B, n_q, P_max] (partials mode)
   float* ws_l;
@@ -47,10 +47,9 @@ constexpr int kScheduleHeader = 8;
 hipError_t launch_decode_schedule(const int32_t* context_lens, int B, int P, int P_max,
                                   int32_t* sched, hipStream_t stream);
 
-// Partition kernels: matrix-core (default) and vector-ALU variants.
+// Partition kernel (matrix cores, decode_mfma.hip).
 hipError_t launch_decode_partition(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_partition_mfma(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_decode_partition_valu(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_splitk_reduce(void* out, int out_dtype, const float* m, const float* l,
                                 const float* o, const int32_t* context_lens, int B, int n_q,
                                 int d, int P_max, int partition, hipStream_t stream,

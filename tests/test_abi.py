@@ -62,7 +62,6 @@ def _decode(desc, **kw):
     ({}, {"d": 96}, _lib.PKV_ERR_UNSUPPORTED),
     ({}, {"dtype": 7}, _lib.PKV_ERR_UNSUPPORTED),
     ({"n_q": 3}, {}, _lib.PKV_ERR_INVALID_ARG),               # n_q not a multiple of n_kv
-    ({"n_q": 6}, {}, _lib.PKV_ERR_UNSUPPORTED),               # G = 3
     ({"max_ctx": 65}, {}, _lib.PKV_ERR_INVALID_ARG),          # beyond max_blocks * bs
     ({"P": 24}, {}, _lib.PKV_ERR_INVALID_ARG),                # not a multiple of bs
     ({"scale": float("nan")}, {}, _lib.PKV_ERR_INVALID_ARG),

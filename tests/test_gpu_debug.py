@@ -179,3 +179,51 @@ def test_debug_off_reports_nothing(pkv):
     torch.cuda.synchronize()
     pkv.debug_check()                                        # off: always OK
     assert torch.isfinite(out).all()
+
+
+def test_schedule_for_other_geometry_or_items_is_reported(pkv, dbg):
+    # A schedule built for this call is accepted; one built for other lengths
+    # (another item count), another partition size or another batch, or one
+    # whose items name a sequence outside the call, is reported. In normal
+    # mode the kernel reads no item of a list whose header does not match and
+    # skips items outside the call, so these calls stay inside the arrays.
+    w = W.custom("dbg_sched", [40, 700, 300, 1], 16, 2, 128, 16, W.BF16, seed=66)
+    kd, vd, qd, bt, cl, *_ = setup(w)
+    P = 64
+    good = pkv.decode_schedule(cl, 700, P)
+    pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, 700, partition_size=P, schedule=good)
+    torch.cuda.synchronize()
+    assert not reported(pkv)
+
+    other_lens = cl.clone()
+    other_lens[1] = 600                                  # one partition fewer
+    bad_count = pkv.decode_schedule(other_lens, 700, P)
+    other_P = pkv.decode_schedule(cl, 700, 2 * P)        # 11 partitions of 128, not 64
+    bad_items = good.clone()
+    bad_items[8] = 9                                     # first item's sequence: not in the call
+    cases = [("count", bad_count, 700), ("partition", other_P, 700),
+             ("items", bad_items, 700)]
+    for what, sched, max_ctx in cases:
+        print(f"[schedule check] {what}", flush=True)
+        pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, max_ctx, partition_size=P,
+                                   schedule=sched)
+        torch.cuda.synchronize()
+        assert reported(pkv), what
+    # a header recording another batch size
+    half = pkv.decode_schedule(cl[:2].contiguous(), 700, P)
+    pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, 700, partition_size=P,
+                               schedule=torch.cat([half, torch.zeros_like(good)])[:good.numel()])
+    torch.cuda.synchronize()
+    assert reported(pkv), "batch"
+
+    # normal mode: the same calls complete, and a valid one afterwards is unaffected
+    pkv.set_debug(False)
+    for _, sched, max_ctx in cases:
+        pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, max_ctx, partition_size=P,
+                                   schedule=sched)
+    ok = pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, 700, partition_size=P,
+                                    schedule=good)
+    plain = pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, 700, partition_size=P)
+    torch.cuda.synchronize()
+    pkv.set_debug(True)
+    assert torch.allclose(ok, plain, rtol=0, atol=1e-6)

@@ -186,6 +186,13 @@ SHAPES = [
     # NaN codes in the rest of the last block
     ([5, 17, 20, 33, 47, 63], 16, 2, 128, 16, W.FP8, 0),
     ([5, 17, 20, 33, 47, 63], 4, 4, 64, 32, W.FP8, 32),
+    # head groups that are not powers of two: partly filled head tiles, and
+    # (G > 16) a last tile of 4 or 8 heads when a schedule keeps the partition
+    # kernel
+    ([1, 15, 16, 17, 200], 12, 4, 128, 16, W.BF16, 0),   # G = 3
+    ([33, 64, 700], 40, 8, 64, 32, W.BF16, 64),          # G = 5
+    ([40, 97, 600], 48, 2, 128, 32, W.FP8, 64),          # G = 24
+    ([513, 66, 1], 20, 1, 128, 16, W.BF16, 128),         # G = 20, one KV head
 ]
 
 
@@ -370,8 +377,8 @@ def test_schedule_is_every_item_longest_first(pkv, lens, P):
     assert klass == sorted(klass)
 
 
-@pytest.mark.parametrize("case", [SHAPES[i] for i in (2, 3, 4, 5, 7, 10)],
-                         ids=[str(i) for i in (2, 3, 4, 5, 7, 10)])
+@pytest.mark.parametrize("case", [SHAPES[i] for i in (2, 3, 4, 5, 7, 10, 13, 14, 15, 16)],
+                         ids=[str(i) for i in (2, 3, 4, 5, 7, 10, 13, 14, 15, 16)])
 def test_scheduled_decode_matches(pkv, case):
     lens, n_q, n_kv, d, bs, dt, P = case
     w = W.custom("sched", lens, n_q, n_kv, d, bs, dt, seed=40 + SHAPES.index(case))

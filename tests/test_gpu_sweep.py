@@ -1,7 +1,8 @@
 """Seeded random sweep of decode and multi-token-query attention against the
 float64 oracle, through the C ABI.
 
-Each case draws its geometry (head grouping G from 1 to 64, 1 to 8 KV heads,
+Each case draws its geometry (head grouping G from 1 to 64, powers of two
+and others, 1 to 8 KV heads,
 d_head 64 or 128, 16- or 32-token blocks, bf16 / FP8 / FP4 cache), its batch
 (1..8 sequences, lengths 0..1500 with block-boundary and empty ones), its
 split-K partition (library default or a random block multiple) and, for the
@@ -23,7 +24,7 @@ MAX_ABS = {W.BF16: 1e-2, W.FP8: 3e-2, W.FP4: 3e-2}
 REL_L2 = 1e-4
 
 
-def draw_cases(n, seed):
+def draw_cases(n, seed, groups=(1, 2, 4, 8, 16, 32, 64)):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -31,7 +32,7 @@ def draw_cases(n, seed):
         dt = [W.BF16, W.FP8, W.FP4][int(rng.integers(0, 3 if d == 128 else 2))]
         bs = int(rng.choice([16, 32]))
         n_kv = int(rng.choice([1, 2, 4, 8]))
-        G = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+        G = int(rng.choice(groups))
         B = int(rng.integers(1, 9))
         lens = [int(x) for x in rng.integers(1, 1501, size=B)]
         special = [0, 1, bs - 1, bs, bs + 1, 2 * bs]
@@ -48,6 +49,9 @@ def draw_cases(n, seed):
 
 
 CASES = draw_cases(24, 2170)
+# head groups that are not powers of two: partly filled head tiles (decode)
+# and row groups that split a query's heads (multi-query)
+CASES += [(24 + c[0],) + c[1:] for c in draw_cases(12, 2171, (3, 5, 6, 7, 12, 20, 24, 40))]
 
 
 @pytest.fixture(scope="module")
