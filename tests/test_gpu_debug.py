@@ -188,7 +188,7 @@ def test_schedule_for_other_geometry_or_items_is_reported(pkv, dbg):
     # mode the kernel reads no item of a list whose header does not match and
     # skips items outside the call, so these calls stay inside the arrays.
     w = W.custom("dbg_sched", [40, 700, 300, 1], 16, 2, 128, 16, W.BF16, seed=66)
-    kd, vd, qd, bt, cl, *_ = setup(w)
+    kd, vd, qd, bt, cl, kc, vc, q = setup(w)
     P = 64
     good = pkv.decode_schedule(cl, 700, P)
     pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, 700, partition_size=P, schedule=good)
@@ -223,7 +223,10 @@ def test_schedule_for_other_geometry_or_items_is_reported(pkv, dbg):
                                    schedule=sched)
     ok = pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, 700, partition_size=P,
                                     schedule=good)
-    plain = pkv.paged_decode_attention(qd, kd, vd, bt, cl, w.scale, 700, partition_size=P)
     torch.cuda.synchronize()
     pkv.set_debug(True)
-    assert torch.allclose(ok, plain, rtol=0, atol=1e-6)
+    expect = ref.decode_attention(W.bits(q), W.bits(kc), W.bits(vc), w.block_tables,
+                                  w.context_lens, w.scale)
+    got = ok.cpu().double().numpy()
+    assert np.max(np.abs(got - expect)) <= 1e-2
+    assert np.linalg.norm(got - expect) / np.linalg.norm(expect) <= 1e-4
