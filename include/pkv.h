@@ -203,6 +203,42 @@ pkv_status pkv_paged_decode_attention(const pkv_cache_desc* desc, void* out, int
                                       void* stream);
 
 /* ---------------------------------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * pkv_paged_decode_attention_static computes exactly what
+ * pkv_paged_decode_attention computes, with the same kernels and the same
+ * arguments except the workspace: its split-K partials live in a file-scope
+ * device array of PKV_STATIC_SCRATCH_BYTES (64 MiB) that every GPU the
+ * library runs on holds from the loading of the library's code until the
+ * process ends. The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); the caller passes inputs and outputs.
+ *   - A call whose partials, pkv_decode_workspace_bytes(B, n_q, d_head,
+ *     max_context_len, P) for the resolved partition size P, exceed
+ *     PKV_STATIC_SCRATCH_BYTES returns PKV_ERR_WORKSPACE_TOO_SMALL and
+ *     launches nothing; a single-pass call (one partition) uses none.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (each call writes every partial it reads). Calls that
+ *     overlap on one GPU (other streams or threads) race on it: serialise them.
+ *   - Debug mode does not apply to this entry point (its checks allocate a
+ *     flag); the normal-mode memory safety of pkv_paged_decode_attention does.
+ *   - Other errors as for pkv_paged_decode_attention; the first call on a
+ *     device looks up the array's device address (PKV_ERR_HIP if that fails).
+ * ------------------------------------------------------------------------- */
+#define PKV_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+pkv_status pkv_paged_decode_attention_static(const pkv_cache_desc* desc, void* out,
+                                             int32_t out_dtype, const void* q,
+                                             const void* k_cache, const void* v_cache,
+                                             const int32_t* block_tables,
+                                             int32_t max_blocks_per_seq,
+                                             const int32_t* context_lens, int32_t B, int32_t n_q,
+                                             int32_t max_context_len, float scale,
+                                             const float* k_scale, const float* v_scale,
+                                             int32_t partition_size, const void* schedule,
+                                             void* stream);
+
+/* ---------------------------------------------------------------------------
  * The two halves of pkv_paged_decode_attention, callable on their own (for
  * timing each kernel and checking partial statistics).
  *

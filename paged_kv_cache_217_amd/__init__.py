@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     CacheDesc,
     OutOfBlocks,
     PkvError,
+    STATIC_SCRATCH_BYTES,
     cache_desc,
     cascade_decode_attention,
     copy_blocks,
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     make_workspace,
     multi_query_partition_size,
     paged_decode_attention,
+    paged_decode_attention_static,
     paged_decode_partials,
     paged_multi_query_attention,
     partial_views,

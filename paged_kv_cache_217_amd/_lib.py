@@ -65,6 +65,9 @@ SIGNATURES = {
     "pkv_paged_decode_attention": (_i32, [ctypes.POINTER(CacheDesc), _vp, _i32, _vp, _vp, _vp,
                                           _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32,
                                           _vp, _sz, _vp, _vp]),
+    "pkv_paged_decode_attention_static": (_i32, [ctypes.POINTER(CacheDesc), _vp, _i32, _vp, _vp,
+                                                 _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
+                                                 _vp, _vp, _i32, _vp, _vp]),
     "pkv_paged_decode_partials": (_i32, [ctypes.POINTER(CacheDesc), _vp, _vp, _vp, _vp, _i32,
                                          _vp, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _sz,
                                          _vp, _vp]),
@@ -337,6 +340,30 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
         _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, n_q,
         int(max_context_len), float(scale), _ptr(k_scale), _ptr(v_scale), P, _ptr(workspace),
         workspace.numel(), _ptr(schedule), _stream(stream)), "pkv_paged_decode_attention")
+    return out
+
+
+# bytes of the device array pkv_paged_decode_attention_static keeps its
+# partials in (PKV_STATIC_SCRATCH_BYTES in pkv.h)
+STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def paged_decode_attention_static(q, k_cache, v_cache, block_tables, context_lens, scale,
+                                  max_context_len, out, k_scale=None, v_scale=None,
+                                  partition_size=0, schedule=None, stream=None):
+    """paged_decode_attention for callers that cannot allocate: the caller
+    passes `out`, and the split-K partials go to the library's static device
+    array (pkv_paged_decode_attention_static in pkv.h). Nothing is allocated."""
+    desc, B, n_q, d = _decode_common(q, k_cache, v_cache, block_tables, context_lens,
+                                     k_scale, v_scale)
+    _check_out(out, (B, n_q, d), q.device)
+    if schedule is not None:
+        _need(schedule, torch.int32, "schedule")
+    _check(lib().pkv_paged_decode_attention_static(
+        ctypes.byref(desc), _ptr(out), _out_code(out.dtype), _ptr(q), _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, n_q,
+        int(max_context_len), float(scale), _ptr(k_scale), _ptr(v_scale), int(partition_size),
+        _ptr(schedule), _stream(stream)), "pkv_paged_decode_attention_static")
     return out
 
 

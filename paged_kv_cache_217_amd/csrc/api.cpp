@@ -244,6 +244,82 @@ pkv_status prepare_decode(const pkv_cache_desc* desc, const void* q, const void*
 
 }  // namespace
 
+namespace pkv {
+
+// The body of pkv_paged_decode_attention, shared with the entry point whose
+// partials live in a static device array: there `workspace` is resolved by
+// `lookup` only once the arguments are valid and the partials are known to
+// fit in `workspace_bytes`. `debug_checks` false skips the debug-mode checks
+// (which allocate a device flag on first use).
+pkv_status decode_attention(const pkv_cache_desc* desc, void* out, int32_t out_dtype,
+                            const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t B, int32_t n_q,
+                            int32_t max_context_len, float scale, const float* k_scale,
+                            const float* v_scale, int32_t partition_size, void* workspace,
+                            size_t workspace_bytes_, WorkspaceLookup lookup,
+                            const void* schedule, void* stream, bool debug_checks) {
+  DecodeArgs a;
+  pkv_status st = prepare_decode(desc, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                                 context_lens, B, n_q, max_context_len, scale, k_scale, v_scale,
+                                 partition_size, &a);
+  if (st != PKV_OK) return st;
+  if (out_dtype != PKV_FP32 && out_dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  if (!out) return PKV_ERR_INVALID_ARG;
+  st = attach_schedule(&a, schedule);
+  if (st != PKV_OK) return st;
+  if (g_debug && debug_checks) {
+    st = debug_take(as_stream(stream));
+    if (st == PKV_OK)
+      st = debug_tables(as_stream(stream), block_tables, max_blocks_per_seq, context_lens, 0,
+                        max_context_len, nullptr, 0, B, desc);
+    if (st == PKV_OK) st = debug_schedule(as_stream(stream), a);
+    if (st != PKV_OK) return st;
+  }
+  a.out = out;
+  a.out_dtype = out_dtype;
+  // With more than 16 query heads per KV head the partition kernel would run
+  // one workgroup per 16-head tile, each reading the KV head's K/V again. The
+  // multi-query kernel with one query per sequence that sees its whole
+  // context computes the same attention and applies each K/V chunk to two
+  // tiles per wave (a schedule, which only the partition kernel follows,
+  // keeps the partition kernel).
+  const bool on_mq = decode_on_multi_query(n_q / desc->n_kv) && a.schedule == nullptr;
+  if (on_mq) {
+    a.Q = 1;
+    a.non_causal = true;
+  }
+  auto launch = [&]() {
+    return on_mq ? launch_multi_query_partition(a, as_stream(stream))
+                 : launch_decode_partition(a, as_stream(stream));
+  };
+  if (a.P_max == 1) {
+    a.write_partials = false;
+    return from_hip(launch());
+  }
+  const size_t need = workspace_bytes(B, n_q, a.d, a.P_max);
+  if (workspace_bytes_ < need) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  if (lookup) {
+    st = lookup(&workspace);
+    if (st != PKV_OK) return st;
+  }
+  if (!workspace) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(workspace)) return PKV_ERR_INVALID_ARG;
+  const Workspace w = carve(workspace, B, n_q, a.P_max);
+  a.ws_m = w.m;
+  a.ws_l = w.l;
+  a.ws_o = w.o;
+  a.write_partials = true;
+  a.wave_partitions = !on_mq && a.schedule == nullptr && use_wave_partitions(a.partition);
+  hipError_t e = launch();
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  return from_hip(launch_splitk_reduce(out, out_dtype, w.m, w.l, w.o, context_lens, B, n_q, a.d,
+                                       a.P_max, a.partition, as_stream(stream)));
+}
+
+}  // namespace pkv
+
 extern "C" {
 
 const char* pkv_status_string(pkv_status s) {
@@ -333,58 +409,10 @@ pkv_status pkv_paged_decode_attention(const pkv_cache_desc* desc, void* out, int
                                       int32_t partition_size, void* workspace,
                                       size_t workspace_bytes_, const void* schedule,
                                       void* stream) {
-  pkv::DecodeArgs a;
-  pkv_status st = prepare_decode(desc, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
-                                 context_lens, B, n_q, max_context_len, scale, k_scale, v_scale,
-                                 partition_size, &a);
-  if (st != PKV_OK) return st;
-  if (out_dtype != PKV_FP32 && out_dtype != PKV_BF16) return PKV_ERR_INVALID_ARG;
-  if (B == 0) return PKV_OK;
-  if (!out) return PKV_ERR_INVALID_ARG;
-  st = attach_schedule(&a, schedule);
-  if (st != PKV_OK) return st;
-  if (g_debug) {
-    st = debug_take(as_stream(stream));
-    if (st == PKV_OK)
-      st = debug_tables(as_stream(stream), block_tables, max_blocks_per_seq, context_lens, 0,
-                        max_context_len, nullptr, 0, B, desc);
-    if (st == PKV_OK) st = debug_schedule(as_stream(stream), a);
-    if (st != PKV_OK) return st;
-  }
-  a.out = out;
-  a.out_dtype = out_dtype;
-  // With more than 16 query heads per KV head the partition kernel would run
-  // one workgroup per 16-head tile, each reading the KV head's K/V again. The
-  // multi-query kernel with one query per sequence that sees its whole
-  // context computes the same attention and applies each K/V chunk to two
-  // tiles per wave (a schedule, which only the partition kernel follows,
-  // keeps the partition kernel).
-  const bool on_mq = decode_on_multi_query(n_q / desc->n_kv) && a.schedule == nullptr;
-  if (on_mq) {
-    a.Q = 1;
-    a.non_causal = true;
-  }
-  auto launch = [&]() {
-    return on_mq ? pkv::launch_multi_query_partition(a, as_stream(stream))
-                 : pkv::launch_decode_partition(a, as_stream(stream));
-  };
-  if (a.P_max == 1) {
-    a.write_partials = false;
-    return from_hip(launch());
-  }
-  const size_t need = workspace_bytes(B, n_q, a.d, a.P_max);
-  if (!workspace || workspace_bytes_ < need) return PKV_ERR_WORKSPACE_TOO_SMALL;
-  if (!aligned16(workspace)) return PKV_ERR_INVALID_ARG;
-  const Workspace w = carve(workspace, B, n_q, a.P_max);
-  a.ws_m = w.m;
-  a.ws_l = w.l;
-  a.ws_o = w.o;
-  a.write_partials = true;
-  a.wave_partitions = !on_mq && a.schedule == nullptr && use_wave_partitions(a.partition);
-  hipError_t e = launch();
-  if (e != hipSuccess) return PKV_ERR_HIP;
-  return from_hip(pkv::launch_splitk_reduce(out, out_dtype, w.m, w.l, w.o, context_lens, B, n_q,
-                                            a.d, a.P_max, a.partition, as_stream(stream)));
+  return pkv::decode_attention(desc, out, out_dtype, q, k_cache, v_cache, block_tables,
+                               max_blocks_per_seq, context_lens, B, n_q, max_context_len, scale,
+                               k_scale, v_scale, partition_size, workspace, workspace_bytes_,
+                               nullptr, schedule, stream, true);
 }
 
 pkv_status pkv_paged_decode_partials(const pkv_cache_desc* desc, const void* q,

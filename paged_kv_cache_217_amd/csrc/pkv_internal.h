@@ -80,6 +80,20 @@ hipError_t launch_swap_unpack(const pkv_cache_desc& d, void* k_cache, void* v_ca
                               const int32_t* block_ids, int n, const void* staging,
                               hipStream_t stream);
 
+// pkv_paged_decode_attention (validation, launches) on `workspace_bytes` of
+// workspace: `workspace` itself, or, when `lookup` is given, the address it
+// returns, asked for only when a valid call needs partials that fit.
+// debug_checks false leaves out the debug-mode checks.
+using WorkspaceLookup = pkv_status (*)(void** workspace);
+pkv_status decode_attention(const pkv_cache_desc* desc, void* out, int32_t out_dtype,
+                            const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t B, int32_t n_q,
+                            int32_t max_context_len, float scale, const float* k_scale,
+                            const float* v_scale, int32_t partition_size, void* workspace,
+                            size_t workspace_bytes, WorkspaceLookup lookup,
+                            const void* schedule, void* stream, bool debug_checks);
+
 // Whether the decode kernels were built for this (d, bs, G, dtype) combination.
 bool decode_supported(int d, int bs, int G, int kv_dtype);
 

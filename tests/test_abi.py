@@ -93,6 +93,36 @@ def test_schedule_validation_and_sizing():
     assert _decode(_desc(), sched=ctypes.c_void_p(0x1004)) == _lib.PKV_ERR_INVALID_ARG
 
 
+def _decode_static(desc, **kw):
+    fake = ctypes.c_void_p(0x1000)       # aligned, never dereferenced: refused before any launch
+    args = dict(out=fake, out_dtype=_lib.PKV_FP32, q=fake, k=fake, v=fake, bt=fake, mb=4096,
+                cl=fake, B=2, n_q=4, max_ctx=64, scale=0.1, ks=None, vs=None, P=0)
+    args.update(kw)
+    return _lib.lib().pkv_paged_decode_attention_static(
+        ctypes.byref(desc), args["out"], args["out_dtype"], args["q"], args["k"], args["v"],
+        args["bt"], args["mb"], args["cl"], args["B"], args["n_q"], args["max_ctx"],
+        args["scale"], args["ks"], args["vs"], args["P"], None, None)
+
+
+def test_static_entry_point_validates_and_bounds_its_scratch():
+    # The header's constant and the binding's agree
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    assert "#define PKV_STATIC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert pkv.STATIC_SCRATCH_BYTES == 64 << 20
+    L = _lib.lib()
+    # same host validation as pkv_paged_decode_attention, before any device call
+    assert _decode_static(_desc(), n_q=3) == _lib.PKV_ERR_INVALID_ARG
+    assert _decode_static(_desc(bs=8)) == _lib.PKV_ERR_UNSUPPORTED
+    assert _decode_static(_desc(), q=None) == _lib.PKV_ERR_INVALID_ARG
+    assert _decode_static(_desc(), B=0) == _lib.PKV_OK
+    # partials larger than the static array are refused before anything runs:
+    # 64 sequences x 64 heads x 16 partitions of 16 tokens need more than 64 MiB
+    need = L.pkv_decode_workspace_bytes(64, 64, 128, 4096, 16)
+    assert need > pkv.STATIC_SCRATCH_BYTES
+    assert _decode_static(_desc(n_kv=8), B=64, n_q=64, max_ctx=4096, P=16) == \
+        _lib.PKV_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_zero_batch_is_a_no_op():
     assert _decode(_desc(), B=0) == _lib.PKV_OK
 
