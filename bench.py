@@ -75,6 +75,9 @@ def parse():
                          "over whole sequences, reported as cpu_baseline_procs (1 disables it)")
     ap.add_argument("--swap", type=int, default=0, metavar="N",
                     help="measure swapping N sequences of the 70B layer to host memory and back")
+    ap.add_argument("--plain", type=int, default=1,
+                    help="shared-prefix workload: also time plain decode on the same tables "
+                         "(0: the cascade alone, e.g. for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB block copy (for scaling HBM counters) and exit")
     return ap.parse_args()
@@ -482,7 +485,7 @@ def bench_cascade(args, w, pkv, W, np, torch, dev):
                 ev[layer][1].record(stream)
 
     res = {}
-    for cascade in (True, False):
+    for cascade in ((True, False) if args.plain else (True,)):
         for _ in range(args.warmup):
             step(cascade)
         torch.cuda.synchronize()
@@ -518,8 +521,9 @@ def bench_cascade(args, w, pkv, W, np, torch, dev):
                    "suffix_len": [int(slen_np.min()), max_s], "n_q": n_q, "n_kv": n_kv,
                    "d_head": d, "block_size": bs, "layers": layers, "kv_dtype": w.kv_dtype},
         "attention_us_per_layer": {"cascade": round(ms_att * 1000, 1),
-                                   "plain_decode": round(res[False][1] * 1000, 1)},
-        "speedup_vs_plain_decode": round(res[False][1] / ms_att, 2),
+                                   "plain_decode": round(res[False][1] * 1000, 1)
+                                   if False in res else None},
+        "speedup_vs_plain_decode": round(res[False][1] / ms_att, 2) if False in res else None,
         "logical_kv_gbs": round(logical / (ms_att * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": "cascade (prefix pass + suffix partitions + merge)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -114,16 +114,29 @@ int32_t pick_partition(const pkv_cache_desc* d, int32_t B, int32_t n_q, int32_t 
 // Workgroups of a multi-query launch per partition: the LDS kernel takes 128
 // (query, head) rows of a KV head per workgroup, the register kernel 32 (two
 // 16-row tiles) or one tile. A launch that fills a round of the chip this way
-// runs in a single pass: splitting it would only add partials (fp32,
-// d_head + 2 words per row and partition), which for a prompt chunk outweigh
-// the K/V it reads. Fewer workgroups split the context as decode does.
+// needs no split to fill it. On the register kernel it runs in a single pass:
+// splitting would only add partials (fp32, d_head + 2 words per row and
+// partition), which outweigh the K/V it reads. On the LDS kernel a
+// workgroup's time is its compute, proportional to the tokens it attends
+// to, so a batch of different context lengths would end with a tail of its
+// longest sequences; partitions of at most kLdsPartition tokens, dispatched
+// deepest first, spread that work (measured: a 512-token prompt chunk at
+// contexts 4K..64K took 3.33 ms in one pass and 2.98-3.01 ms with partitions
+// of 4096-32768 tokens), at a cost in partials that is small next to the
+// compute. Fewer workgroups split the context as decode does.
+constexpr int32_t kLdsPartition = 16384;
+
 int32_t pick_partition_mq(const pkv_cache_desc* d, int32_t B, int32_t Q, int32_t n_q,
                           int32_t max_ctx) {
   const int64_t rows = static_cast<int64_t>(Q) * (n_q / d->n_kv);
   const int64_t tiles = cdiv(rows, 16);
-  const int64_t per_head = tiles >= 8 ? cdiv(rows, 128) : (tiles >= 2 ? cdiv(tiles, 2) : 1);
+  const bool lds = tiles >= 8;
+  const int64_t per_head = lds ? cdiv(rows, 128) : (tiles >= 2 ? cdiv(tiles, 2) : 1);
   const int64_t units = static_cast<int64_t>(B) * d->n_kv * per_head;
-  if (units >= 512) return static_cast<int32_t>(std::max<int64_t>(32, cdiv(max_ctx, 32) * 32));
+  if (units >= 512) {
+    const int64_t whole = std::max<int64_t>(32, cdiv(max_ctx, 32) * 32);
+    return static_cast<int32_t>(lds ? std::min<int64_t>(whole, kLdsPartition) : whole);
+  }
   return pick_partition_units(units, max_ctx, kv_row_bytes(d));
 }
 

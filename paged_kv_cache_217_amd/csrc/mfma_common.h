@@ -105,6 +105,28 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Two fp32 weights -> their bf16 head (truncation: the upper half of each
+// pattern, so the head as a float is the pattern with its low half cleared)
+// and bf16 tail (the exact remainder p - head, rounded to nearest even). The
+// remainder is below 2^-7 p, so head + tail carries p to about 2^-16
+// relative; both halves are fed to the matrix cores as separate operands.
+struct Bf16Split {
+  uint32_t hi, lo;
+};
+__device__ __forceinline__ Bf16Split split_bf16(float p0, float p1) {
+  const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+  const float r0 = p0 - __uint_as_float(b0 & 0xffff0000u);
+  const float r1 = p1 - __uint_as_float(b1 & 0xffff0000u);
+  return Bf16Split{__builtin_amdgcn_perm(b1, b0, 0x07060302u), pack_bf16(r0, r1)};
+}
+
+// max that propagates NaN (a NaN score of a live token makes the row NaN, as
+// the definition does); gfx950 has it as one instruction for three operands
+// and, unlike fmaxf, it needs no quieting of its inputs first
+__device__ __forceinline__ float vmax(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   uint4 u = make_uint4(a, b, c, d);
   return __builtin_bit_cast(bf16x8_t, u);

@@ -26,6 +26,8 @@
 //    into that XCD's L2 once.
 #include <float.h>
 
+#include <type_traits>
+
 #include "mfma_common.h"
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -200,12 +202,12 @@ void multi_query_lds_mfma(DecodeArgs a) {
     return 16 * (2 * (s >> 3) + (s8 >> 2)) + 4 * g4 + (s8 & 3);
   };
 
-  float m_ref[TPW], m_true[TPW], l[TPW];
+  float m_ref[TPW], m_raw[TPW], l[TPW];
   f32x4_t acc[TPW][NJ];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     m_ref[t] = -INFINITY;
-    m_true[t] = -INFINITY;
+    m_raw[t] = -INFINITY;
     l[t] = 0.0f;
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) acc[t][jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -217,11 +219,15 @@ void multi_query_lds_mfma(DecodeArgs a) {
   const int k_lane = c * LR + 16 * g4;
   const int v_lane = 4 * g4 * LR + VB * c;
   const int v_tr = (4 * g4 + c / 4) * LR + 8 * (c % 4);
-  auto compute = [&](int buf, int ci) {
+  // A step's chunks go through three phases: the scores of every chunk (K Q^T
+  // on the matrix cores, masked), one lazy-rescale check over all of them,
+  // then the weights and P V of each chunk. With the rare rescale branch out
+  // of the way, the weights of one chunk and the P V products of the other
+  // are in one basic block, where the compiler can pair vector instructions
+  // with matrix-core work.
+  auto scores = [&](int buf, int ci, float (&s)[TPW][4 * NRG]) {
     const uint8_t* kl_ = sk[buf];
-    const uint8_t* vl_ = sv[buf];
     const int tok0 = t0 + ci * CT;
-    float s[TPW][4 * NRG];
     // K Q^T for every (row group, tile): kk outermost so that the NRG x TPW
     // accumulation chains interleave
     f32x4_t sc[NRG][TPW];
@@ -272,24 +278,48 @@ void multi_query_lds_mfma(DecodeArgs a) {
             if (tok0 + 16 * rg + 4 * g4 + i >= lim) s[t][4 * rg + i] = -INFINITY;
       }
     }
-    float m_use[TPW];
+  };
+
+  // Lazy rescaling, checked per lane: the row's reference m_ref only has to
+  // stay within 2^8 of every weight, so each lane compares the largest of its
+  // own scores (of all the step's chunks) with it, and the row maximum (a
+  // cross-lane reduction) is taken only in the rare step where some lane
+  // exceeds it. The true maximum is kept per lane (raw q . k units) and
+  // reduced once at the end.
+  auto rescale = [&](auto NC, float (&s)[decltype(NC)::value][TPW][4 * NRG]) {
+    constexpr int N = decltype(NC)::value;
+    float lmax[TPW];
+    bool need_any = false;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      float mx = s[t][0];
+      float mx = s[0][t][0];
 #pragma unroll
-      for (int i = 1; i < 4 * NRG; ++i) mx = fmaxf(mx, s[t][i]);
-      mx = max_xor32(max_xor16(mx)) * qscale;          // base-2 units
-      m_true[t] = fmaxf(m_true[t], mx);
-      const bool need = mx > m_ref[t] + kLazyRescale;
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      for (int n = 0; n < N; ++n)
+#pragma unroll
+        for (int i = (n == 0 ? 1 : 0); i < 4 * NRG; ++i) mx = vmax(mx, s[n][t][i]);
+      lmax[t] = mx;
+      m_raw[t] = vmax(m_raw[t], mx);
+      need_any |= mx * qscale > m_ref[t] + kLazyRescale;
+    }
+    if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const float mx = max_xor32(max_xor16(lmax[t])) * qscale;   // the row's, base-2 units
+        const bool need = mx > m_ref[t] + kLazyRescale;
         const float alpha = need ? fast_exp2(m_ref[t] - mx) : 1.0f;
         if (need) m_ref[t] = mx;
         l[t] *= alpha;
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj) acc[t][jj] *= alpha;
       }
-      m_use[t] = m_ref[t] == -INFINITY ? 0.0f : m_ref[t];
     }
+  };
+
+  auto accumulate = [&](int buf, const float (&s)[TPW][4 * NRG]) {
+    const uint8_t* vl_ = sv[buf];
+    float m_use[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) m_use[t] = m_ref[t] == -INFINITY ? 0.0f : m_ref[t];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       bf16x8_t pop_hi[TPW], pop_lo[TPW];
@@ -304,10 +334,9 @@ void multi_query_lds_mfma(DecodeArgs a) {
         uint32_t ph[4], pl[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          ph[u] = pack_bf16(p[2 * u], p[2 * u + 1]);
-          float h0f, h1f;
-          bf16x2_to_f32(ph[u], h0f, h1f);
-          pl[u] = pack_bf16(p[2 * u] - h0f, p[2 * u + 1] - h1f);
+          const Bf16Split sp = split_bf16(p[2 * u], p[2 * u + 1]);
+          ph[u] = sp.hi;
+          pl[u] = sp.lo;
         }
         pop_hi[t] = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
         pop_lo[t] = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
@@ -389,8 +418,24 @@ void multi_query_lds_mfma(DecodeArgs a) {
       const bool more = ci + 2 < n_ch;
       if (more) fetch(sa, ci + 2);
       if (ci + 3 < n_ch) fetch(sb, ci + 3);
-      compute(2 * h, ci);
-      if (ci + 1 < n_ch) compute(2 * h + 1, ci + 1);
+      const bool two = ci + 1 < n_ch;
+      float sa_[1][TPW][4 * NRG], sb_[1][TPW][4 * NRG];
+      scores(2 * h, ci, sa_[0]);
+      rescale(std::integral_constant<int, 1>{}, sa_);
+      if constexpr (FMT == kFmtBf16) {
+        // the second chunk's scores are issued beside the first chunk's
+        // weights and P V products (one basic block); quantised chunks are
+        // twice as long, and their score registers would not fit twice
+        if (two) scores(2 * h + 1, ci + 1, sb_[0]);
+        accumulate(2 * h, sa_[0]);
+      } else {
+        accumulate(2 * h, sa_[0]);
+        if (two) scores(2 * h + 1, ci + 1, sb_[0]);
+      }
+      if (two) {
+        rescale(std::integral_constant<int, 1>{}, sb_);
+        accumulate(2 * h + 1, sb_[0]);
+      }
       if (more) commit(sa, 2 * (h ^ 1), ci + 2);
       if (ci + 3 < n_ch) commit(sb, 2 * (h ^ 1) + 1, ci + 3);
       __syncthreads();
@@ -407,7 +452,8 @@ void multi_query_lds_mfma(DecodeArgs a) {
   for (int t = 0; t < TPW; ++t) {
     float lt = l[t];
     lt = sum_xor32(sum_xor16(lt));
-    const float f = m_true[t] == -INFINITY ? 0.0f : fast_exp2(m_ref[t] - m_true[t]);
+    const float m_true = max_xor32(max_xor16(m_raw[t])) * qscale;   // the row's true maximum
+    const float f = m_true == -INFINITY ? 0.0f : fast_exp2(m_ref[t] - m_true);
     const float L = lt * f;
     const int rr = wrow0 + 16 * t + c;
     if (rr >= rows) continue;
@@ -418,7 +464,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
     if (a.write_partials) {
       const int64_t mi = orow * a.P_max + j;
       if (g4 == 0) {
-        a.ws_m[mi] = m_true[t];
+        a.ws_m[mi] = m_true;
         a.ws_l[mi] = live ? L : 0.0f;
       }
 #pragma unroll
