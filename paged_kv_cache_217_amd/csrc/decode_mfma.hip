@@ -119,10 +119,13 @@ void decode_partition_mfma(DecodeArgs a) {
   if (a.schedule != nullptr) {
     const int hxn = a.n_kv * tiles;
     const int item = blockIdx.x / hxn;
-    // a list built for another geometry is not followed (and its items may lie
-    // past the caller's buffer)
-    if (a.schedule[1] != a.partition || a.schedule[2] != a.B || a.schedule[3] != a.P_max) return;
-    if (item >= a.schedule[0]) return;                 // past the list: nothing to do
+    // A list built for another geometry is not followed (and its items may lie
+    // past the caller's buffer). The header is read whole and tested without
+    // short-circuits, so its words arrive in one round trip.
+    const int2 h01 = reinterpret_cast<const int2*>(a.schedule)[0];
+    const int2 h23 = reinterpret_cast<const int2*>(a.schedule)[1];
+    const bool stale = (h01.y != a.partition) | (h23.x != a.B) | (h23.y != a.P_max);
+    if (stale | (item >= h01.x)) return;               // or past the list: nothing to do
     const int2 it = reinterpret_cast<const int2*>(a.schedule + kScheduleHeader)[item];
     if (it.x < 0 || it.x >= a.B || it.y < 0 || it.y >= a.P_max) return;
     hx = blockIdx.x % hxn;
@@ -172,20 +175,31 @@ void decode_partition_mfma(DecodeArgs a) {
     return FP8 ? 64 * (kk >> 1) + 16 * g4 + 8 * (kk & 1) : 32 * kk + 8 * g4;
   };
 
+  // Scores and the softmax reference stay in raw q . k units; the weight of a
+  // score s is 2^((s - m) qscale), so the largest score's weight is exactly 1
+  // (a one-token context returns V exactly). That needs qscale > 0, so that
+  // the maximum of the raw scores is that of the scaled ones: a negative
+  // product is made positive by negating Q (exact in bf16), a zero one by
+  // zeroing Q (every score is then 0, as 0 . q . k would be).
+  float qscale = a.scale * kLog2e;
+  if constexpr (QNT) qscale *= a.k_scale[g];
+  const uint32_t qflip = qscale < 0.0f ? 0x80008000u : 0u;
+  const bool qzero = qscale == 0.0f;
+  qscale = qzero ? 1.0f : fabsf(qscale);
+
   // Q^T operand: lane (c, g4) holds q[h0 + c][dimbase(kk) .. +8] for each kk
   bf16x8_t qop[NKK];
   {
-    const bool live = c < nh;
-    const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * a.n_q + h0 + (live ? c : 0)) * D;
+    const bool live = c < nh && !qzero;
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * a.n_q + h0 + (c < nh ? c : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       uint4 w = *reinterpret_cast<const uint4*>(qrow + dimbase(kk));
+      w = make_uint4(w.x ^ qflip, w.y ^ qflip, w.z ^ qflip, w.w ^ qflip);
       if (!live) w = make_uint4(0, 0, 0, 0);
       qop[kk] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
-  float qscale = a.scale * kLog2e;
-  if constexpr (QNT) qscale *= a.k_scale[g];
 
   const int64_t tile_bytes = FP4 ? static_cast<int64_t>(BS) * RB : static_cast<int64_t>(BS) * D * EB;
   const int64_t head_off = static_cast<int64_t>(g) * tile_bytes;
@@ -236,8 +250,9 @@ void decode_partition_mfma(DecodeArgs a) {
     }
   };
 
-  float m_ref = -INFINITY;      // reference max of this lane's head (base-2 units)
-  float m_true = -INFINITY;
+  float m_ref = -INFINITY;      // reference max of this lane's head (raw q . k units)
+  float m_raw = -INFINITY;      // largest of this lane's own scores
+  const float thr = kLazyRescale / qscale;   // the rescale threshold in raw units
   float l = 0.0f;               // this lane's share of the row sum
   f32x4_t acc[NJ];
 #pragma unroll
@@ -272,7 +287,7 @@ void decode_partition_mfma(DecodeArgs a) {
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[kk], sc, 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[4 * r + i] = sc[i] * qscale;
+      for (int i = 0; i < 4; ++i) s[4 * r + i] = sc[i];
     }
     if (tok0 + CT > t1) {                              // only the partition's last chunk
 #pragma unroll
@@ -284,21 +299,25 @@ void decode_partition_mfma(DecodeArgs a) {
       for (int si = sub * 8 * KSS; si < (sub + 1) * 8 * KSS; ++si)
         if (tok0 + v_tok(si) >= t1) ch.v[si] = VT{};
     }
-    // ---- online softmax for head c (shared by the 4 k-group lanes)
-    float mx = s[0];
+    // ---- online softmax for head c (shared by the 4 k-group lanes). Lazy
+    // rescaling, checked per lane: the head's reference m_ref only has to stay
+    // within 2^8 of every weight, so each lane compares its own largest score
+    // with it, and the head's maximum (a cross-lane reduction) is taken only
+    // in the rare chunk where some lane exceeds it.
+    float lm = s[0];
 #pragma unroll
-    for (int i = 1; i < 4 * RGS; ++i) mx = fmaxf(mx, s[i]);
-    mx = max_xor32(max_xor16(mx));
-    m_true = fmaxf(m_true, mx);
-    const bool need = mx > m_ref + kLazyRescale;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float m_new = need ? mx : m_ref;
-      const float alpha = fast_exp2(m_ref - m_new);
+    for (int i = 1; i < 4 * RGS; ++i) lm = vmax(lm, s[i]);
+    m_raw = vmax(m_raw, lm);
+    if (__builtin_amdgcn_ballot_w64(lm > m_ref + thr) != 0) {
+      const float mx = max_xor32(max_xor16(lm));       // the head's maximum
+      const bool need = mx > m_ref + thr;
+      const float alpha = need ? fast_exp2((m_ref - mx) * qscale) : 1.0f;
+      if (need) m_ref = mx;
       l *= alpha;
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) acc[jj] *= alpha;
-      m_ref = m_new;
     }
+    const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
 #pragma unroll
     for (int kq = 0; kq < KSS; ++kq) {
       const int ks = sub * KSS + kq;
@@ -306,17 +325,18 @@ void decode_partition_mfma(DecodeArgs a) {
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = fast_exp2(s[8 * kq + i] - m_ref);
+        p[i] = fast_exp2((s[8 * kq + i] - m_use) * qscale);
         l += p[i];
       }
       uint32_t ph[4], pl[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        ph[t] = pack_bf16(p[2 * t], p[2 * t + 1]);
         if constexpr (SPLIT_P) {
-          float h0f, h1f;
-          bf16x2_to_f32(ph[t], h0f, h1f);
-          pl[t] = pack_bf16(p[2 * t] - h0f, p[2 * t + 1] - h1f);
+          const Bf16Split sp = split_bf16(p[2 * t], p[2 * t + 1]);
+          ph[t] = sp.hi;
+          pl[t] = sp.lo;
+        } else {
+          ph[t] = pack_bf16(p[2 * t], p[2 * t + 1]);
         }
       }
       const bf16x8_t pop_hi = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
@@ -400,10 +420,11 @@ void decode_partition_mfma(DecodeArgs a) {
 
   // ---- wave totals for head c, rebased on the true max
   l = sum_xor32(sum_xor16(l));
-  const float f = m_true == -INFINITY ? 0.0f : fast_exp2(m_ref - m_true);
+  const float m_true = max_xor32(max_xor16(m_raw));
+  const float f = m_true == -INFINITY ? 0.0f : fast_exp2((m_ref - m_true) * qscale);
   l *= f;
   if (g4 == 0) {
-    sm_m[wave][c] = m_true;
+    sm_m[wave][c] = m_true * qscale;                  // base-2 units
     sm_l[wave][c] = l;
   }
 #pragma unroll

@@ -105,19 +105,22 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Two fp32 weights -> their bf16 head (truncation: the upper half of each
-// pattern, so the head as a float is the pattern with its low half cleared)
-// and bf16 tail (the exact remainder p - head, rounded to nearest even). The
-// remainder is below 2^-7 p, so head + tail carries p to about 2^-16
+// Two fp32 weights -> their bf16 heads (round to nearest even, packed) and
+// bf16 tails (the exact remainders p - head, rounded the same way). The
+// remainder is at most 2^-9 p, so head + tail carries p to about 2^-18
 // relative; both halves are fed to the matrix cores as separate operands.
+// The heads are widened back from the packed word itself (a shift and a
+// mask); the empty asm hides the word's origin, without which the compiler
+// converts the first weight a second time to get the low half.
 struct Bf16Split {
   uint32_t hi, lo;
 };
 __device__ __forceinline__ Bf16Split split_bf16(float p0, float p1) {
-  const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
-  const float r0 = p0 - __uint_as_float(b0 & 0xffff0000u);
-  const float r1 = p1 - __uint_as_float(b1 & 0xffff0000u);
-  return Bf16Split{__builtin_amdgcn_perm(b1, b0, 0x07060302u), pack_bf16(r0, r1)};
+  uint32_t hi = pack_bf16(p0, p1);
+  asm("" : "+v"(hi));
+  const float r0 = p0 - __uint_as_float(hi << 16);
+  const float r1 = p1 - __uint_as_float(hi & 0xffff0000u);
+  return Bf16Split{hi, pack_bf16(r0, r1)};
 }
 
 // max that propagates NaN (a NaN score of a live token makes the row NaN, as

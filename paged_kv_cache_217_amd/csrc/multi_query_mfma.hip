@@ -132,6 +132,17 @@ void multi_query_partition_mfma(DecodeArgs a) {
     if constexpr (FP4) return 32 * g4 + 8 * kk;
     return FP8 ? 64 * (kk >> 1) + 16 * g4 + 8 * (kk & 1) : 32 * kk + 8 * g4;
   };
+  // Scores and the softmax reference stay in raw q . k units; the weight of a
+  // score s is 2^((s - m) qscale), so a row's largest score weighs exactly 1,
+  // as in the decode kernel. That needs qscale > 0, so that the row maximum of
+  // the raw scores is that of the scaled ones: a negative product is made
+  // positive by negating Q (exact in bf16), a zero one by zeroing Q (every
+  // score is then 0, as 0 . q . k would be).
+  float qscale = a.scale * kLog2e;
+  if constexpr (QNT) qscale *= a.k_scale[g];
+  const uint32_t qflip = qscale < 0.0f ? 0x80008000u : 0u;
+  const bool qzero = qscale == 0.0f;
+  qscale = qzero ? 1.0f : fabsf(qscale);
   bf16x8_t qop[QLDS ? 1 : TPW][NKK];
   int pos[TPW];
 #pragma unroll
@@ -146,10 +157,12 @@ void multi_query_partition_mfma(DecodeArgs a) {
       const int col = 8 * (e % (D / 8));
       const int row = row0 + r;
       uint4 w = make_uint4(0, 0, 0, 0);
-      if (row < rows && row / G < ql)
+      if (row < rows && row / G < ql && !qzero) {
         w = *reinterpret_cast<const uint4*>(
             a.q + ((static_cast<int64_t>(b) * a.Q + row / G) * a.n_q + g * G + row % G) * D +
             col);
+        w = make_uint4(w.x ^ qflip, w.y ^ qflip, w.z ^ qflip, w.w ^ qflip);
+      }
       *reinterpret_cast<uint4*>(&sm_q[r][col]) = w;
     }
     __syncthreads();
@@ -158,12 +171,13 @@ void multi_query_partition_mfma(DecodeArgs a) {
     for (int t = 0; t < TPW; ++t) {
       const int row = wrow0 + 16 * t + c;
       const int qi = row / G;
-      const bool live_row = row < rows && qi < ql;
+      const bool live_row = row < rows && qi < ql && !qzero;
       const int64_t qrow =
           live_row ? (static_cast<int64_t>(b) * a.Q + qi) * a.n_q + g * G + row % G : 0;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         uint4 w = *reinterpret_cast<const uint4*>(a.q + qrow * D + dimbase(kk));
+        w = make_uint4(w.x ^ qflip, w.y ^ qflip, w.z ^ qflip, w.w ^ qflip);
         if (!live_row) w = make_uint4(0, 0, 0, 0);
         qop[t][kk] = __builtin_bit_cast(bf16x8_t, w);
       }
@@ -180,8 +194,6 @@ void multi_query_partition_mfma(DecodeArgs a) {
           bf16x8_t, *reinterpret_cast<const uint4*>(base + 2 * dimbase(kk) + salt));
     }
   };
-  float qscale = a.scale * kLog2e;
-  if constexpr (QNT) qscale *= a.k_scale[g];
 
   const int64_t tile_bytes = static_cast<int64_t>(BS) * RB;
   const int64_t head_off = static_cast<int64_t>(g) * tile_bytes;
@@ -238,12 +250,13 @@ void multi_query_partition_mfma(DecodeArgs a) {
     }
   };
 
-  float m_ref[TPW], m_true[TPW], l[TPW];
+  float m_ref[TPW], m_raw[TPW], l[TPW];     // reference and own maximum in raw units
+  const float thr = kLazyRescale / qscale;   // the rescale threshold in raw units
   f32x4_t acc[TPW][NJ];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     m_ref[t] = -INFINITY;
-    m_true[t] = -INFINITY;
+    m_raw[t] = -INFINITY;
     l[t] = 0.0f;
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) acc[t][jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -293,7 +306,7 @@ void multi_query_partition_mfma(DecodeArgs a) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[t][4 * rg + i] = sc[rg][t][i] * qscale;
+        for (int i = 0; i < 4; ++i) s[t][4 * rg + i] = sc[rg][t][i];
     if (tok0 + CT > min(p_lo + 1, t1)) {
       // causal: each row sees tokens up to its own position, and nothing past
       // the partition's end (such slots were not loaded)
@@ -317,26 +330,37 @@ void multi_query_partition_mfma(DecodeArgs a) {
       for (int si = 0; si < NVS; ++si)
         if (tok0 + v_tok(si) >= t1) vc.v[si] = VT{};
     }
-    float m_use[TPW];
+    // Lazy rescaling, checked per lane: a row's reference m_ref only has to
+    // stay within 2^8 of every weight, so each lane compares its own largest
+    // score with it, and the row maximum (a cross-lane reduction) is taken
+    // only in the rare chunk where some lane exceeds it. A row may see none
+    // of a chunk's tokens (all -inf): it keeps its state.
+    float lmax[TPW];
+    bool need_any = false;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       float mx = s[t][0];
 #pragma unroll
-      for (int i = 1; i < 4 * NRG; ++i) mx = fmaxf(mx, s[t][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      m_true[t] = fmaxf(m_true[t], mx);
-      // a row may see none of a chunk's tokens (all -inf): it keeps its state
-      const bool need = mx > m_ref[t] + kLazyRescale;
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        const float alpha = need ? fast_exp2(m_ref[t] - mx) : 1.0f;
+      for (int i = 1; i < 4 * NRG; ++i) mx = vmax(mx, s[t][i]);
+      lmax[t] = mx;
+      m_raw[t] = vmax(m_raw[t], mx);
+      need_any |= mx > m_ref[t] + thr;
+    }
+    if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const float mx = max_xor32(max_xor16(lmax[t]));   // the row's maximum
+        const bool need = mx > m_ref[t] + thr;
+        const float alpha = need ? fast_exp2((m_ref[t] - mx) * qscale) : 1.0f;
         if (need) m_ref[t] = mx;
         l[t] *= alpha;
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj) acc[t][jj] *= alpha;
       }
-      m_use[t] = m_ref[t] == -INFINITY ? 0.0f : m_ref[t];
     }
+    float m_use[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) m_use[t] = m_ref[t] == -INFINITY ? 0.0f : m_ref[t];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       bf16x8_t pop_hi[TPW], pop_lo[TPW];
@@ -345,16 +369,15 @@ void multi_query_partition_mfma(DecodeArgs a) {
         float p[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          p[i] = fast_exp2(s[t][8 * ks + i] - m_use[t]);
+          p[i] = fast_exp2((s[t][8 * ks + i] - m_use[t]) * qscale);
           l[t] += p[i];
         }
         uint32_t ph[4], pl[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          ph[u] = pack_bf16(p[2 * u], p[2 * u + 1]);
-          float h0f, h1f;
-          bf16x2_to_f32(ph[u], h0f, h1f);
-          pl[u] = pack_bf16(p[2 * u] - h0f, p[2 * u + 1] - h1f);
+          const Bf16Split sp = split_bf16(p[2 * u], p[2 * u + 1]);
+          ph[u] = sp.hi;
+          pl[u] = sp.lo;
         }
         pop_hi[t] = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
         pop_lo[t] = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
@@ -430,9 +453,10 @@ void multi_query_partition_mfma(DecodeArgs a) {
     float lt = l[t];
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
-    const float f = m_true[t] == -INFINITY ? 0.0f : fast_exp2(m_ref[t] - m_true[t]);
+    const float m_true = max_xor32(max_xor16(m_raw[t]));   // the row's true maximum
+    const float f = m_true == -INFINITY ? 0.0f : fast_exp2((m_ref[t] - m_true) * qscale);
     if (g4 == 0) {
-      sm_m[wave][16 * t + c] = m_true[t];
+      sm_m[wave][16 * t + c] = m_true * qscale;           // base-2 units
       sm_l[wave][16 * t + c] = lt * f;
     }
 #pragma unroll
