@@ -75,6 +75,8 @@ def parse():
                          "over whole sequences, reported as cpu_baseline_procs (1 disables it)")
     ap.add_argument("--swap", type=int, default=0, metavar="N",
                     help="measure swapping N sequences of the 70B layer to host memory and back")
+    ap.add_argument("--prefix-partition", type=int, default=0,
+                    help="shared-prefix workload: prefix partition size (0: library)")
     ap.add_argument("--plain", type=int, default=1,
                     help="shared-prefix workload: also time plain decode on the same tables "
                          "(0: the cascade alone, e.g. for counter runs)")
@@ -459,8 +461,8 @@ def bench_cascade(args, w, pkv, W, np, torch, dev):
     desc = pkv.cache_desc(caches[0][0])
     import ctypes
     cws = torch.empty(max(16, pkv.lib().pkv_cascade_workspace_bytes(
-        ctypes.byref(desc), B, n_q, plen, 0, max_s, args.partition)), dtype=torch.uint8,
-        device=dev)
+        ctypes.byref(desc), B, n_q, plen, args.prefix_partition, max_s, args.partition)),
+        dtype=torch.uint8, device=dev)
     P = pkv.default_partition_size(caches[0][0], B, n_q, max_ctx)
     dws, _ = pkv.make_workspace(caches[0][0], B, n_q, max_ctx, P)
     stream = torch.cuda.current_stream()
@@ -476,6 +478,7 @@ def bench_cascade(args, w, pkv, W, np, torch, dev):
                 ev[layer][0].record(stream)
             if cascade:
                 pkv.cascade_decode_attention(q[layer], kc, vc, pt, plen, st, slen, w.scale, max_s,
+                                             prefix_partition=args.prefix_partition,
                                              suffix_partition=args.partition, out=out,
                                              workspace=cws)
             else:
