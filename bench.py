@@ -38,6 +38,15 @@ KERNEL_SOURCES = ["paged_kv_cache_217_amd/csrc/decode_mfma.hip",
                   "paged_kv_cache_217_amd/csrc/pkv_device.h",
                   "paged_kv_cache_217_amd/csrc/pkv_internal.h"]
 MQ_COUNTERS = os.path.join(ROOT, "profiles", "multi_query_counters.json")
+CASCADE_COUNTERS = os.path.join(ROOT, "profiles", "cascade_counters.json")
+CASCADE_KERNEL_SOURCES = ["paged_kv_cache_217_amd/csrc/decode_mfma.hip",
+                          "paged_kv_cache_217_amd/csrc/multi_query_lds.hip",
+                          "paged_kv_cache_217_amd/csrc/decode_attention.hip",
+                          "paged_kv_cache_217_amd/csrc/schedule.hip",
+                          "paged_kv_cache_217_amd/csrc/api.cpp",
+                          "paged_kv_cache_217_amd/csrc/mfma_common.h",
+                          "paged_kv_cache_217_amd/csrc/pkv_device.h",
+                          "paged_kv_cache_217_amd/csrc/pkv_internal.h"]
 MQ_KERNEL_SOURCES = ["paged_kv_cache_217_amd/csrc/multi_query_mfma.hip",
                      "paged_kv_cache_217_amd/csrc/multi_query_lds.hip",
                      "paged_kv_cache_217_amd/csrc/mfma_common.h",
@@ -305,6 +314,12 @@ def run(args, w, pool, np, torch, W):
     # ---------------------------------------------------------------- oracle on the CPU
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, caches[0], q[0], args.cpu_seconds)
+        if layers > 1:
+            # the oracle's time for one whole step at the measured rate: layer 0
+            # only was sampled, so this is extrapolated to every layer
+            cb = result["cpu_baseline"]
+            cb["step_seconds_extrapolated"] = round(kv_bytes_layer * layers / (cb["value"] * 1e9), 1)
+            cb["extrapolation"] = f"rate on layer 0 x {layers} layers"
         if pool is not None:
             try:
                 result["cpu_baseline_procs"] = cpu_baseline_procs(
@@ -323,8 +338,6 @@ def counter_traffic(name, P):
     c = json.load(open(COUNTERS))
     if c.get("kernel_hash") != kernel_hash():
         return None
-    if c.get("workload") == name and c.get("partition") == P:
-        return c.get("traffic_bytes_per_launch")
     e = c.get("workloads", {}).get(name, {})
     return e.get("traffic_bytes_per_launch") if e.get("partition") == P else None
 
@@ -533,6 +546,15 @@ def bench_cascade(args, w, pkv, W, np, torch, dev):
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": att_bytes,
                      "traffic": None},
     }
+    # HBM bytes of one call (all its launches), from the committed counters,
+    # while the sources they were taken on are unchanged and the call is the
+    # library's default one
+    if os.path.exists(CASCADE_COUNTERS) and not args.partition and not args.prefix_partition:
+        c = json.load(open(CASCADE_COUNTERS))
+        if c.get("kernel_hash") == kernel_hash(CASCADE_KERNEL_SOURCES):
+            t = c["traffic_bytes_per_call"]
+            result["roofline"].update(traffic=t["total"], traffic_read=t["read"],
+                                      traffic_written=t["written"])
     print(json.dumps(result), flush=True)
 
 

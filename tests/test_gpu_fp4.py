@@ -114,9 +114,9 @@ def test_fp4_decode_shapes(pkv, case):
 
 
 def test_fp4_decode_query_dynamic_range(pkv):
-    # the FP4 K.Q^T path splits each head's query into two E4M3 terms under a
-    # per-head power of two; elements far below the head's largest, zeros and
-    # negative zeros must still give the oracle's result
+    # FP4 K is widened exactly to bf16 and multiplied with the bf16 query as
+    # given: query elements over a wide range of magnitudes (far below the
+    # head's largest, zeros, negative zeros) must give the oracle's result
     w = W.custom("fp4q", [700, 33, 2048], 64, 8, 128, 32, W.FP4, seed=135)
     kc, vc, ks, vs = W.make_cache(w)
     g = torch.Generator().manual_seed(136)
