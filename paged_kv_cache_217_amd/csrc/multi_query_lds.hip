@@ -56,9 +56,14 @@ void multi_query_lds_mfma(DecodeArgs a) {
   using VT = typename Vec<VB>::T;
   constexpr int VW = (DPL * 2) / 4;           // bf16 words per V slice
   static_assert(!FP4 || D == 128, "FP4 is built for d = 128");
-  constexpr int LR = RB + 16;                 // padded LDS row
+  constexpr int LR = RB + 16;                 // padded LDS row of K
+  // padded LDS row of V: bf16 V is read transposed, 4 rows of 32 bytes per
+  // 16 lanes, which a 32-byte pad puts on 32 different banks (a 16-byte pad
+  // overlaps consecutive rows by 4 banks)
+  constexpr int LRV = FMT == kFmtBf16 ? RB + 32 : LR;
   constexpr int CB = CT * RB;                 // bytes of K (or V) per chunk
-  constexpr int LB = CT * LR;                 // LDS bytes of K (or V) per chunk
+  constexpr int LB = CT * LR;                 // LDS bytes of K per chunk
+  constexpr int LBV = CT * LRV;               // LDS bytes of V per chunk
   constexpr int TB = BS * RB;                 // bytes of one (block, head) tile
   constexpr int PIECES = CB / (16 * 256);     // 16-byte pieces per thread
   static_assert(PIECES >= 1 && CB % (16 * 256) == 0, "chunk must split into thread pieces");
@@ -155,7 +160,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
   }
 
   __shared__ __align__(16) uint8_t sk[4][LB];
-  __shared__ __align__(16) uint8_t sv[4][LB];
+  __shared__ __align__(16) uint8_t sv[4][LBV];
 
   // chunk ci into registers: piece e = threadIdx + 256 k is bytes
   // [16 e, 16 e + 16) of the chunk; a wave's 64 pieces lie in one tile
@@ -191,9 +196,9 @@ void multi_query_lds_mfma(DecodeArgs a) {
     for (int k = 0; k < PIECES; ++k) {
       const int e = threadIdx.x + 256 * k;
       if (tok0 + CT > t1 && tok0 + (16 * e) / RB >= t1) st.v[k] = make_uint4(0, 0, 0, 0);
-      const int at = (16 * e) / RB * LR + (16 * e) % RB;
-      *reinterpret_cast<uint4*>(&sk[buf][at]) = st.k[k];
-      *reinterpret_cast<uint4*>(&sv[buf][at]) = st.v[k];
+      const int row = (16 * e) / RB, col = (16 * e) % RB;
+      *reinterpret_cast<uint4*>(&sk[buf][row * LR + col]) = st.k[k];
+      *reinterpret_cast<uint4*>(&sv[buf][row * LRV + col]) = st.v[k];
     }
   };
 
@@ -217,8 +222,8 @@ void multi_query_lds_mfma(DecodeArgs a) {
   // dims DPL c (FP8, FP4); bf16 V is read transposed: lane (c, g4) addresses
   // token 4 g4 + c / 4, dims 4 (c % 4) .. of a 16-dim column block
   const int k_lane = c * LR + 16 * g4;
-  const int v_lane = 4 * g4 * LR + VB * c;
-  const int v_tr = (4 * g4 + c / 4) * LR + 8 * (c % 4);
+  const int v_lane = 4 * g4 * LRV + VB * c;
+  const int v_tr = (4 * g4 + c / 4) * LRV + 8 * (c % 4);
   // A step's chunks go through three phases: the scores of every chunk (K Q^T
   // on the matrix cores, masked), one lazy-rescale check over all of them,
   // then the weights and P V of each chunk. With the rare rescale branch out
@@ -346,9 +351,9 @@ void multi_query_lds_mfma(DecodeArgs a) {
         // 16 + 4 g4 .. (second half) of the k-step, straight from LDS
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj) {
-          const uint8_t* vt = vl_ + v_tr + 32 * ks * LR + 32 * jj;
+          const uint8_t* vt = vl_ + v_tr + 32 * ks * LRV + 32 * jj;
           const uint2 v0 = lds_read_tr16(vt);
-          const uint2 v1 = lds_read_tr16(vt + 16 * LR);
+          const uint2 v1 = lds_read_tr16(vt + 16 * LRV);
           const bf16x8_t vop = as_bf16x8(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
           for (int t = 0; t < TPW; ++t) {
@@ -365,7 +370,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
 #pragma unroll
         for (int si = 0; si < 8; ++si) {
           const int tv = v_tok(8 * ks + si);
-          vraw[si] = *reinterpret_cast<const VT*>(vl_ + v_lane + (tv - 4 * g4) * LR);
+          vraw[si] = *reinterpret_cast<const VT*>(vl_ + v_lane + (tv - 4 * g4) * LRV);
           if constexpr (FP4) {
             if (si % 2 == 1) vp[si / 2] = fp4_interleave(word(vraw[si - 1], 0), word(vraw[si], 0));
           } else {
