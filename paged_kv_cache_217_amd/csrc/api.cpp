@@ -112,8 +112,10 @@ int32_t pick_partition(const pkv_cache_desc* d, int32_t B, int32_t n_q, int32_t 
 }
 
 // Workgroups of a multi-query launch per partition: the LDS kernel takes 128
-// (query, head) rows of a KV head per workgroup, the register kernel 32 (two
-// 16-row tiles) or one tile. A launch that fills a round of the chip this way
+// (query, head) rows of a KV head per workgroup (its bf16 ping-pong form 256,
+// at one workgroup per CU instead of two: the same share of a round), the
+// register kernel 32 (two 16-row tiles) or one tile. A launch that fills a
+// round of the chip this way
 // needs no split to fill it. On the register kernel it runs in a single pass:
 // splitting would only add partials (fp32, d_head + 2 words per row and
 // partition), which outweigh the K/V it reads. On the LDS kernel a

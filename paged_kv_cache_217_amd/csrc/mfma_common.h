@@ -76,6 +76,16 @@ __device__ __forceinline__ void ld_stream(uint32_t& out, __amdgpu_buffer_rsrc_t 
   out = __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, kLoadNonTemporal);
 }
 
+// A wave-uniform 32-bit read that stays a scalar load. A plain global read
+// placed after a barrier or a store becomes a vector load (the compiler can
+// no longer rule out that the memory was written), and a vector load used as
+// a scalar waits on every vector load in flight. Read through the constant
+// address space instead; only for data that nothing in flight writes (block
+// tables).
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }

@@ -24,6 +24,9 @@
 //  - the row groups of one (sequence, KV head) run on one XCD (blocks are
 //    handed to the 8 XCDs round-robin), so the K/V they all read is fetched
 //    into that XCD's L2 once.
+// A second form for bf16 at d = 128 (multi_query_lds_pp, below) takes 256
+// rows per workgroup and splits each chunk's work into a matrix phase and a
+// vector phase that the two waves of a SIMD run in opposite order.
 #include <float.h>
 
 #include <type_traits>
@@ -494,10 +497,485 @@ void multi_query_lds_mfma(DecodeArgs a) {
   }
 }
 
+// Ping-pong form of the kernel above, for bf16 caches at d = 128 with 256 or
+// more rows per KV head. Two waves share each SIMD; in the form above they
+// belong to different workgroups, drift into the same phase and take turns
+// on the matrix core and the vector ALU rather than using both at once. Here
+// a workgroup has 8 waves (256 rows), so one workgroup fills a CU with two
+// waves per SIMD, and the two waves of a SIMD take opposite roles. The work
+// on a 64-token chunk is split into a matrix phase (the previous chunk's
+// P V products, then this chunk's K Q^T) and a vector phase (masks, the
+// rescale check, the weights and their bf16 head/tail split), and the second
+// role runs one phase behind the first. Every phase ends at a workgroup
+// barrier, so while one wave of a SIMD issues products the other computes
+// weights. The role is taken per SIMD from an LDS counter (the first wave of
+// a SIMD to arrive leads); every wave runs the same code and the same number
+// of barriers, so the roles only decide timing, never the result.
+//
+// LDS: K and V of a chunk are held in separate two-deep rings, rows padded by
+// 32 bytes (K and V both: no bank conflicts left, measured). K of chunk n is
+// read in phases 2n, 2n + 1 (scores) and V of chunk n in phases 2n + 2,
+// 2n + 3 (its P V products, one phase later than its weights); at the start
+// of phase 2k the workgroup writes K of chunk k + 1 and V of chunk k from
+// registers loaded two phases earlier. In the matrix phase the LDS reads are
+// interleaved with the products (a dozen reads ahead, then one read per two
+// products), so that the reads' latency is covered.
+template <int BS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void multi_query_lds_pp(DecodeArgs a) {
+  constexpr int D = 128;
+  constexpr int NW = 8;                       // waves
+  constexpr int NT = NW * 64;                 // threads
+  constexpr int TPW = 2;                      // 16-row tiles per wave
+  constexpr int GR = NW * TPW * 16;           // rows per workgroup
+  constexpr int CT = 64;                      // tokens per chunk
+  constexpr int NRG = CT / 16;                // 16-token row groups per chunk
+  constexpr int NKS = CT / 32;                // 32-token PV k-steps per chunk
+  constexpr int NKK = D / 32;                 // QK MFMA steps over d
+  constexpr int NJ = D / 16;                  // PV MFMAs per k-step
+  constexpr int RB = 2 * D;                   // bytes per token row
+  constexpr int LR = RB + 32;                 // padded LDS row (K and V)
+  constexpr int CB = CT * RB;                 // bytes of K (or V) per chunk
+  constexpr int TB = BS * RB;                 // bytes of one (block, head) tile
+  constexpr int PIECES = CB / (16 * NT);      // 16-byte pieces of a chunk's K per thread
+  static_assert(PIECES >= 1 && CB % (16 * NT) == 0, "chunk must split into thread pieces");
+  static_assert(TB % 1024 == 0, "a wave's 1 KiB slice must lie in one tile");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15;
+  const int g4 = lane >> 4;
+
+  // grid as for the kernel above, GR rows per workgroup
+  const int G = a.n_q / a.n_kv;
+  const int rows = a.Q * G;
+  const int groups = (rows + GR - 1) / GR;
+  int wid = blockIdx.x;
+  if (gridDim.x % 8 == 0) wid = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  const int g = wid / groups;
+  const int row0 = (wid % groups) * GR;
+  const int b = blockIdx.y;
+  const int j = gridDim.z - 1 - blockIdx.z;
+  const int ctx = min(a.context_lens ? a.context_lens[b] : a.fixed_ctx, a.max_blocks * BS);
+  const int ql = a.non_causal ? (ctx > 0 ? a.Q : 0)
+                              : max(0, min(min(a.query_lens[b], a.Q), ctx));
+  auto qpos = [&](int i) -> int { return a.non_causal ? ctx - 1 : ctx - ql + i; };
+  const int t0 = j * a.partition;
+  auto last_pos = [&](int r0, int r1) -> int {
+    const int i_hi = min((min(r1, rows) - 1) / G, ql - 1);
+    return r0 / G < ql && r0 < rows ? qpos(i_hi) : -1;
+  };
+  const int p_grp = last_pos(row0, row0 + GR);
+  if (t0 > p_grp) {                           // the whole workgroup leaves here
+    if (!a.write_partials && j == 0) {
+      for (int e = threadIdx.x; e < GR * D; e += blockDim.x) {
+        const int r = row0 + e / D;
+        if (r >= rows) continue;
+        const int64_t oi =
+            ((static_cast<int64_t>(b) * a.Q + r / G) * a.n_q + g * G + r % G) * D + e % D;
+        if (a.out_dtype == PKV_FP32)
+          static_cast<float*>(a.out)[oi] = 0.0f;
+        else
+          static_cast<uint16_t*>(a.out)[oi] = 0;
+      }
+    }
+    return;
+  }
+  const int t1 = min(t0 + a.partition, p_grp + 1);
+  const int blk0 = t0 / BS;
+  const int blk1 = (t1 + BS - 1) / BS;
+  const int n_ch = (t1 - t0 + CT - 1) / CT;
+
+  // role: 0 for the first wave of its SIMD to get here, 1 for the second
+  __shared__ int simd_count[4];
+  if (threadIdx.x < 4) simd_count[threadIdx.x] = 0;
+  __syncthreads();
+  int role;
+  {
+    // HW_ID bits 5:4 are the wave's SIMD
+    const int simd = __builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3;
+    int r = 0;
+    if (lane == 0) r = atomicAdd(&simd_count[simd], 1);
+    role = __builtin_amdgcn_readfirstlane(r) & 1;
+  }
+
+  // this wave's rows and their Q^T operands, as in the kernel above
+  const int wrow0 = row0 + wave * TPW * 16;
+  const int p_lo = qpos(wrow0 / G);
+  bf16x8_t qop[TPW][NKK];
+  int pos[TPW];
+  float qscale = a.scale * kLog2e;
+  const uint32_t qflip = qscale < 0.0f ? 0x80008000u : 0u;
+  const bool qzero = qscale == 0.0f;
+  qscale = qzero ? 1.0f : fabsf(qscale);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int row = wrow0 + 16 * t + c;
+    const int qi = row / G;
+    const bool live_row = row < rows && qi < ql && !qzero;
+    pos[t] = qpos(qi);
+    const int64_t qrow =
+        live_row ? (static_cast<int64_t>(b) * a.Q + qi) * a.n_q + g * G + row % G : 0;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      uint4 w = *reinterpret_cast<const uint4*>(a.q + qrow * D + 32 * kk + 8 * g4);
+      w = make_uint4(w.x ^ qflip, w.y ^ qflip, w.z ^ qflip, w.w ^ qflip);
+      if (!live_row) w = make_uint4(0, 0, 0, 0);
+      qop[t][kk] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+
+  __shared__ __align__(16) uint8_t sk[2][CT * LR];
+  __shared__ __align__(16) uint8_t sv[2][CT * LR];
+
+  const int64_t tile_bytes = TB;
+  const int64_t head_off = static_cast<int64_t>(g) * tile_bytes;
+  const int64_t block_stride = static_cast<int64_t>(a.n_kv) * tile_bytes;
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
+  // Piece e = threadIdx + NT x of a chunk's K (or V) is bytes [16 e, 16 e +
+  // 16); a wave's 64 pieces lie in one tile. A chunk past the partition reads
+  // nothing (its blocks get size-0 resources), so every fetch is issued
+  // unconditionally and the outstanding-load count is the same in every phase.
+  // The physical blocks of a fetch are resolved a phase ahead, in a vector
+  // phase: a scalar load in flight would make every LDS wait of the matrix
+  // phase a wait for all of them.
+  using Piece = uint4[PIECES];
+  using Blocks = int[PIECES];
+  auto resolve = [&](Blocks& pb, int ci) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < PIECES; ++x) {
+      const int blk = blk0 + ci * (CT / BS) + (16 * (NT * x + 64 * wave)) / TB;
+      int p = ld_uniform(bt + min(blk, blk1 - 1));    // always a valid entry
+      if (blk >= blk1 || p < 0 || p >= a.num_blocks) p = 0;
+      pb[x] = p;
+    }
+  };
+  auto fetch = [&](Piece& out, const uint8_t* cache, int ci, const Blocks& pb)
+                   __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < PIECES; ++x) {
+      const int wbyte = 16 * (NT * x + 64 * wave);
+      const bool have = blk0 + ci * (CT / BS) + wbyte / TB < blk1;
+      ld_stream(out[x], tile_rsrc(cache + pb[x] * block_stride + head_off, have ? TB : 0),
+                static_cast<uint32_t>(wbyte % TB + 16 * lane), 0);
+    }
+  };
+  auto st_off = [&](int x) -> int {
+    const int e = threadIdx.x + NT * x;
+    return ((16 * e) / RB) * LR + (16 * e) % RB;
+  };
+  auto commit_k = [&](const Piece& w, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < PIECES; ++x) *reinterpret_cast<uint4*>(&sk[buf][st_off(x)]) = w[x];
+  };
+  // V slots past t1 may hold anything (NaN in a tail block): zeroed here so
+  // that P = 0 times them gives 0. K needs nothing: those scores become -inf.
+  auto commit_v = [&](const Piece& w, int buf, int ci) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < PIECES; ++x) {
+      const bool dead = t0 + ci * CT + (16 * (threadIdx.x + NT * x)) / RB >= t1;
+      const uint4 v = make_uint4(dead ? 0u : w[x].x, dead ? 0u : w[x].y, dead ? 0u : w[x].z,
+                                 dead ? 0u : w[x].w);
+      *reinterpret_cast<uint4*>(&sv[buf][st_off(x)]) = v;
+    }
+  };
+
+  float m_ref[TPW], m_raw[TPW], l[TPW];
+  f32x4_t acc[TPW][NJ];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    m_ref[t] = -INFINITY;
+    m_raw[t] = -INFINITY;
+    l[t] = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) acc[t][jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // per-lane LDS offsets: K token c at dims of lane group g4; V read
+  // transposed, lane (c, g4) addressing token 4 g4 + c / 4, dims 4 (c % 4) ..
+  // of a 16-dim column block
+  const int k_lane = c * LR + 16 * g4;
+  const int v_tr = (4 * g4 + c / 4) * LR + 8 * (c % 4);
+
+  // carried between phases: the scores of the chunk whose weights come next
+  // and the weights (bf16 head and tail) of the chunk whose products come next
+  float s[TPW][4 * NRG];
+  bf16x8_t pop_hi[TPW][NKS], pop_lo[TPW][NKS];
+  // A phase's results are taken as read by an empty volatile asm at its end.
+  // Arithmetic is otherwise free to move across a barrier, and the compiler
+  // does sink the weights into the next phase, beside their products, which
+  // would undo the split into phases.
+  auto pin_scores = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4 * NRG; ++i) asm volatile("" : "+v"(s[t][i]));
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) asm volatile("" : "+v"(acc[t][jj]));
+  };
+  auto pin_weights = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        asm volatile("" : "+v"(pop_hi[t][ks]));
+        asm volatile("" : "+v"(pop_lo[t][ks]));
+      }
+      asm volatile("" : "+v"(l[t]));
+    }
+  };
+
+  // matrix phase: products of P with the V buffer vb, then K Q^T of the K
+  // buffer kb into s
+  auto pv = [&](int vb) __attribute__((always_inline)) {
+    const uint8_t* vl_ = sv[vb];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        // V^T operand of dims 16 jj ..: tokens 4 g4 .. and 16 + 4 g4 .. of
+        // the k-step
+        const uint8_t* vt = vl_ + v_tr + 32 * ks * LR + 32 * jj;
+        const uint2 v0 = lds_read_tr16(vt);
+        const uint2 v1 = lds_read_tr16(vt + 16 * LR);
+        const bf16x8_t vop = as_bf16x8(v0.x, v0.y, v1.x, v1.y);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          acc[t][jj] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi[t][ks], acc[t][jj], 0, 0, 0);
+          acc[t][jj] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[t][ks], acc[t][jj], 0, 0, 0);
+        }
+      }
+    }
+  };
+  auto qk = [&](int kb) __attribute__((always_inline)) {
+    const uint8_t* kl_ = sk[kb];
+    f32x4_t sc[NRG][TPW];
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) sc[rg][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+      for (int rg = 0; rg < NRG; ++rg) {
+        const bf16x8_t kop = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(kl_ + k_lane + 16 * rg * LR + 64 * kk));
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+          sc[rg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[t][kk], sc[rg][t], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[t][4 * rg + i] = sc[rg][t][i];
+  };
+  // the matrix phase's order: 12 LDS reads, then one read per two products
+  // (48 reads and 96 products in all)
+  auto matrix_order = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+    for (int i = 0; i < 36; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
+  };
+
+  // vector phase for chunk n: masks, the lazy-rescale check (as in the kernel
+  // above), then the weights, split into bf16 head and tail
+  auto weights = [&](int n) __attribute__((always_inline)) {
+    const int tok0 = t0 + n * CT;
+    if (tok0 + CT > min(p_lo + 1, t1)) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int lim = min(pos[t] + 1, t1);
+#pragma unroll
+        for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (tok0 + 16 * rg + 4 * g4 + i >= lim) s[t][4 * rg + i] = -INFINITY;
+      }
+    }
+    float lmax[TPW];
+    bool need_any = false;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      float mx = s[t][0];
+#pragma unroll
+      for (int i = 1; i < 4 * NRG; ++i) mx = vmax(mx, s[t][i]);
+      lmax[t] = mx;
+      m_raw[t] = vmax(m_raw[t], mx);
+      need_any |= mx * qscale > m_ref[t] + kLazyRescale;
+    }
+    if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const float mx = max_xor32(max_xor16(lmax[t])) * qscale;
+        const bool need = mx > m_ref[t] + kLazyRescale;
+        const float alpha = need ? fast_exp2(m_ref[t] - mx) : 1.0f;
+        if (need) m_ref[t] = mx;
+        l[t] *= alpha;
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) acc[t][jj] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const float m_use = m_ref[t] == -INFINITY ? 0.0f : m_ref[t];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p[i] = fast_exp2(fmaf(s[t][8 * ks + i], qscale, -m_use));
+          l[t] += p[i];
+        }
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const Bf16Split sp = split_bf16(p[2 * u], p[2 * u + 1]);
+          ph[u] = sp.hi;
+          pl[u] = sp.lo;
+        }
+        pop_hi[t][ks] = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
+        pop_lo[t][ks] = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
+      }
+    }
+  };
+
+  // A wave's phases are M0 W0 M1 W1 ... W(N-1) MN, where Mk is the products
+  // of chunk k - 1 (k >= 1) and the scores of chunk k (k < N), and Wk the
+  // weights of chunk k; each phase ends at a barrier. Role 1 passes one
+  // barrier before its first phase and role 0 one after its last, so role 1
+  // runs one phase behind: while one wave of a SIMD is in Mk the other is in
+  // W(k-1) or Wk. Both roles run the same code. K of chunk n sits in
+  // sk[n % 2] and V of chunk n in sv[n % 2]; a wave writes its slice of K of
+  // chunk k + 1 and of V of chunk k at the start of Mk, so with the lag K of
+  // chunk k is complete one phase before role 0 reads it and V of chunk k one
+  // phase before role 0's M(k+1), and neither overwrites a buffer before role
+  // 1's last read of its previous contents (K of chunk N, written by M(N-1),
+  // is zeros that nobody reads). The staged registers are refilled right
+  // after they are written out, so a load has a whole step (two phases) to
+  // land. The first and last phases are peeled so that the loop's phases have
+  // no branches around their products.
+  {
+    const int N = n_ch;                       // >= 1
+    Piece stk, stv;             // staged K of chunk k + 1 and V of chunk k
+    Blocks bk, bv;              // blocks of the next K and V fetches
+    resolve(bk, 0);
+    fetch(stv, a.k_cache, 0, bk);             // K of chunk 0, through stv
+    resolve(bk, 1);
+    fetch(stk, a.k_cache, 1, bk);
+    commit_k(stv, 0);
+    resolve(bv, 0);
+    fetch(stv, a.v_cache, 0, bv);
+    resolve(bk, 2);
+    resolve(bv, 1);
+    __syncthreads();
+    if (role == 1) __syncthreads();
+    // M0, W0
+    commit_k(stk, 1);
+    commit_v(stv, 0, 0);
+    fetch(stk, a.k_cache, 2, bk);
+    fetch(stv, a.v_cache, 1, bv);
+    qk(0);
+    pin_scores();
+    __syncthreads();
+    weights(0);
+    resolve(bk, 3);
+    resolve(bv, 2);
+    pin_weights();
+    __syncthreads();
+    // Mk and Wk for 1 <= k < N: write K of chunk k + 1 and V of chunk k, fetch
+    // K of chunk k + 2 and V of chunk k + 1 into the registers just freed,
+    // then the products; the weights, then the blocks of the next fetches
+    for (int k = 1; k < N; ++k) {
+      const int par = k & 1;
+      commit_k(stk, par ^ 1);
+      commit_v(stv, par, k);
+      fetch(stk, a.k_cache, k + 2, bk);
+      fetch(stv, a.v_cache, k + 1, bv);
+      pv(par ^ 1);
+      qk(par);
+      matrix_order();
+      pin_scores();
+      __syncthreads();
+      weights(k);
+      resolve(bk, k + 3);
+      resolve(bv, k + 2);
+      pin_weights();
+      __syncthreads();
+    }
+    // MN: the last chunk's products (V of chunk N - 1 in sv[(N - 1) % 2])
+    pv((N - 1) & 1);
+    __syncthreads();
+    if (role == 0) __syncthreads();
+  }
+
+  // outputs as in the kernel above: lane (c, g4) holds, of row 16 t + c, dims
+  // 16 jj + 4 g4 + i
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    float lt = l[t];
+    lt = sum_xor32(sum_xor16(lt));
+    const float m_true = max_xor32(max_xor16(m_raw[t])) * qscale;
+    const float f = m_true == -INFINITY ? 0.0f : fast_exp2(m_ref[t] - m_true);
+    const float L = lt * f;
+    const int rr = wrow0 + 16 * t + c;
+    if (rr >= rows) continue;
+    const int ri = rr / G;
+    const bool live = ri < ql;
+    const int64_t orow = (static_cast<int64_t>(b) * a.Q + ri) * a.n_q + g * G + rr % G;
+    const float inv = live && L > 0.0f ? f / L : 0.0f;
+    if (a.write_partials) {
+      const int64_t mi = orow * a.P_max + j;
+      if (g4 == 0) {
+        a.ws_m[mi] = m_true;
+        a.ws_l[mi] = live ? L : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+          a.ws_o[mi * D + 16 * jj + 4 * g4 + i] = acc[t][jj][i] * inv;
+    } else if (a.out_dtype == PKV_FP32) {
+      float* o = static_cast<float*>(a.out) + orow * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) o[16 * jj + 4 * g4 + i] = acc[t][jj][i] * inv;
+    } else {
+      uint16_t* o = static_cast<uint16_t*>(a.out) + orow * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+          o[16 * jj + 4 * g4 + i] = f32_to_bf16_rne(acc[t][jj][i] * inv);
+    }
+  }
+}
+
 template <int D, int BS, int FMT>
 static hipError_t launch_lds(const DecodeArgs& a, hipStream_t s) {
-  const int G = a.n_q / a.n_kv;
-  const int groups = (a.Q * G + 127) / 128;
+  const int rows = a.Q * (a.n_q / a.n_kv);
+  if constexpr (D == 128 && FMT == kFmtBf16) {
+    // the ping-pong form where its 256-row workgroups cover the rows with no
+    // more padding than 128-row ones (measured slower otherwise, and for FP8,
+    // whose widening adds vector work to the matrix phase)
+    const int groups = (rows + 255) / 256;
+    if (rows >= 256 && 2 * groups == (rows + 127) / 128) {
+      const dim3 grid(a.n_kv * groups, a.B, a.P_max);
+      multi_query_lds_pp<BS><<<grid, 512, 0, s>>>(a);
+      return hipGetLastError();
+    }
+  }
+  const int groups = (rows + 127) / 128;
   const dim3 grid(a.n_kv * groups, a.B, a.P_max);
   multi_query_lds_mfma<D, BS, FMT><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
