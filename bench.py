@@ -558,6 +558,20 @@ def bench_cascade(args, w, pkv, W, np, torch, dev):
     print(json.dumps(result), flush=True)
 
 
+def multi_query_kernel_name(w, Q):
+    """The kernel the library dispatches a multi-token query batch to: 128 or
+    more (query, head) rows per KV head run on the LDS-shared kernel, in its
+    ping-pong form for bf16 at d 128 when 256-row groups pad no more than
+    128-row ones; fewer rows on the register kernel."""
+    rows = Q * (w.n_q // w.n_kv)
+    if rows < 128:
+        return "multi_query_partition_mfma"
+    if (w.kv_dtype == "bf16" and w.d == 128 and rows >= 256
+            and 2 * -(-rows // 256) == -(-rows // 128)):
+        return "multi_query_lds_pp"
+    return "multi_query_lds_mfma"
+
+
 def bench_multi_query(args, w, pkv, W, np, torch, dev):
     """Several query tokens per sequence: per layer, kv_append of the Q new
     tokens of every sequence, then causal multi-query paged attention."""
@@ -635,8 +649,7 @@ def bench_multi_query(args, w, pkv, W, np, torch, dev):
     kv_bytes_layer = kv_bytes(w)
     flops, att_bytes = multi_query_work(w, P_max)
     intensity = flops / att_bytes
-    # 128 or more (query, head) rows per KV head run on the LDS-shared kernel
-    kname = "multi_query_lds_mfma" if Q * (n_q // n_kv) >= 128 else "multi_query_partition_mfma"
+    kname = multi_query_kernel_name(w, Q)
     if P_max > 1:
         kname += " + splitk_reduce"
     mfma_bound = intensity > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
