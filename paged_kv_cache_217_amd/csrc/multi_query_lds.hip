@@ -24,9 +24,10 @@
 //  - the row groups of one (sequence, KV head) run on one XCD (blocks are
 //    handed to the 8 XCDs round-robin), so the K/V they all read is fetched
 //    into that XCD's L2 once.
-// A second form for bf16 at d = 128 (multi_query_lds_pp, below) takes 256
-// rows per workgroup and splits each chunk's work into a matrix phase and a
-// vector phase that the two waves of a SIMD run in opposite order.
+// A second form at d = 128 (multi_query_lds_pp, below) takes 256 rows per
+// workgroup, holds chunks in LDS as bf16 (FP8 and FP4 widened as they are
+// written) and splits each chunk's work into a matrix phase and a vector
+// phase that the two waves of a SIMD run in opposite order.
 #include <float.h>
 
 #include <type_traits>
@@ -497,8 +498,8 @@ void multi_query_lds_mfma(DecodeArgs a) {
   }
 }
 
-// Ping-pong form of the kernel above, for bf16 caches at d = 128 with 256 or
-// more rows per KV head. Two waves share each SIMD; in the form above they
+// Ping-pong form of the kernel above, for d = 128 with 256 or more rows per KV
+// head. Two waves share each SIMD; in the form above they
 // belong to different workgroups, drift into the same phase and take turns
 // on the matrix core and the vector ALU rather than using both at once. Here
 // a workgroup has 8 waves (256 rows), so one workgroup fills a CU with two
@@ -512,18 +513,25 @@ void multi_query_lds_mfma(DecodeArgs a) {
 // a SIMD to arrive leads); every wave runs the same code and the same number
 // of barriers, so the roles only decide timing, never the result.
 //
-// LDS: K and V of a chunk are held in separate two-deep rings, rows padded by
-// 32 bytes (K and V both: no bank conflicts left, measured). K of chunk n is
+// LDS: K and V of a chunk are held in separate two-deep rings as bf16, rows
+// padded by 32 bytes (K and V both: no bank conflicts left, measured). FP8 and
+// FP4 codes are widened exactly to bf16 by the thread that writes them into
+// LDS, once per chunk, so the matrix phase is the same for every format and
+// holds no conversions (the per-head scales go into the score scale and the
+// output, as in the kernel above). K of chunk n is
 // read in phases 2n, 2n + 1 (scores) and V of chunk n in phases 2n + 2,
 // 2n + 3 (its P V products, one phase later than its weights); at the start
 // of phase 2k the workgroup writes K of chunk k + 1 and V of chunk k from
 // registers loaded two phases earlier. In the matrix phase the LDS reads are
 // interleaved with the products (a dozen reads ahead, then one read per two
 // products), so that the reads' latency is covered.
-template <int BS>
+template <int BS, int FMT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void multi_query_lds_pp(DecodeArgs a) {
   constexpr int D = 128;
+  constexpr bool FP8 = FMT == kFmtFp8;
+  constexpr bool FP4 = FMT == kFmtFp4;
+  constexpr bool QNT = FMT != kFmtBf16;       // per-head scales
   constexpr int NW = 8;                       // waves
   constexpr int NT = NW * 64;                 // threads
   constexpr int TPW = 2;                      // 16-row tiles per wave
@@ -533,13 +541,16 @@ void multi_query_lds_pp(DecodeArgs a) {
   constexpr int NKS = CT / 32;                // 32-token PV k-steps per chunk
   constexpr int NKK = D / 32;                 // QK MFMA steps over d
   constexpr int NJ = D / 16;                  // PV MFMAs per k-step
-  constexpr int RB = 2 * D;                   // bytes per token row
+  constexpr int RB = 2 * D;                   // bytes per bf16 token row (LDS)
   constexpr int LR = RB + 32;                 // padded LDS row (K and V)
-  constexpr int CB = CT * RB;                 // bytes of K (or V) per chunk
-  constexpr int TB = BS * RB;                 // bytes of one (block, head) tile
-  constexpr int PIECES = CB / (16 * NT);      // 16-byte pieces of a chunk's K per thread
-  static_assert(PIECES >= 1 && CB % (16 * NT) == 0, "chunk must split into thread pieces");
-  static_assert(TB % 1024 == 0, "a wave's 1 KiB slice must lie in one tile");
+  constexpr int RBS = FP4 ? D / 2 : FP8 ? D : 2 * D;   // bytes per token row in the cache
+  constexpr int CB = CT * RBS;                // cache bytes of K (or V) per chunk
+  constexpr int TB = BS * RBS;                // bytes of one (block, head) tile
+  constexpr int PB = FP4 ? 8 : 16;            // bytes of one piece (16 elements for FP8/FP4)
+  constexpr int PIECES = CB / (PB * NT);      // pieces of a chunk's K per thread
+  using VT = typename Vec<PB>::T;
+  static_assert(PIECES >= 1 && CB % (PB * NT) == 0, "chunk must split into thread pieces");
+  static_assert(TB % (64 * PB) == 0, "a wave's slice of a chunk must lie in one tile");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -605,6 +616,7 @@ void multi_query_lds_pp(DecodeArgs a) {
   bf16x8_t qop[TPW][NKK];
   int pos[TPW];
   float qscale = a.scale * kLog2e;
+  if constexpr (QNT) qscale *= a.k_scale[g];
   const uint32_t qflip = qscale < 0.0f ? 0x80008000u : 0u;
   const bool qzero = qscale == 0.0f;
   qscale = qzero ? 1.0f : fabsf(qscale);
@@ -632,19 +644,19 @@ void multi_query_lds_pp(DecodeArgs a) {
   const int64_t head_off = static_cast<int64_t>(g) * tile_bytes;
   const int64_t block_stride = static_cast<int64_t>(a.n_kv) * tile_bytes;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
-  // Piece e = threadIdx + NT x of a chunk's K (or V) is bytes [16 e, 16 e +
-  // 16); a wave's 64 pieces lie in one tile. A chunk past the partition reads
+  // Piece e = threadIdx + NT x of a chunk's K (or V) is cache bytes [PB e,
+  // PB e + PB); a wave's 64 pieces lie in one tile. A chunk past the partition reads
   // nothing (its blocks get size-0 resources), so every fetch is issued
   // unconditionally and the outstanding-load count is the same in every phase.
   // The physical blocks of a fetch are resolved a phase ahead, in a vector
   // phase: a scalar load in flight would make every LDS wait of the matrix
   // phase a wait for all of them.
-  using Piece = uint4[PIECES];
+  using Piece = VT[PIECES];
   using Blocks = int[PIECES];
   auto resolve = [&](Blocks& pb, int ci) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < PIECES; ++x) {
-      const int blk = blk0 + ci * (CT / BS) + (16 * (NT * x + 64 * wave)) / TB;
+      const int blk = blk0 + ci * (CT / BS) + (PB * (NT * x + 64 * wave)) / TB;
       int p = ld_uniform(bt + min(blk, blk1 - 1));    // always a valid entry
       if (blk >= blk1 || p < 0 || p >= a.num_blocks) p = 0;
       pb[x] = p;
@@ -654,30 +666,55 @@ void multi_query_lds_pp(DecodeArgs a) {
                    __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < PIECES; ++x) {
-      const int wbyte = 16 * (NT * x + 64 * wave);
+      const int wbyte = PB * (NT * x + 64 * wave);
       const bool have = blk0 + ci * (CT / BS) + wbyte / TB < blk1;
       ld_stream(out[x], tile_rsrc(cache + pb[x] * block_stride + head_off, have ? TB : 0),
-                static_cast<uint32_t>(wbyte % TB + 16 * lane), 0);
+                static_cast<uint32_t>(wbyte % TB + PB * lane), 0);
     }
   };
+  // piece x of this thread: its token row within the chunk and its LDS offset
+  auto st_row = [&](int x) -> int { return (PB * (threadIdx.x + NT * x)) / RBS; };
   auto st_off = [&](int x) -> int {
-    const int e = threadIdx.x + NT * x;
-    return ((16 * e) / RB) * LR + (16 * e) % RB;
+    const int byte = (PB * (threadIdx.x + NT * x)) % RBS;       // cache byte within the row
+    return st_row(x) * LR + (FP4 ? 4 * byte : FP8 ? 2 * byte : byte);
+  };
+  // a piece as bf16: 16 bytes of bf16 as they are, 16 FP8 or FP4 codes widened
+  // exactly into 32 bytes (`zero`: a V slot past t1, which may hold anything;
+  // P = 0 times it must give 0)
+  auto store = [&](uint8_t* dst, const VT& w, bool zero) __attribute__((always_inline)) {
+    if constexpr (FMT == kFmtBf16) {
+      *reinterpret_cast<uint4*>(dst) = zero ? make_uint4(0, 0, 0, 0) : w;
+    } else {
+      uint32_t h[8];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          h[2 * i] = fp8x2_to_bf16x2<false>(word(w, i));
+          h[2 * i + 1] = fp8x2_to_bf16x2<true>(word(w, i));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          h[4 * i] = fp4x2_to_bf16x2<0>(word(w, i));
+          h[4 * i + 1] = fp4x2_to_bf16x2<1>(word(w, i));
+          h[4 * i + 2] = fp4x2_to_bf16x2<2>(word(w, i));
+          h[4 * i + 3] = fp4x2_to_bf16x2<3>(word(w, i));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = zero ? 0u : h[i];
+      *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
+      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(h[4], h[5], h[6], h[7]);
+    }
   };
   auto commit_k = [&](const Piece& w, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int x = 0; x < PIECES; ++x) *reinterpret_cast<uint4*>(&sk[buf][st_off(x)]) = w[x];
+    for (int x = 0; x < PIECES; ++x) store(&sk[buf][st_off(x)], w[x], false);
   };
-  // V slots past t1 may hold anything (NaN in a tail block): zeroed here so
-  // that P = 0 times them gives 0. K needs nothing: those scores become -inf.
   auto commit_v = [&](const Piece& w, int buf, int ci) __attribute__((always_inline)) {
 #pragma unroll
-    for (int x = 0; x < PIECES; ++x) {
-      const bool dead = t0 + ci * CT + (16 * (threadIdx.x + NT * x)) / RB >= t1;
-      const uint4 v = make_uint4(dead ? 0u : w[x].x, dead ? 0u : w[x].y, dead ? 0u : w[x].z,
-                                 dead ? 0u : w[x].w);
-      *reinterpret_cast<uint4*>(&sv[buf][st_off(x)]) = v;
-    }
+    for (int x = 0; x < PIECES; ++x)
+      store(&sv[buf][st_off(x)], w[x], t0 + ci * CT + st_row(x) >= t1);
   };
 
   float m_ref[TPW], m_raw[TPW], l[TPW];
@@ -932,7 +969,8 @@ void multi_query_lds_pp(DecodeArgs a) {
     const int ri = rr / G;
     const bool live = ri < ql;
     const int64_t orow = (static_cast<int64_t>(b) * a.Q + ri) * a.n_q + g * G + rr % G;
-    const float inv = live && L > 0.0f ? f / L : 0.0f;
+    const float vscale = QNT ? a.v_scale[g] : 1.0f;
+    const float inv = live && L > 0.0f ? f * vscale / L : 0.0f;
     if (a.write_partials) {
       const int64_t mi = orow * a.P_max + j;
       if (g4 == 0) {
@@ -964,14 +1002,13 @@ void multi_query_lds_pp(DecodeArgs a) {
 template <int D, int BS, int FMT>
 static hipError_t launch_lds(const DecodeArgs& a, hipStream_t s) {
   const int rows = a.Q * (a.n_q / a.n_kv);
-  if constexpr (D == 128 && FMT == kFmtBf16) {
+  if constexpr (D == 128) {
     // the ping-pong form where its 256-row workgroups cover the rows with no
-    // more padding than 128-row ones (measured slower otherwise, and for FP8,
-    // whose widening adds vector work to the matrix phase)
+    // more padding than 128-row ones (measured slower otherwise)
     const int groups = (rows + 255) / 256;
     if (rows >= 256 && 2 * groups == (rows + 127) / 128) {
       const dim3 grid(a.n_kv * groups, a.B, a.P_max);
-      multi_query_lds_pp<BS><<<grid, 512, 0, s>>>(a);
+      multi_query_lds_pp<BS, FMT><<<grid, 512, 0, s>>>(a);
       return hipGetLastError();
     }
   }

@@ -3,9 +3,9 @@
 Bars as for decode (max abs 1e-2 BF16 / 3e-2 FP8, relative L2 1e-4), and
 agreement with plain decode attention over the concatenated tables. Cases
 put the prefix rows (sequences x G) on each multi-query kernel (fewer than
-128 rows per KV head, 128 or more, and the bf16 ping-pong form at 512), cover
-FP8, MQA, an empty prefix, empty suffixes, ragged suffixes with NaN-poisoned
-tails, and explicit partitions.
+128 rows per KV head, 128 or more, and the ping-pong form at 512, bf16 and
+FP8), cover MQA, an empty prefix, empty suffixes, ragged suffixes with
+NaN-poisoned tails, and explicit partitions.
 """
 
 import numpy as np
@@ -54,6 +54,7 @@ CASES = [
     (list(range(3, 3 + 36 * 29, 29)), 2048, 64, 8, 128, 16, W.BF16, 0, 0),   # 288 rows
     (list(range(2, 2 + 64 * 17, 17)), 3072, 64, 8, 128, 32, W.BF16, 1024, 0),  # 512 rows
     (list(range(1, 1 + 40 * 13, 13)), 1024, 64, 8, 128, 32, W.FP8, 512, 0),  # 320 rows
+    (list(range(5, 5 + 64 * 11, 11)), 2048, 64, 8, 128, 16, W.FP8, 0, 0),    # 512 rows
 ]
 
 

@@ -181,6 +181,8 @@ MQ_SHAPES = [
     ([300, 1025], [40, 200], 200, 16, 2, 32, 0),         # 1600 rows: LDS kernel
     ([300, 1025], [40, 200], 200, 16, 2, 16, 256),
     ([77, 640, 5], [77, 130, 5], 130, 8, 8, 16, 96),     # 130 rows, mid-chunk partitions
+    ([300, 1025, 64], [40, 64, 64], 64, 64, 8, 16, 0),   # 512 rows: ping-pong kernel
+    ([2050, 99], [64, 31], 64, 64, 8, 32, 160),
 ]
 
 

@@ -78,14 +78,16 @@ CASES = [
     ([300, 1025], [40, 200], 200, 16, 2, 128, 32, W.FP8, 256),
     ([77, 640, 5], [77, 130, 5], 130, 8, 2, 64, 16, W.BF16, 0),
     ([77, 640, 5], [77, 130, 5], 130, 8, 2, 64, 16, W.FP8, 96),
-    # bf16 at d 128 with 256-row groups as full as 128-row ones: the
-    # ping-pong kernel (a ragged last group, rows past a short sequence's
-    # queries, partitions ending mid-chunk, both block sizes); FP8 and a
-    # 288-row case of the same shapes stay on the 128-row kernel
+    # d 128 with 256-row groups as full as 128-row ones: the ping-pong kernel
+    # (a ragged last group, rows past a short sequence's queries, partitions
+    # ending mid-chunk, both block sizes, FP8 widened into LDS); 288 and 320
+    # rows of the same shapes stay on the 128-row kernel
     ([2000, 31], [50, 31], 50, 64, 8, 128, 32, W.BF16, 0),
     ([2000, 31], [36, 31], 36, 64, 8, 128, 32, W.BF16, 0),
     ([900, 45, 3000], [40, 40, 17], 40, 64, 8, 128, 16, W.FP8, 0),
     ([900, 45, 3000], [40, 40, 17], 40, 64, 8, 128, 16, W.FP8, 128),
+    ([900, 45, 3000], [64, 45, 17], 64, 64, 8, 128, 16, W.FP8, 0),
+    ([2000, 70, 999], [64, 64, 64], 64, 64, 8, 128, 32, W.FP8, 96),
     ([1111, 260], [64, 64], 64, 32, 4, 128, 16, W.BF16, 48),
     ([70, 3000, 129], [48, 64, 0], 64, 64, 8, 128, 16, W.BF16, 1024),
 ]
