@@ -561,13 +561,12 @@ def bench_cascade(args, w, pkv, W, np, torch, dev):
 def multi_query_kernel_name(w, Q):
     """The kernel the library dispatches a multi-token query batch to: 128 or
     more (query, head) rows per KV head run on the LDS-shared kernel, in its
-    ping-pong form for bf16 at d 128 when 256-row groups pad no more than
-    128-row ones; fewer rows on the register kernel."""
+    ping-pong form at d 128 unless 256-row groups pad the rows by more than a
+    tenth beyond 128-row ones; fewer rows on the register kernel."""
     rows = Q * (w.n_q // w.n_kv)
     if rows < 128:
         return "multi_query_partition_mfma"
-    if (w.kv_dtype == "bf16" and w.d == 128 and rows >= 256
-            and 2 * -(-rows // 256) == -(-rows // 128)):
+    if w.d == 128 and rows >= 256 and 10 * 2 * -(-rows // 256) <= 11 * -(-rows // 128):
         return "multi_query_lds_pp"
     return "multi_query_lds_mfma"
 
