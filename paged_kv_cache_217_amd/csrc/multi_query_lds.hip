@@ -16,17 +16,21 @@
 //    walks the context in chunks; each chunk is fetched once by the whole
 //    workgroup (a wave fetches one 1 KiB slice of one (block, head) tile per
 //    load) into an LDS double buffer and every wave reads it from there;
-//  - LDS rows are padded by 16 bytes, so the 16 lanes that read the same
-//    16-byte column of 16 consecutive tokens hit 16 different 4-bank groups,
-//    and every LDS address is one per-lane register plus an immediate;
+//  - the chunk sits in LDS as bf16: FP8 and FP4 codes are widened exactly
+//    (scale 1) by the thread that writes them, once per chunk, so the inner
+//    loop is the same for every format and holds no conversions (the
+//    per-head scales go into the score scale and the output);
+//  - LDS rows are padded (K by 16 bytes, V by 32), so the 16 lanes that read
+//    the same 16-byte column of 16 consecutive tokens hit 16 different
+//    4-bank groups, and every LDS address is one per-lane register plus an
+//    immediate;
 //  - each wave keeps its rows' softmax state and output in registers for the
 //    whole context, so there is no merge between waves;
 //  - the row groups of one (sequence, KV head) run on one XCD (blocks are
 //    handed to the 8 XCDs round-robin), so the K/V they all read is fetched
 //    into that XCD's L2 once.
 // A second form at d = 128 (multi_query_lds_pp, below) takes 256 rows per
-// workgroup, holds chunks in LDS as bf16 (FP8 and FP4 widened as they are
-// written) and splits each chunk's work into a matrix phase and a vector
+// workgroup and splits each chunk's work into a matrix phase and a vector
 // phase that the two waves of a SIMD run in opposite order.
 #include <float.h>
 
@@ -40,6 +44,45 @@ namespace pkv {
 
 using namespace mfma;
 
+// One thread's piece of a chunk, stored into LDS as bf16: bf16 bytes as they
+// are, FP8 or FP4 codes widened exactly (scale 1) into twice or four times
+// the bytes (a zero code widens to +0).
+template <int FMT, typename T>
+__device__ __forceinline__ void store_bf16(uint8_t* dst, const T& w) {
+  constexpr int NIN = sizeof(T) / 4;                  // input words
+  constexpr int NOUT = FMT == kFmtBf16 ? NIN : FMT == kFmtFp8 ? 2 * NIN : 4 * NIN;
+  static_assert(NOUT % 4 == 0, "whole 16-byte stores");
+  uint32_t h[NOUT];
+#pragma unroll
+  for (int i = 0; i < NIN; ++i) {
+    const uint32_t x = word(w, i);
+    if constexpr (FMT == kFmtBf16) {
+      h[i] = x;
+    } else if constexpr (FMT == kFmtFp8) {
+      h[2 * i] = fp8x2_to_bf16x2<false>(x);
+      h[2 * i + 1] = fp8x2_to_bf16x2<true>(x);
+    } else {
+      h[4 * i] = fp4x2_to_bf16x2<0>(x);
+      h[4 * i + 1] = fp4x2_to_bf16x2<1>(x);
+      h[4 * i + 2] = fp4x2_to_bf16x2<2>(x);
+      h[4 * i + 3] = fp4x2_to_bf16x2<3>(x);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NOUT / 4; ++q)
+    *reinterpret_cast<uint4*>(dst + 16 * q) =
+        make_uint4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+}
+
+// w, or zeros where z holds, word by word (no select of whole vectors, which
+// the compiler can route through scratch memory)
+__device__ __forceinline__ uint4 zero_if(const uint4& w, bool z) {
+  return make_uint4(z ? 0u : w.x, z ? 0u : w.y, z ? 0u : w.z, z ? 0u : w.w);
+}
+__device__ __forceinline__ uint2 zero_if(const uint2& w, bool z) {
+  return make_uint2(z ? 0u : w.x, z ? 0u : w.y);
+}
+
 template <int D, int BS, int FMT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void multi_query_lds_mfma(DecodeArgs a) {
@@ -49,29 +92,28 @@ void multi_query_lds_mfma(DecodeArgs a) {
   constexpr int NW = 4;                       // waves
   constexpr int TPW = 2;                      // 16-row tiles per wave
   constexpr int GR = NW * TPW * 16;           // rows per workgroup
-  constexpr int CT = QNT ? 64 : 32;           // tokens per chunk
+  constexpr int CT = 32;                      // tokens per chunk
   constexpr int NRG = CT / 16;                // 16-token row groups per chunk
   constexpr int NKS = CT / 32;                // 32-token PV k-steps per chunk
   constexpr int NKK = D / 32;                 // QK MFMA steps over d
   constexpr int NJ = D / 16;                  // PV MFMAs per k-step
-  constexpr int DPL = D / 16;                 // dims per lane per V row
-  constexpr int RB = FP4 ? D / 2 : FP8 ? D : 2 * D;   // bytes per token row
-  constexpr int VB = FP4 ? DPL / 2 : FP8 ? DPL : 2 * DPL;   // bytes of one lane's V slice
-  using VT = typename Vec<VB>::T;
-  constexpr int VW = (DPL * 2) / 4;           // bf16 words per V slice
   static_assert(!FP4 || D == 128, "FP4 is built for d = 128");
+  constexpr int RB = 2 * D;                   // bytes per bf16 token row (LDS)
+  constexpr int RBS = FP4 ? D / 2 : FP8 ? D : 2 * D;   // bytes per token row in the cache
   constexpr int LR = RB + 16;                 // padded LDS row of K
-  // padded LDS row of V: bf16 V is read transposed, 4 rows of 32 bytes per
-  // 16 lanes, which a 32-byte pad puts on 32 different banks (a 16-byte pad
+  // padded LDS row of V: V is read transposed, 4 rows of 32 bytes per 16
+  // lanes, which a 32-byte pad puts on 32 different banks (a 16-byte pad
   // overlaps consecutive rows by 4 banks)
-  constexpr int LRV = FMT == kFmtBf16 ? RB + 32 : LR;
-  constexpr int CB = CT * RB;                 // bytes of K (or V) per chunk
+  constexpr int LRV = RB + 32;
+  constexpr int CB = CT * RBS;                // cache bytes of K (or V) per chunk
   constexpr int LB = CT * LR;                 // LDS bytes of K per chunk
   constexpr int LBV = CT * LRV;               // LDS bytes of V per chunk
-  constexpr int TB = BS * RB;                 // bytes of one (block, head) tile
-  constexpr int PIECES = CB / (16 * 256);     // 16-byte pieces per thread
-  static_assert(PIECES >= 1 && CB % (16 * 256) == 0, "chunk must split into thread pieces");
-  static_assert(TB % 1024 == 0, "a wave's 1 KiB slice must lie in one tile");
+  constexpr int TB = BS * RBS;                // bytes of one (block, head) tile
+  constexpr int PB = CB / 256 >= 16 ? 16 : CB / 256;   // bytes per thread piece
+  constexpr int PIECES = CB / (PB * 256);     // pieces per thread
+  using PT = typename Vec<PB>::T;
+  static_assert(PIECES >= 1 && CB % (PB * 256) == 0, "chunk must split into thread pieces");
+  static_assert(TB % (64 * PB) == 0, "a wave's slice of a chunk must lie in one tile");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -130,10 +172,8 @@ void multi_query_lds_mfma(DecodeArgs a) {
   // this wave's rows
   const int wrow0 = row0 + wave * TPW * 16;
   const int p_lo = qpos(wrow0 / G);
-  auto dimbase = [&](int kk) -> int {
-    if constexpr (FP4) return 32 * g4 + 8 * kk;
-    return FP8 ? 64 * (kk >> 1) + 16 * g4 + 8 * (kk & 1) : 32 * kk + 8 * g4;
-  };
+  // dims of MFMA step kk used by lane (c, g4), as in the bf16 K rows in LDS
+  auto dimbase = [&](int kk) -> int { return 32 * kk + 8 * g4; };
   bf16x8_t qop[TPW][NKK];
   int pos[TPW];
   // Scores stay unscaled (q . k) until the exponent, where 2^(s qscale - m)
@@ -166,8 +206,8 @@ void multi_query_lds_mfma(DecodeArgs a) {
   __shared__ __align__(16) uint8_t sk[4][LB];
   __shared__ __align__(16) uint8_t sv[4][LBV];
 
-  // chunk ci into registers: piece e = threadIdx + 256 k is bytes
-  // [16 e, 16 e + 16) of the chunk; a wave's 64 pieces lie in one tile
+  // chunk ci into registers: piece e = threadIdx + 256 k is cache bytes
+  // [PB e, PB e + PB) of the chunk; a wave's 64 pieces lie in one tile
   const int64_t tile_bytes = TB;
   const int64_t head_off = static_cast<int64_t>(g) * tile_bytes;
   const int64_t block_stride = static_cast<int64_t>(a.n_kv) * tile_bytes;
@@ -175,40 +215,45 @@ void multi_query_lds_mfma(DecodeArgs a) {
   // two register stage sets, filled together at the top of a step that
   // computes two chunks: a load has two chunks of compute to land
   struct Stage {
-    uint4 k[PIECES], v[PIECES];
+    PT k[PIECES], v[PIECES];
   };
   auto fetch = [&](Stage& st, int ci) {
 #pragma unroll
     for (int k = 0; k < PIECES; ++k) {
-      const int wbyte = (256 * k + 64 * wave) * 16;   // first byte of the wave's slice
+      const int wbyte = (256 * k + 64 * wave) * PB;   // first byte of the wave's slice
       const int blk = blk0 + ci * (CT / BS) + wbyte / TB;
       const bool have = blk < blk1;
       int p = __builtin_amdgcn_readfirstlane(have ? bt[blk] : 0);
       if (p < 0 || p >= a.num_blocks) p = 0;
       const int bytes = have ? TB : 0;                // absent: loads give 0
-      const uint32_t off = static_cast<uint32_t>(wbyte % TB + 16 * lane);
+      const uint32_t off = static_cast<uint32_t>(wbyte % TB + PB * lane);
       ld_stream(st.k[k], tile_rsrc(a.k_cache + p * block_stride + head_off, bytes), off, 0);
       ld_stream(st.v[k], tile_rsrc(a.v_cache + p * block_stride + head_off, bytes), off, 0);
     }
   };
-  // V slots past t1 may hold anything (NaN in a tail block): they are
-  // zeroed here, once per chunk, so that P = 0 times them gives 0. K needs
-  // nothing: the scores of those slots are replaced by -inf.
+  // into LDS as bf16. V slots past t1 may hold anything (NaN in a tail
+  // block): they are zeroed here, once per chunk, so that P = 0 times them
+  // gives 0. K needs nothing: the scores of those slots are replaced by -inf.
   auto commit = [&](Stage& st, int buf, int ci) {
     const int tok0 = t0 + ci * CT;
 #pragma unroll
     for (int k = 0; k < PIECES; ++k) {
-      const int e = threadIdx.x + 256 * k;
-      if (tok0 + CT > t1 && tok0 + (16 * e) / RB >= t1) st.v[k] = make_uint4(0, 0, 0, 0);
-      const int row = (16 * e) / RB, col = (16 * e) % RB;
-      *reinterpret_cast<uint4*>(&sk[buf][row * LR + col]) = st.k[k];
-      *reinterpret_cast<uint4*>(&sv[buf][row * LRV + col]) = st.v[k];
+      if constexpr (FMT == kFmtBf16) {
+        // 16 bytes of bf16 at bytes 16 e of the chunk, stored as loaded
+        const int e = threadIdx.x + 256 * k;
+        if (tok0 + CT > t1 && tok0 + (16 * e) / RB >= t1) st.v[k] = make_uint4(0, 0, 0, 0);
+        const int row = (16 * e) / RB, col = (16 * e) % RB;
+        *reinterpret_cast<uint4*>(&sk[buf][row * LR + col]) = st.k[k];
+        *reinterpret_cast<uint4*>(&sv[buf][row * LRV + col]) = st.v[k];
+      } else {
+        const int src = PB * (threadIdx.x + 256 * k);   // cache byte within the chunk
+        const int row = src / RBS;
+        const int col = (src % RBS) * (RB / RBS);       // its bf16 byte within the row
+        if (tok0 + CT > t1 && tok0 + row >= t1) st.v[k] = PT{};
+        store_bf16<FMT>(&sk[buf][row * LR + col], st.k[k]);
+        store_bf16<FMT>(&sv[buf][row * LRV + col], st.v[k]);
+      }
     }
-  };
-
-  auto v_tok = [&](int s) -> int {
-    const int s8 = s & 7;
-    return 16 * (2 * (s >> 3) + (s8 >> 2)) + 4 * g4 + (s8 & 3);
   };
 
   float m_ref[TPW], m_raw[TPW], l[TPW];
@@ -222,11 +267,10 @@ void multi_query_lds_mfma(DecodeArgs a) {
     for (int jj = 0; jj < NJ; ++jj) acc[t][jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  // per-lane LDS offsets: K token c at dims of lane group g4; V token 4 g4 at
-  // dims DPL c (FP8, FP4); bf16 V is read transposed: lane (c, g4) addresses
-  // token 4 g4 + c / 4, dims 4 (c % 4) .. of a 16-dim column block
+  // per-lane LDS offsets: K token c at dims of lane group g4; V is read
+  // transposed: lane (c, g4) addresses token 4 g4 + c / 4, dims 4 (c % 4) ..
+  // of a 16-dim column block
   const int k_lane = c * LR + 16 * g4;
-  const int v_lane = 4 * g4 * LRV + VB * c;
   const int v_tr = (4 * g4 + c / 4) * LRV + 8 * (c % 4);
   // A step's chunks go through three phases: the scores of every chunk (K Q^T
   // on the matrix cores, masked), one lazy-rescale check over all of them,
@@ -249,22 +293,8 @@ void multi_query_lds_mfma(DecodeArgs a) {
 #pragma unroll
       for (int rg = 0; rg < NRG; ++rg) {
         const uint8_t* kt = kl_ + k_lane + 16 * rg * LR;   // this lane's K token 16 rg + c
-        bf16x8_t kop;
-        if constexpr (FMT == kFmtBf16) {
-          kop = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kt + 64 * kk));
-        } else if constexpr (FP4) {
-          // 32 codes at dims 32 g4 .., of which this step uses the 8 at 8 kk
-          const uint32_t w = word(*reinterpret_cast<const uint4*>(kt), kk);
-          kop = as_bf16x8(fp4x2_to_bf16x2<0>(w), fp4x2_to_bf16x2<1>(w),
-                          fp4x2_to_bf16x2<2>(w), fp4x2_to_bf16x2<3>(w));
-        } else {
-          // 16 FP8 codes at dims 64 (kk / 2) + 16 g4, of which this step uses 8
-          const uint4 w = *reinterpret_cast<const uint4*>(kt + 64 * (kk >> 1));
-          const uint32_t w0 = (kk & 1) ? w.z : w.x;
-          const uint32_t w1 = (kk & 1) ? w.w : w.y;
-          kop = as_bf16x8(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
-                          fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
-        }
+        const bf16x8_t kop =
+            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kt + 64 * kk));
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
           sc[rg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[t][kk], sc[rg][t], 0, 0, 0);
@@ -350,63 +380,20 @@ void multi_query_lds_mfma(DecodeArgs a) {
         pop_hi[t] = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
         pop_lo[t] = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
       }
-      if constexpr (FMT == kFmtBf16) {
-        // V^T operand of dims 16 jj ..: tokens 4 g4 .. (first half) and
-        // 16 + 4 g4 .. (second half) of the k-step, straight from LDS
+      // V^T operand of dims 16 jj ..: tokens 4 g4 .. (first half) and
+      // 16 + 4 g4 .. (second half) of the k-step, straight from LDS
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          const uint8_t* vt = vl_ + v_tr + 32 * ks * LRV + 32 * jj;
-          const uint2 v0 = lds_read_tr16(vt);
-          const uint2 v1 = lds_read_tr16(vt + 16 * LRV);
-          const bf16x8_t vop = as_bf16x8(v0.x, v0.y, v1.x, v1.y);
+      for (int jj = 0; jj < NJ; ++jj) {
+        const uint8_t* vt = vl_ + v_tr + 32 * ks * LRV + 32 * jj;
+        const uint2 v0 = lds_read_tr16(vt);
+        const uint2 v1 = lds_read_tr16(vt + 16 * LRV);
+        const bf16x8_t vop = as_bf16x8(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
-          for (int t = 0; t < TPW; ++t) {
-            acc[t][jj] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi[t], acc[t][jj], 0, 0, 0);
-            acc[t][jj] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[t], acc[t][jj], 0, 0, 0);
-          }
-        }
-      } else {
-        uint32_t vw[8][FP4 ? 1 : VW];
-        Fp4Pair vp[4];                   // FP4: slots 2u, 2u + 1 interleaved
-        VT vraw[8];
-#pragma unroll
-        for (int si = 0; si < 8; ++si) {
-          const int tv = v_tok(8 * ks + si);
-          vraw[si] = *reinterpret_cast<const VT*>(vl_ + v_lane + (tv - 4 * g4) * LRV);
-          if constexpr (FP4) {
-            if (si % 2 == 1) vp[si / 2] = fp4_interleave(word(vraw[si - 1], 0), word(vraw[si], 0));
-          } else {
-#pragma unroll
-            for (int w = 0; w < VW / 2; ++w) {
-              const uint32_t x = word(vraw[si], w);
-              vw[si][2 * w] = fp8x2_to_bf16x2<false>(x);
-              vw[si][2 * w + 1] = fp8x2_to_bf16x2<true>(x);
-            }
-          }
-        }
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          uint32_t t4[4];
-          if constexpr (FP4) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) t4[u] = fp4_pair_dim(vp[u], jj);
-          } else {
-            const int w = jj >> 1;
-            const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              t4[u] = __builtin_amdgcn_perm(vw[2 * u + 1][w], vw[2 * u][w], sel);
-          }
-          const bf16x8_t vop = as_bf16x8(t4[0], t4[1], t4[2], t4[3]);
-#pragma unroll
-          for (int t = 0; t < TPW; ++t) {
-            acc[t][jj] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi[t], acc[t][jj], 0, 0, 0);
-            acc[t][jj] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[t], acc[t][jj], 0, 0, 0);
-          }
+        for (int t = 0; t < TPW; ++t) {
+          acc[t][jj] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi[t], acc[t][jj], 0, 0, 0);
+          acc[t][jj] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[t], acc[t][jj], 0, 0, 0);
         }
       }
     }
@@ -431,16 +418,10 @@ void multi_query_lds_mfma(DecodeArgs a) {
       float sa_[1][TPW][4 * NRG], sb_[1][TPW][4 * NRG];
       scores(2 * h, ci, sa_[0]);
       rescale(std::integral_constant<int, 1>{}, sa_);
-      if constexpr (FMT == kFmtBf16) {
-        // the second chunk's scores are issued beside the first chunk's
-        // weights and P V products (one basic block); quantised chunks are
-        // twice as long, and their score registers would not fit twice
-        if (two) scores(2 * h + 1, ci + 1, sb_[0]);
-        accumulate(2 * h, sa_[0]);
-      } else {
-        accumulate(2 * h, sa_[0]);
-        if (two) scores(2 * h + 1, ci + 1, sb_[0]);
-      }
+      // the second chunk's scores are issued beside the first chunk's
+      // weights and P V products (one basic block)
+      if (two) scores(2 * h + 1, ci + 1, sb_[0]);
+      accumulate(2 * h, sa_[0]);
       if (two) {
         rescale(std::integral_constant<int, 1>{}, sb_);
         accumulate(2 * h + 1, sb_[0]);
@@ -452,10 +433,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
   }
 
   // outputs: lane (c, g4) holds, of row 16 t + c, dims 16 jj + 4 g4 + i
-  // (bf16: V read transposed) or DPL (4 g4 + i) + jj (FP8, FP4)
-  auto odim = [&](int jj, int i) -> int {
-    return QNT ? DPL * (4 * g4 + i) + jj : 16 * jj + 4 * g4 + i;
-  };
+  auto odim = [&](int jj, int i) -> int { return 16 * jj + 4 * g4 + i; };
   const float vscale = QNT ? a.v_scale[g] : 1.0f;
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
@@ -678,43 +656,17 @@ void multi_query_lds_pp(DecodeArgs a) {
     const int byte = (PB * (threadIdx.x + NT * x)) % RBS;       // cache byte within the row
     return st_row(x) * LR + (FP4 ? 4 * byte : FP8 ? 2 * byte : byte);
   };
-  // a piece as bf16: 16 bytes of bf16 as they are, 16 FP8 or FP4 codes widened
-  // exactly into 32 bytes (`zero`: a V slot past t1, which may hold anything;
-  // P = 0 times it must give 0)
-  auto store = [&](uint8_t* dst, const VT& w, bool zero) __attribute__((always_inline)) {
-    if constexpr (FMT == kFmtBf16) {
-      *reinterpret_cast<uint4*>(dst) = zero ? make_uint4(0, 0, 0, 0) : w;
-    } else {
-      uint32_t h[8];
-      if constexpr (FP8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          h[2 * i] = fp8x2_to_bf16x2<false>(word(w, i));
-          h[2 * i + 1] = fp8x2_to_bf16x2<true>(word(w, i));
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          h[4 * i] = fp4x2_to_bf16x2<0>(word(w, i));
-          h[4 * i + 1] = fp4x2_to_bf16x2<1>(word(w, i));
-          h[4 * i + 2] = fp4x2_to_bf16x2<2>(word(w, i));
-          h[4 * i + 3] = fp4x2_to_bf16x2<3>(word(w, i));
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) h[i] = zero ? 0u : h[i];
-      *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
-      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(h[4], h[5], h[6], h[7]);
-    }
-  };
+  // into LDS as bf16 (store_bf16); V slots past t1 may hold anything (NaN in
+  // a tail block) and are zeroed so that P = 0 times them gives 0. K needs
+  // nothing: those scores become -inf.
   auto commit_k = [&](const Piece& w, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int x = 0; x < PIECES; ++x) store(&sk[buf][st_off(x)], w[x], false);
+    for (int x = 0; x < PIECES; ++x) store_bf16<FMT>(&sk[buf][st_off(x)], w[x]);
   };
   auto commit_v = [&](const Piece& w, int buf, int ci) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < PIECES; ++x)
-      store(&sv[buf][st_off(x)], w[x], t0 + ci * CT + st_row(x) >= t1);
+      store_bf16<FMT>(&sv[buf][st_off(x)], zero_if(w[x], t0 + ci * CT + st_row(x) >= t1));
   };
 
   float m_ref[TPW], m_raw[TPW], l[TPW];
@@ -812,9 +764,12 @@ void multi_query_lds_pp(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[t][4 * rg + i] = sc[rg][t][i];
   };
-  // the matrix phase's order: 12 LDS reads, then one read per two products
-  // (48 reads and 96 products in all)
+  // the matrix phase's order: (bf16) the chunk's LDS writes, then 12 LDS
+  // reads, then one read per two products (48 reads and 96 products in all).
+  // FP8 and FP4 writes are left free: pinned first, their widening delays the
+  // first products (measured 4-7% slower).
   auto matrix_order = [&]() __attribute__((always_inline)) {
+    if constexpr (FMT == kFmtBf16) __builtin_amdgcn_sched_group_barrier(0x200, 2 * PIECES, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
     for (int i = 0; i < 36; ++i) {
