@@ -19,7 +19,7 @@ namespace pkv {
 
 // ---------------------------------------------------------------------------
 // Split-K reduce, two shapes chosen by the partition count:
-//   <= 32 partitions: one wave per (sequence, query head) (below);
+//   <= 32 partitions: D / 4 lanes per (sequence, query head) (below);
 //   more: one 256-thread workgroup per (sequence, query head). Thread t owns
 //   output dims 4*(t % (D/4)) .. +4 for the partitions j = t / (D/4)
 //   (mod 256 / (D/4)), reading 16 bytes per partition row, so a long list of
@@ -67,59 +67,107 @@ __device__ __forceinline__ int row_partitions(const ReduceRows& r, int64_t row) 
   return last > 0 ? min((last + r.partition - 1) / r.partition, r.P_max) : 0;
 }
 
-// Few partitions per sequence: one wave per (sequence, query head), lanes own
-// output dims, weights broadcast by cross-lane reads (no LDS, no barrier).
+// Few partitions per sequence: D / 4 lanes per output row (two rows per wave
+// at d 128, four at d 64), each lane owning 4 output dims. A lane first loads
+// the m and l of up to two of its row's partitions, so the row's maximum and
+// weights w_j = l_j 2^(m_j - M) take one memory round trip and a few
+// cross-lane steps; the partial outputs are then loaded 16 bytes per lane,
+// eight partitions at a time, each weight broadcast from the lane that holds
+// it. A row with np partitions thus waits for about 1 + np / 8 round trips
+// instead of one per partition.
 template <int D>
 __global__ __launch_bounds__(256) void splitk_reduce_wave_kernel(
     void* __restrict__ out, int out_dtype, const float* __restrict__ m,
     const float* __restrict__ l, const float* __restrict__ o,
     ReduceRows rows, int64_t n_rows) {
-  constexpr int DL = D / 64;                         // output dims per lane
+  constexpr int LPR = D / 4;                         // lanes per row
+  constexpr int RPW = 64 / LPR;                      // rows per wave
+  constexpr int WPR = (kWaveReduceMaxPartitions + LPR - 1) / LPR;   // weights per lane
+  constexpr int UNROLL = 8;                          // partition rows loaded together
   const int lane = threadIdx.x & 63;
-  const int64_t bh = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (bh >= n_rows) return;                          // whole wave
+  const int sub = lane / LPR;                        // the lane's row within the wave
+  const int lr = lane % LPR;                         // its dims 4 lr .. 4 lr + 3
+  const int64_t bh =
+      (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * RPW + sub;
+  const bool live = bh < n_rows;
   const int P_max = rows.P_max;
-  const int np1 = row_partitions(rows, bh);
-  const int np = np1 + rows.P2;
-  const float* mb = m + static_cast<int64_t>(bh) * P_max;
-  const float* lb = l + static_cast<int64_t>(bh) * P_max;
-  const float* ob = o + static_cast<int64_t>(bh) * P_max * D;
-  const float* mb2 = rows.m2 + static_cast<int64_t>(bh) * rows.P2;
-  const float* lb2 = rows.l2 + static_cast<int64_t>(bh) * rows.P2;
-  const float* ob2 = rows.o2 + static_cast<int64_t>(bh) * rows.P2 * D;
-  auto pm = [&](int j) { return j < np1 ? mb[j] : mb2[j - np1]; };
-  auto pl = [&](int j) { return j < np1 ? lb[j] : lb2[j - np1]; };
+  const int np1 = live ? row_partitions(rows, bh) : 0;
+  const int np = live ? np1 + rows.P2 : 0;
+  const int64_t r = live ? bh : 0;
+  const float* mb = m + r * P_max;
+  const float* lb = l + r * P_max;
+  const float* ob = o + r * P_max * D;
+  const float* mb2 = rows.m2 + r * rows.P2;
+  const float* lb2 = rows.l2 + r * rows.P2;
+  const float* ob2 = rows.o2 + r * rows.P2 * D;
   auto po = [&](int j) { return j < np1 ? ob + static_cast<int64_t>(j) * D
                                         : ob2 + static_cast<int64_t>(j - np1) * D; };
 
+  // partitions lr + LPR k of this row: m and l, the row's maximum and weights
+  float mj[WPR], lj[WPR];
   float mx = -INFINITY;
-  for (int jj = lane; jj < np; jj += 64) mx = fmaxf(mx, pm(jj));
-  const float M = wave_max(mx);
-  float acc[DL];
 #pragma unroll
-  for (int k = 0; k < DL; ++k) acc[k] = 0.0f;
-  float lsum = 0.0f;
-  for (int j0 = 0; j0 < np; j0 += 64) {
-    const int jl = j0 + lane;
-    const float wl = jl < np ? pl(jl) * fast_exp2(pm(jl) - M) : 0.0f;
-    lsum += wl;
-    const int n = min(64, np - j0);
-    for (int jj = 0; jj < n; ++jj) {
-      const float wj = __shfl(wl, jj);
-      const float* row = po(j0 + jj);
+  for (int k = 0; k < WPR; ++k) {
+    const int j = lr + LPR * k;
+    mj[k] = -INFINITY;
+    lj[k] = 0.0f;
+    if (j < np) {
+      mj[k] = j < np1 ? mb[j] : mb2[j - np1];
+      lj[k] = j < np1 ? lb[j] : lb2[j - np1];
+    }
+    mx = fmaxf(mx, mj[k]);
+  }
 #pragma unroll
-      for (int k = 0; k < DL; ++k) acc[k] = fmaf(wj, row[lane + 64 * k], acc[k]);
+  for (int off = LPR / 2; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float w[WPR];
+  float ls = 0.0f;
+#pragma unroll
+  for (int k = 0; k < WPR; ++k) {
+    w[k] = lr + LPR * k < np && mj[k] != -INFINITY ? lj[k] * fast_exp2(mj[k] - mx) : 0.0f;
+    ls += w[k];
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) ls += __shfl_xor(ls, off);
+
+  // every partition row: weight from lane sub LPR + j % LPR, 16 bytes per lane
+  int npw = np;                                      // the wave's largest np
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) npw = max(npw, __shfl_xor(npw, off));
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int j0 = 0; j0 < npw; j0 += UNROLL) {
+    float4 v[UNROLL];
+    float wj[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int j = j0 + u;
+      float wk = 0.0f;
+#pragma unroll
+      for (int k = 0; k < WPR; ++k)
+        if (j / LPR == k) wk = __shfl(w[k], sub * LPR + j % LPR);
+      wj[u] = j < np ? wk : 0.0f;
+      v[u] = j < np ? *reinterpret_cast<const float4*>(po(j) + 4 * lr)
+                    : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      acc.x = fmaf(wj[u], v[u].x, acc.x);
+      acc.y = fmaf(wj[u], v[u].y, acc.y);
+      acc.z = fmaf(wj[u], v[u].z, acc.z);
+      acc.w = fmaf(wj[u], v[u].w, acc.w);
     }
   }
-  const float L = wave_sum(lsum);
-#pragma unroll
-  for (int k = 0; k < DL; ++k) {
-    const float v = np > 0 ? acc[k] / L : 0.0f;
-    const int64_t oi = static_cast<int64_t>(bh) * D + lane + 64 * k;
-    if (out_dtype == PKV_FP32)
-      static_cast<float*>(out)[oi] = v;
-    else
-      static_cast<uint16_t*>(out)[oi] = f32_to_bf16_rne(v);
+  if (!live) return;
+  const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;     // no weight at all: zeros
+  const int64_t oi = bh * D + 4 * lr;
+  if (out_dtype == PKV_FP32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + oi) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  } else {
+    uint16_t* ob16 = static_cast<uint16_t*>(out) + oi;
+    ob16[0] = f32_to_bf16_rne(acc.x * inv);
+    ob16[1] = f32_to_bf16_rne(acc.y * inv);
+    ob16[2] = f32_to_bf16_rne(acc.z * inv);
+    ob16[3] = f32_to_bf16_rne(acc.w * inv);
   }
 }
 
@@ -228,7 +276,8 @@ hipError_t launch_splitk_reduce(void* out, int out_dtype, const float* m, const 
                         m2, l2, o2, m2 ? P2 : 0};
   const int64_t n_rows = static_cast<int64_t>(B) * Q * n_q;
   if (P_max + rows.P2 <= kWaveReduceMaxPartitions) {
-    const unsigned grid = static_cast<unsigned>((n_rows + 3) / 4);
+    const int64_t rows_per_block = 4 * (64 / (d / 4));
+    const unsigned grid = static_cast<unsigned>((n_rows + rows_per_block - 1) / rows_per_block);
     if (d == 128)
       splitk_reduce_wave_kernel<128><<<grid, 256, 0, stream>>>(out, out_dtype, m, l, o, rows,
                                                                n_rows);
