@@ -112,21 +112,23 @@ int32_t pick_partition(const pkv_cache_desc* d, int32_t B, int32_t n_q, int32_t 
 }
 
 // Workgroups of a multi-query launch per partition: the LDS kernel takes 128
-// (query, head) rows of a KV head per workgroup (its bf16 ping-pong form 256,
-// at one workgroup per CU instead of two: the same share of a round), the
+// (query, head) rows of a KV head per workgroup (its ping-pong form 256, at
+// one workgroup per CU instead of two: the same share of a round), the
 // register kernel 32 (two 16-row tiles) or one tile. A launch that fills a
-// round of the chip this way
-// needs no split to fill it. On the register kernel it runs in a single pass:
-// splitting would only add partials (fp32, d_head + 2 words per row and
-// partition), which outweigh the K/V it reads. On the LDS kernel a
-// workgroup's time is its compute, proportional to the tokens it attends
-// to, so a batch of different context lengths would end with a tail of its
-// longest sequences; partitions of at most kLdsPartition tokens, dispatched
-// deepest first, spread that work (measured: a 512-token prompt chunk at
-// contexts 4K..64K took 3.33 ms in one pass and 2.98-3.01 ms with partitions
-// of 4096-32768 tokens), at a cost in partials that is small next to the
-// compute. Fewer workgroups split the context as decode does.
-constexpr int32_t kLdsPartition = 16384;
+// round of the chip this way needs no split to fill it. On the register
+// kernel it runs in a single pass: splitting would only add partials (fp32,
+// d_head + 2 words per row and partition), which outweigh the K/V it reads.
+// On the LDS kernels a workgroup's time is its compute, proportional to the
+// tokens it attends to, so a batch of different context lengths would end
+// with a tail of its longest sequences; partitions of at most kLdsPartition
+// tokens, dispatched deepest first, spread that work at a cost in partials
+// that is small next to the compute. Measured on a 512-token prompt chunk at
+// contexts 4K..64K: 3.33 ms in one pass and 2.98-3.01 ms with partitions of
+// 4096-32768 tokens (128-row kernel); with the ping-pong kernel 2.39 ms at
+// 8192, 2.43-2.53 ms at 16384, 2.44-2.47 at 24576, 2.49-2.52 at 4096 and
+// 2.87-2.95 in one pass (one box). Fewer workgroups split the context as
+// decode does.
+constexpr int32_t kLdsPartition = 8192;
 
 int32_t pick_partition_mq(const pkv_cache_desc* d, int32_t B, int32_t Q, int32_t n_q,
                           int32_t max_ctx) {
