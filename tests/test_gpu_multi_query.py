@@ -17,7 +17,7 @@ from oracle import paged as ref
 
 pytestmark = pytest.mark.gpu
 
-MAX_ABS = {W.BF16: 1e-2, W.FP8: 3e-2}
+MAX_ABS = {W.BF16: 1e-2, W.FP8: 3e-2, W.FP4: 3e-2}
 REL_L2 = 1e-4
 DEV = "cuda:0"
 
@@ -167,3 +167,33 @@ def test_negative_zero_and_large_scales(pkv, scale):
         w = W.custom("mqscale", [300, 77, 1029], n_q, 8, 128, 16, W.BF16, seed=90, scale=scale)
         out, expect, ql = run_mq(pkv, w, Q, [Q, min(Q, 77), Q // 2])
         check(out, expect, ql, W.BF16, f"scale {scale} Q {Q}")
+
+
+def random_shapes(n, seed):
+    """Seeded shapes at 64/8 heads, d 128: 160 to 576 rows per KV head, so
+    both LDS kernels run (the ping-pong form at 256 and 512 rows, the 128-row
+    kernel at 160, 320 and 576), every cache format and block size, random
+    context and query lengths, single pass and partitions ending mid-chunk."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = (W.BF16, W.FP8, W.FP4)[i % 3]
+        bs = (16, 32)[i % 2]
+        Q = (64, 32, 64, 40, 20, 32, 72, 64, 40)[i % 9]
+        B = int(rng.integers(1, 4))
+        lens = [int(x) for x in rng.integers(1, 2500, size=B)]
+        qlens = [int(min(c, rng.integers(0, Q + 1))) for c in lens]
+        P = int(rng.choice([0, 0, 64, 256, 1024]))
+        out.append((lens, qlens, Q, bs, dt, P))
+    return out
+
+
+RANDOM = random_shapes(9, 2170)
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[str(i) for i in range(len(RANDOM))])
+def test_multi_query_random_shapes(pkv, case):
+    lens, qlens, Q, bs, dt, P = case
+    w = W.custom("mqrand", lens, 64, 8, 128, bs, dt, seed=2171 + RANDOM.index(case))
+    out, expect, ql = run_mq(pkv, w, Q, qlens, partition_size=P)
+    check(out, expect, ql, dt, f"random {case}")
