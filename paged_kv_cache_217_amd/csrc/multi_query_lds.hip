@@ -846,8 +846,13 @@ void multi_query_lds_pp(DecodeArgs a) {
   // weights of chunk k; each phase ends at a barrier. Role 1 passes one
   // barrier before its first phase and role 0 one after its last, so role 1
   // runs one phase behind: while one wave of a SIMD is in Mk the other is in
-  // W(k-1) or Wk. Both roles run the same code. K of chunk n sits in
-  // sk[n % 2] and V of chunk n in sv[n % 2]; a wave writes its slice of K of
+  // W(k-1) or Wk. Both roles run the same code. Those two extra barriers sit
+  // under a condition that is uniform within a wave but not across the
+  // workgroup: s_barrier counts one arrival per wave, whatever instruction it
+  // is reached at, and every wave reaches the same number of barriers
+  // (2 N + 3 after the role set-up), so each barrier releases all 8 waves.
+  // K of chunk n sits in sk[n % 2] and V of chunk n in sv[n % 2]; a wave
+  // writes its slice of K of
   // chunk k + 1 and of V of chunk k at the start of Mk, so with the lag K of
   // chunk k is complete one phase before role 0 reads it and V of chunk k one
   // phase before role 0's M(k+1), and neither overwrites a buffer before role
