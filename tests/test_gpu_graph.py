@@ -3,7 +3,7 @@
 The library allocates, clears and synchronises nothing itself, so a whole
 step (slot mapping, kv_append, longest-first schedule, partition kernel,
 split-K reduce), a multi-token-query launch and a shared-prefix (cascade)
-call can be captured once and replayed. Each replay, with eager work and synchronisation between replays,
+call can be captured once and replayed, on each multi-query kernel. Each replay, with eager work and synchronisation between replays,
 must reproduce the eager result bit for bit; the eager result is checked
 against the oracle.
 """
@@ -89,12 +89,14 @@ def test_decode_step_replays(pkv, dt, bs, n_q, n_kv):
             torch.cuda.synchronize()
 
 
-def test_multi_query_replays(pkv):
+# 24 queries x 8 heads per KV head run on the 128-row LDS kernel, 64 x 8 on
+# its 256-row ping-pong form
+@pytest.mark.parametrize("Q,qlens", [(24, [24, 7, 24]), (64, [64, 20, 64])])
+def test_multi_query_replays(pkv, Q, qlens):
     w = W.custom("graphmq", [700, 33, 1500], 64, 8, 128, 16, W.BF16, seed=171)
     kc, vc, _, _ = W.make_cache(w)
-    Q = 24
     q = W.make_multi_query(w, Q).to(DEV)
-    ql = torch.tensor([24, 7, 24], dtype=torch.int32, device=DEV)
+    ql = torch.tensor(qlens, dtype=torch.int32, device=DEV)
     kd, vd = kc.to(DEV), vc.to(DEV)
     bt = torch.from_numpy(w.block_tables).to(DEV)
     cl = torch.from_numpy(w.context_lens).to(DEV)
@@ -130,9 +132,13 @@ def test_multi_query_replays(pkv):
         assert torch.equal(out, eager), f"replay {r}"
 
 
-def test_cascade_replays(pkv):
-    # prefix pass, suffix schedule and partitions, two-source merge
-    plen, suffix, n_q, n_kv, bs = 2048, [5, 700, 0, 2500, 33, 1200], 64, 8, 16
+# prefix pass, suffix schedule and partitions, two-source merge; 6 sharers
+# give the prefix pass 48 rows per KV head (register kernel), 40 give 320
+# (LDS kernel) and 64 give 512 (its ping-pong form)
+@pytest.mark.parametrize("n_seq", [6, 40, 64])
+def test_cascade_replays(pkv, n_seq):
+    plen, n_q, n_kv, bs = 2048, 64, 8, 16
+    suffix = ([5, 700, 0, 2500, 33, 1200] * 11)[:n_seq]
     w = W.custom("graphcas", [plen] + suffix, n_q, n_kv, 128, bs, W.BF16, seed=172)
     kc, vc, _, _ = W.make_cache(w)
     pt = torch.from_numpy(w.block_tables[0, :plen // bs].copy()).to(DEV)
