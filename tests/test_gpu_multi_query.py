@@ -197,3 +197,25 @@ def test_multi_query_random_shapes(pkv, case):
     w = W.custom("mqrand", lens, 64, 8, 128, bs, dt, seed=2171 + RANDOM.index(case))
     out, expect, ql = run_mq(pkv, w, Q, qlens, partition_size=P)
     check(out, expect, ql, dt, f"random {case}")
+
+
+# Head groups other than 8 on the 256-row ping-pong kernel: a row r of a
+# workgroup is query r // G, head r % G, so with G not a power of two the
+# rows of one query straddle the row tiles and the workgroups. Each shape
+# has 256 or more rows per KV head and pads them by at most a tenth.
+HEAD_GROUPS = [
+    # n_q, n_kv, Q, lens, qlens, bs, dtype, partition
+    (64, 1, 8, [900, 1500], [8, 5], 16, W.BF16, 0),           # MQA, 512 rows
+    (40, 8, 100, [700, 1300], [100, 64], 16, W.FP8, 256),     # G 5, 500 rows
+    (24, 8, 170, [300, 1100], [170, 170], 32, W.BF16, 0),     # G 3, 510 rows
+    (32, 4, 64, [1200, 90], [64, 64], 32, W.FP4, 1024),       # G 8 over 4 KV heads
+    (32, 16, 128, [600], [128], 32, W.FP8, 0),                # G 2, 256 rows
+]
+
+
+@pytest.mark.parametrize("case", HEAD_GROUPS, ids=[f"G{c[0] // c[1]}-{c[6]}" for c in HEAD_GROUPS])
+def test_multi_query_head_groups_ping_pong(pkv, case):
+    n_q, n_kv, Q, lens, qlens, bs, dt, P = case
+    w = W.custom("mqgroups", lens, n_q, n_kv, 128, bs, dt, seed=2180 + HEAD_GROUPS.index(case))
+    out, expect, ql = run_mq(pkv, w, Q, qlens, partition_size=P)
+    check(out, expect, ql, dt, f"head groups {case[:3]}")
