@@ -478,12 +478,27 @@ def bench_cascade(args, w, pkv, W, np, torch, dev):
         dtype=torch.uint8, device=dev)
     P = pkv.default_partition_size(caches[0][0], B, n_q, max_ctx)
     dws, _ = pkv.make_workspace(caches[0][0], B, n_q, max_ctx, P)
+    # longest-first lists, built once per step for all layers (as the decode
+    # step does): the suffix partitions' for the cascade, the sequences' for
+    # plain decode
+    Ps = pkv.cascade_suffix_partition(caches[0][0], B, n_q, plen, max_s, args.prefix_partition,
+                                      args.partition)
+    c_sched = torch.empty(max(32, pkv.lib().pkv_decode_schedule_bytes(B, max_s, max(Ps, 16))) // 4,
+                          dtype=torch.int32, device=dev)
+    d_sched = torch.empty(max(32, pkv.lib().pkv_decode_schedule_bytes(B, max_ctx, P)) // 4,
+                          dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     log(f"[bench] workload {w.name}: B={B} prefix={plen} suffix {slen_np.min()}..{max_s} "
-        f"layers={layers}")
+        f"(partition {Ps}) layers={layers}")
 
     def step(cascade, ev=None):
         pkv.slot_mapping(bt, pos, bs, out=slots)
+        if cascade:
+            sched = pkv.cascade_schedule(caches[0][0], slen, n_q, plen, max_s,
+                                         args.prefix_partition, args.partition,
+                                         out=c_sched) if args.schedule else None
+        else:
+            sched = pkv.decode_schedule(cl, max_ctx, P, out=d_sched) if args.schedule else None
         for layer in range(layers):
             kc, vc, ks, vs = caches[layer]
             pkv.kv_append(kc, vc, k_new[layer], v_new[layer], slots, ks, vs)
@@ -493,10 +508,11 @@ def bench_cascade(args, w, pkv, W, np, torch, dev):
                 pkv.cascade_decode_attention(q[layer], kc, vc, pt, plen, st, slen, w.scale, max_s,
                                              prefix_partition=args.prefix_partition,
                                              suffix_partition=args.partition, out=out,
-                                             workspace=cws)
+                                             workspace=cws, schedule=sched)
             else:
                 pkv.paged_decode_attention(q[layer], kc, vc, bt, cl, w.scale, max_ctx,
-                                           partition_size=P, out=out, workspace=dws)
+                                           partition_size=P, out=out, workspace=dws,
+                                           schedule=sched)
             if ev is not None:
                 ev[layer][1].record(stream)
 

@@ -392,18 +392,32 @@ pkv_status pkv_gather_kv(const pkv_cache_desc* desc, void* k_out, void* v_out,
  * multiples; 0 picks them. workspace: at least
  * pkv_cascade_workspace_bytes(...) for the same arguments. Other arguments
  * as for pkv_paged_decode_attention.
+ *
+ * suffix_schedule (optional): when the suffixes take more than one partition
+ * the call runs them longest first, from a list it builds in its workspace,
+ * or from this one: pkv_decode_schedule(suffix_lens, B, max_suffix_len,
+ * pkv_cascade_suffix_partition(...), ...) built once per step, since the list
+ * depends only on the suffix lengths, serves every layer (the rules of
+ * pkv_paged_decode_attention's schedule apply). Ignored when the suffixes take
+ * one partition. pkv_cascade_suffix_partition returns the suffix partition
+ * size the call resolves for the same arguments, or 0 when there is no suffix
+ * or the arguments are invalid.
  * ------------------------------------------------------------------------- */
 size_t pkv_cascade_workspace_bytes(const pkv_cache_desc* desc, int32_t B, int32_t n_q,
                                    int32_t prefix_len, int32_t prefix_partition,
                                    int32_t max_suffix_len, int32_t suffix_partition);
+
+int32_t pkv_cascade_suffix_partition(const pkv_cache_desc* desc, int32_t B, int32_t n_q,
+                                     int32_t prefix_len, int32_t prefix_partition,
+                                     int32_t max_suffix_len, int32_t suffix_partition);
 
 pkv_status pkv_cascade_decode_attention(
     const pkv_cache_desc* desc, void* out, int32_t out_dtype, const void* q, const void* k_cache,
     const void* v_cache, const int32_t* prefix_table, int32_t prefix_len,
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* suffix_lens,
     int32_t B, int32_t n_q, int32_t max_suffix_len, float scale, const float* k_scale,
-    const float* v_scale, int32_t prefix_partition, int32_t suffix_partition, void* workspace,
-    size_t workspace_bytes, void* stream);
+    const float* v_scale, int32_t prefix_partition, int32_t suffix_partition,
+    const void* suffix_schedule, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Swap of KV blocks to host memory and back ([LLMI] "9. Failure modes and

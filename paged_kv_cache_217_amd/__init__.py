@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     STATIC_SCRATCH_BYTES,
     cache_desc,
     cascade_decode_attention,
+    cascade_schedule,
+    cascade_suffix_partition,
     copy_blocks,
     debug_check,
     decode_schedule,

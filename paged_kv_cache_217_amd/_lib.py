@@ -79,9 +79,11 @@ SIGNATURES = {
                                                _f32, _vp, _vp, _i32, _vp, _sz, _vp]),
     "pkv_cascade_workspace_bytes": (_sz, [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32,
                                           _i32, _i32]),
+    "pkv_cascade_suffix_partition": (_i32, [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32,
+                                            _i32, _i32]),
     "pkv_cascade_decode_attention": (_i32, [ctypes.POINTER(CacheDesc), _vp, _i32, _vp, _vp, _vp,
                                             _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
-                                            _vp, _vp, _i32, _i32, _vp, _sz, _vp]),
+                                            _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
     "pkv_decode_schedule_bytes": (_sz, [_i32, _i32, _i32]),
     "pkv_decode_schedule": (_i32, [_vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "pkv_splitk_reduce": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -406,10 +408,32 @@ def paged_multi_query_attention(q, query_lens, k_cache, v_cache, block_tables, c
     return out
 
 
+def cascade_suffix_partition(k_cache, B, n_q, prefix_len, max_suffix_len, prefix_partition=0,
+                             suffix_partition=0):
+    """Suffix partition size a cascade call resolves for these arguments (0: none)."""
+    return int(lib().pkv_cascade_suffix_partition(
+        ctypes.byref(cache_desc(k_cache)), int(B), int(n_q), int(prefix_len),
+        int(prefix_partition), int(max_suffix_len), int(suffix_partition)))
+
+
+def cascade_schedule(k_cache, suffix_lens, n_q, prefix_len, max_suffix_len, prefix_partition=0,
+                     suffix_partition=0, out=None, stream=None):
+    """Longest-first list of a cascade call's suffix partitions, to build once
+    per step and pass as `schedule` to every layer's call (see pkv.h); None
+    when the suffixes take a single partition."""
+    B = suffix_lens.numel()
+    P = cascade_suffix_partition(k_cache, B, n_q, prefix_len, max_suffix_len, prefix_partition,
+                                 suffix_partition)
+    if P <= 0 or -(-int(max_suffix_len) // P) <= 1:
+        return None
+    return decode_schedule(suffix_lens, max_suffix_len, P, out=out, stream=stream)
+
+
 def cascade_decode_attention(q, k_cache, v_cache, prefix_table, prefix_len, block_tables,
                              suffix_lens, scale, max_suffix_len, k_scale=None, v_scale=None,
                              prefix_partition=0, suffix_partition=0, out=None,
-                             out_dtype=torch.float32, workspace=None, stream=None):
+                             out_dtype=torch.float32, workspace=None, schedule=None,
+                             stream=None):
     """Decode attention over prefix_table ++ block_tables[b] with the shared
     prefix's K/V read once for the whole batch (see pkv.h)."""
     desc, B, n_q, d = _decode_common(q, k_cache, v_cache, block_tables, suffix_lens,
@@ -427,13 +451,15 @@ def cascade_decode_attention(q, k_cache, v_cache, prefix_table, prefix_len, bloc
             int(max_suffix_len), int(suffix_partition)))
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     _check_workspace(workspace, q.device)
+    if schedule is not None:
+        _need(schedule, torch.int32, "schedule")
     _check(lib().pkv_cascade_decode_attention(
         ctypes.byref(desc), _ptr(out), _out_code(out.dtype), _ptr(q), _ptr(k_cache),
         _ptr(v_cache), _ptr(prefix_table) if prefix_len else None, int(prefix_len),
         _ptr(block_tables), block_tables.shape[1], _ptr(suffix_lens), B, n_q,
         int(max_suffix_len), float(scale), _ptr(k_scale), _ptr(v_scale), int(prefix_partition),
-        int(suffix_partition), _ptr(workspace), workspace.numel(), _stream(stream)),
-        "pkv_cascade_decode_attention")
+        int(suffix_partition), _ptr(schedule), _ptr(workspace), workspace.numel(),
+        _stream(stream)), "pkv_cascade_decode_attention")
     return out
 
 

@@ -623,13 +623,23 @@ size_t pkv_cascade_workspace_bytes(const pkv_cache_desc* desc, int32_t B, int32_
   return pl.prefix_bytes + pl.suffix_bytes + pl.schedule_bytes;
 }
 
+int32_t pkv_cascade_suffix_partition(const pkv_cache_desc* desc, int32_t B, int32_t n_q,
+                                     int32_t prefix_len, int32_t prefix_partition,
+                                     int32_t max_suffix_len, int32_t suffix_partition) {
+  CascadePlan pl;
+  if (plan_cascade(desc, B, n_q, prefix_len, prefix_partition, max_suffix_len,
+                   suffix_partition, &pl) != PKV_OK)
+    return 0;
+  return pl.Ps;
+}
+
 pkv_status pkv_cascade_decode_attention(
     const pkv_cache_desc* desc, void* out, int32_t out_dtype, const void* q, const void* k_cache,
     const void* v_cache, const int32_t* prefix_table, int32_t prefix_len,
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* suffix_lens,
     int32_t B, int32_t n_q, int32_t max_suffix_len, float scale, const float* k_scale,
-    const float* v_scale, int32_t prefix_partition, int32_t suffix_partition, void* workspace,
-    size_t workspace_bytes_, void* stream) {
+    const float* v_scale, int32_t prefix_partition, int32_t suffix_partition,
+    const void* suffix_schedule, void* workspace, size_t workspace_bytes_, void* stream) {
   CascadePlan pl;
   pkv_status st = plan_cascade(desc, B, n_q, prefix_len, prefix_partition, max_suffix_len,
                                suffix_partition, &pl);
@@ -709,10 +719,16 @@ pkv_status pkv_cascade_decode_attention(
     a.ws_o = wsuf.o;
     a.write_partials = true;
     if (pl.schedule_bytes > 0) {
-      int32_t* sched = reinterpret_cast<int32_t*>(ws + pl.prefix_bytes + pl.suffix_bytes);
-      hipError_t e = pkv::launch_decode_schedule(suffix_lens, B, pl.Ps, pl.Ps_max, sched, s);
-      if (e != hipSuccess) return PKV_ERR_HIP;
+      // the caller's longest-first list, or one built here
+      const void* sched = suffix_schedule;
+      if (!sched) {
+        int32_t* own = reinterpret_cast<int32_t*>(ws + pl.prefix_bytes + pl.suffix_bytes);
+        hipError_t e = pkv::launch_decode_schedule(suffix_lens, B, pl.Ps, pl.Ps_max, own, s);
+        if (e != hipSuccess) return PKV_ERR_HIP;
+        sched = own;
+      }
       st = attach_schedule(&a, sched);
+      if (st == PKV_OK && g_debug && suffix_schedule) st = debug_schedule(s, a);
       if (st != PKV_OK) return st;
     }
     a.wave_partitions = a.schedule == nullptr && use_wave_partitions(a.partition);

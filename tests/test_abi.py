@@ -143,6 +143,21 @@ def test_default_partition_size_is_a_block_multiple():
         assert -(-ctx // P) <= 8192
 
 
+def test_cascade_suffix_partition_resolves_like_the_call():
+    L = _lib.lib()
+    d = _desc(num_blocks=8192, n_kv=8)
+    part = lambda *a: L.pkv_cascade_suffix_partition(ctypes.byref(d), *a)
+    P = part(64, 64, 16384, 0, 3978, 0)                    # library default: at most 2048
+    assert 0 < P <= 2048 and P % 16 == 0
+    assert part(64, 64, 16384, 0, 3978, 512) == 512        # explicit
+    assert part(64, 64, 16384, 0, 0, 0) == 0               # no suffix
+    assert part(64, 60, 16384, 0, 3978, 0) == 0            # invalid: 60 heads over 8
+    assert part(64, 64, 16384, 0, 3978, 24) == 0           # invalid: not a block multiple
+    # the workspace it implies: suffix partials for ceil(3978 / P) partitions
+    ws = L.pkv_cascade_workspace_bytes(ctypes.byref(d), 64, 64, 0, 0, 3978, 512)
+    assert ws >= pkv.decode_workspace_bytes(64, 64, 128, 3978, 512)
+
+
 def test_other_entry_points_validate():
     L = _lib.lib()
     fake = ctypes.c_void_p(0x1000)
@@ -178,7 +193,7 @@ def test_fp4_validation_on_every_attention_entry_point():
     def cascade(d, ks, B=2):
         return L.pkv_cascade_decode_attention(ctypes.byref(d), fake, _lib.PKV_FP32, fake, fake,
                                               fake, fake, 32, fake, 4, fake, B, 4, 32, 0.1, ks,
-                                              ks, 0, 0, fake, 1 << 20, None)
+                                              ks, 0, 0, None, fake, 1 << 20, None)
 
     assert _decode(f64, ks=fake, vs=fake) == _lib.PKV_ERR_UNSUPPORTED
     assert _decode(f128) == _lib.PKV_ERR_INVALID_ARG                  # no scales

@@ -5,7 +5,8 @@ agreement with plain decode attention over the concatenated tables. Cases
 put the prefix rows (sequences x G) on each multi-query kernel (fewer than
 128 rows per KV head, 128 or more, and the ping-pong form at 512, bf16 and
 FP8), cover MQA, an empty prefix, empty suffixes, ragged suffixes with
-NaN-poisoned tails, and explicit partitions.
+NaN-poisoned tails, and explicit partitions; each call is repeated with
+the suffixes' longest-first list built by the caller.
 """
 
 import numpy as np
@@ -66,10 +67,14 @@ def test_cascade_matches_oracle_and_plain_decode(pkv, case):
     t = lambda x: None if x is None else x.to(DEV)
     kd, vd = kc.to(DEV), vc.to(DEV)
     max_s = int(slen.max())
-    out = pkv.cascade_decode_attention(
-        q.to(DEV), kd, vd, torch.from_numpy(pt).to(DEV), plen, torch.from_numpy(tables).to(DEV),
-        torch.from_numpy(slen).to(DEV), w.scale, max_s, k_scale=t(ks), v_scale=t(vs),
-        prefix_partition=Pp, suffix_partition=Ps)
+    args = (q.to(DEV), kd, vd, torch.from_numpy(pt).to(DEV), plen,
+            torch.from_numpy(tables).to(DEV), torch.from_numpy(slen).to(DEV), w.scale, max_s)
+    kw = dict(k_scale=t(ks), v_scale=t(vs), prefix_partition=Pp, suffix_partition=Ps)
+    out = pkv.cascade_decode_attention(*args, **kw)
+    # the suffixes' longest-first list built by the caller (once per step in
+    # a model) instead of by the call: the same work, so the same bits
+    sched = pkv.cascade_schedule(kd, args[6], n_q, plen, max_s, Pp, Ps)
+    out_sched = pkv.cascade_decode_attention(*args, schedule=sched, **kw)
     # the same attention through plain decode on the concatenated tables
     full = np.concatenate([np.tile(pt[:plen // bs], (len(suffix), 1)), tables], axis=1)
     cl = (plen + slen).astype(np.int32)
@@ -81,6 +86,7 @@ def test_cascade_matches_oracle_and_plain_decode(pkv, case):
                                           slen, w.scale, dt,
                                           None if ks is None else ks.numpy(),
                                           None if vs is None else vs.numpy())
+    assert torch.equal(out, out_sched)
     got = out.cpu().double().numpy()
     assert np.all(np.isfinite(got))
     err = np.max(np.abs(got - expect))

@@ -230,3 +230,30 @@ def test_schedule_for_other_geometry_or_items_is_reported(pkv, dbg):
     got = ok.cpu().double().numpy()
     assert np.max(np.abs(got - expect)) <= 1e-2
     assert np.linalg.norm(got - expect) / np.linalg.norm(expect) <= 1e-4
+
+
+def test_cascade_suffix_schedule_for_other_lengths_is_reported(pkv, dbg):
+    # The suffixes' longest-first list a caller builds once per step: one
+    # built for these suffix lengths is accepted, one built for other lengths
+    # (another item count) is reported.
+    bs, B, n_q, n_kv, d = 16, 4, 16, 2, 128
+    w = W.custom("dbg_cas_sched", [64 + 300, 64 + 20, 64 + 180, 64 + 5], n_q, n_kv, d, bs,
+                 W.BF16, seed=68)
+    kd, vd, qd, bt, cl, *_ = setup(w)
+    prefix = bt[0, :4].contiguous()                         # 64 tokens
+    suffix_tables = bt[:, 4:].contiguous()
+    suffix_lens = (cl - 64).contiguous()
+    Ps = 64
+    good = pkv.cascade_schedule(kd, suffix_lens, n_q, 64, 300, 0, Ps)
+    assert good is not None
+    pkv.cascade_decode_attention(qd, kd, vd, prefix, 64, suffix_tables, suffix_lens, w.scale, 300,
+                                 suffix_partition=Ps, schedule=good)
+    torch.cuda.synchronize()
+    assert not reported(pkv)
+    other = suffix_lens.clone()
+    other[0] = 200                                          # two partitions fewer
+    bad = pkv.cascade_schedule(kd, other, n_q, 64, 300, 0, Ps)
+    pkv.cascade_decode_attention(qd, kd, vd, prefix, 64, suffix_tables, suffix_lens, w.scale, 300,
+                                 suffix_partition=Ps, schedule=bad)
+    torch.cuda.synchronize()
+    assert reported(pkv)
