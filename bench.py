@@ -68,7 +68,8 @@ def kernel_hash(sources=KERNEL_SOURCES):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed steps (0: 10 for a multi-layer workload, 20 for a single layer)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gqa_70b",
                     choices=["gqa_70b", "mha_7b", "gqa_70b_fp8", "gqa_70b_fp4", "long_prefix", "tiny",
@@ -125,6 +126,9 @@ def main():
     import workloads as W
 
     w = W.ALL[args.workload]()
+    if args.steps <= 0:
+        # at least 20 timed launches of every kernel
+        args.steps = 10 if (args.layers or w.layers) > 1 else 20
     decode = not (args.copy_calibration or args.swap or w.Q > 1 or w.notes.get("prefix_len"))
     # The processes of the multi-process oracle baseline are started here,
     # before anything touches the GPU (libpkv is not loaded yet, and
