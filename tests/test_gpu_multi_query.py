@@ -219,3 +219,15 @@ def test_multi_query_head_groups_ping_pong(pkv, case):
     w = W.custom("mqgroups", lens, n_q, n_kv, 128, bs, dt, seed=2180 + HEAD_GROUPS.index(case))
     out, expect, ql = run_mq(pkv, w, Q, qlens, partition_size=P)
     check(out, expect, ql, dt, f"head groups {case[:3]}")
+
+
+# bf16 output straight from the LDS kernels (one pass, no reduce): the same
+# values as their fp32 output, rounded to nearest even
+@pytest.mark.parametrize("Q", [20, 64], ids=["128-row", "ping-pong"])
+def test_bf16_output_of_the_lds_kernels_is_the_rounded_fp32_output(pkv, Q):
+    w = W.custom("mqbf_lds", [700, 1900, 64], 64, 8, 128, 16, W.BF16, seed=82)
+    qlens = [Q, Q // 2, Q]
+    out32, expect, ql = run_mq(pkv, w, Q, qlens, partition_size=4096)
+    out16, _, _ = run_mq(pkv, w, Q, qlens, partition_size=4096, out_dtype=torch.bfloat16)
+    check(out32, expect, ql, W.BF16, f"fp32 Q={Q}")
+    assert torch.equal(out16, out32.to(torch.bfloat16))
