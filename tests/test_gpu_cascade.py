@@ -142,3 +142,19 @@ def test_prefix_cache_feeds_cascade_attention(pkv):
     assert np.linalg.norm(got - expect) / np.linalg.norm(expect) <= 1e-4
     assert np.max(np.abs(got - plain.cpu().double().numpy())) <= 2e-3
     bm.close()
+
+
+def test_bf16_output_is_the_rounded_fp32_output(pkv):
+    # the two-source merge writes bf16 from the same fp32 values it would
+    # write as fp32
+    suffix, plen, n_q, n_kv, d, bs = [30, 0, 700, 129], 2048, 64, 8, 128, 16
+    w, kc, vc, ks, vs, pt, tables, slen, q = shared_prefix_case(
+        suffix, plen, n_q, n_kv, d, bs, W.BF16, seed=150)
+    args = (q.to(DEV), kc.to(DEV), vc.to(DEV), torch.from_numpy(pt).to(DEV), plen,
+            torch.from_numpy(tables).to(DEV), torch.from_numpy(slen).to(DEV), w.scale,
+            int(slen.max()))
+    out32 = pkv.cascade_decode_attention(*args)
+    out16 = pkv.cascade_decode_attention(*args, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert out16.dtype == torch.bfloat16
+    assert torch.equal(out16, out32.to(torch.bfloat16))
