@@ -575,6 +575,9 @@ def bench_cascade(args, w, pkv, W, np, torch, dev):
             t = c["traffic_bytes_per_call"]
             result["roofline"].update(traffic=t["total"], traffic_read=t["read"],
                                       traffic_written=t["written"])
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_cascade(w, caches[0], q[0], plen, slen_np,
+                                                      args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
@@ -709,7 +712,85 @@ def bench_multi_query(args, w, pkv, W, np, torch, dev):
                        "multi_query_attention": round(ms_att, 5)},
         "roofline": roof,
     }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_mq(w, caches[0], q[0], args.cpu_seconds, layers)
     print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_mq(w, layer_cache, q0, budget, layers):
+    """The float64 oracle on layer 0, one (sequence, query) at a time with all
+    heads (query i of sequence b is the one-query problem over its visible
+    tokens 0..p), taking query 0 of every sequence, then query 1, ..., until
+    the budget is spent; the rate is divided by the layer count to compare
+    with the step's query tokens/s."""
+    import numpy as np
+    import threadpoolctl
+
+    import workloads as W
+    from oracle import paged as ref
+
+    kc, vc, ks, vs = layer_cache
+    log("[bench] copying layer 0 to the host for the oracle")
+    kb, vb, qb = W.bits(kc), W.bits(vc), W.bits(q0)
+    ksn = None if ks is None else ks.cpu().numpy()
+    vsn = None if vs is None else vs.cpu().numpy()
+    ql = w.query_lens
+    units = [(b, i) for i in range(w.Q) for b in range(w.B) if i < ql[b]]
+    n = tokens = 0
+    with threadpoolctl.threadpool_limits(1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget and n < len(units):
+            b, i = units[n]
+            p = int(w.context_lens[b]) - int(ql[b]) + i            # the query's position
+            ref.multi_query_attention(qb[b:b + 1, i:i + 1], kb, vb, w.block_tables[b:b + 1],
+                                      np.array([p + 1], dtype=np.int32),
+                                      np.array([1], dtype=np.int32), w.scale, w.kv_dtype,
+                                      ksn, vsn)
+            tokens += p + 1
+            n += 1
+        dt = time.perf_counter() - t0
+    rate = n / dt
+    log(f"[bench] oracle: {n} queries in {dt:.1f}s")
+    return {"value": round(rate / layers, 3), "unit": "query tokens/s", "cores": 1,
+            "kind": "oracle", "per_layer_value": round(rate, 3),
+            "extrapolation": f"rate on layer 0 / {layers} layers",
+            "sample": f"{n} queries of layer 0 (query 0 of every sequence, then query 1, ...; "
+                      f"{tokens} visible tokens, all {w.n_q} heads), numpy float64, 1 process, "
+                      f"1 BLAS thread, {dt:.1f} s; host has {os.cpu_count()} logical CPUs"}
+
+
+def cpu_baseline_cascade(w, layer_cache, q0, plen, slen_np, budget):
+    """The float64 cascade oracle on layer 0, whole sequences (index mod B)
+    until the budget is spent: sequences per second is decode tokens/s per
+    layer, the metric's unit."""
+    import numpy as np
+    import threadpoolctl
+
+    import workloads as W
+    from oracle import paged as ref
+
+    kc, vc, ks, vs = layer_cache
+    log("[bench] copying layer 0 to the host for the oracle")
+    kb, vb, qb = W.bits(kc), W.bits(vc), W.bits(q0)
+    pb = plen // w.bs
+    prefix = np.ascontiguousarray(w.block_tables[0, :pb])
+    tables = np.ascontiguousarray(w.block_tables[:, pb:])
+    n = tokens = 0
+    with threadpoolctl.threadpool_limits(1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget and n < 64 * w.B:
+            b = n % w.B
+            ref.cascade_decode_attention(qb[b:b + 1], kb, vb, prefix, plen, tables[b:b + 1],
+                                         slen_np[b:b + 1], w.scale)
+            tokens += plen + int(slen_np[b])
+            n += 1
+        dt = time.perf_counter() - t0
+    log(f"[bench] oracle: {n} sequences in {dt:.1f}s")
+    return {"value": round(n / dt, 3), "unit": "decode tokens/s per layer", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} whole sequences of layer 0 (sequence index mod {w.B}; {tokens} tokens "
+                      f"attended, all {w.n_q} heads), numpy float64, 1 process, 1 BLAS thread, "
+                      f"{dt:.1f} s; host has {os.cpu_count()} logical CPUs"}
 
 
 def cpu_baseline(w, layer_cache, q0, budget):
