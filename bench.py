@@ -448,7 +448,34 @@ def bench_swap(args, pkv, W, np, torch, dev):
                      "peak": 64.0, "unit": "GB/s", "frac": round(gb / (t_out * 1e-3) / 64.0, 4),
                      "note": "peak = PCIe 5.0 x16 nominal per direction", "traffic": None},
     }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_swap(kc, vc, ids, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_swap(kc, vc, ids, budget):
+    """The oracle's swap (the listed blocks' bytes packed into a host image,
+    then unpacked into other blocks) on host copies of the pools, repeated
+    until the budget is spent; GB/s of image per direction."""
+    import workloads as W
+    from oracle import paged as ref
+
+    log("[bench] copying the pools to the host for the oracle")
+    kb, vb = W.bits(kc), W.bits(vc)
+    back = ids[::-1].copy()
+    n = 0
+    t0 = time.perf_counter()
+    while n == 0 or time.perf_counter() - t0 < budget:
+        image = ref.swap_out(kb, vb, ids)
+        kb, vb = ref.swap_in(kb, vb, back, image)
+        n += 1
+    dt = time.perf_counter() - t0
+    gb = 2 * n * image.nbytes / 1e9
+    log(f"[bench] oracle: {n} swap round trips in {dt:.1f}s")
+    return {"value": round(gb / dt, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} round trips of a {image.nbytes / 1e6:.0f} MB image ({len(ids)} blocks; "
+                      f"the oracle's swap-in returns new copies of the whole pools), numpy, 1 process, "
+                      f"{dt:.1f} s; host has {os.cpu_count()} logical CPUs"}
 
 
 def bench_cascade(args, w, pkv, W, np, torch, dev):
