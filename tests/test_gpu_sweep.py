@@ -6,7 +6,8 @@ and others, 1 to 8 KV heads,
 d_head 64 or 128, 16- or 32-token blocks, bf16 / FP8 / FP4 cache), its batch
 (1..8 sequences, lengths 0..1500 with block-boundary and empty ones), its
 split-K partition (library default or a random block multiple) and, for the
-multi-query half, the query count and per-sequence query lengths. Bars as in
+multi-query half, the query count and per-sequence query lengths; a third
+set has contexts to 20,000 tokens and up to 520 queries. Bars as in
 the other parity tests: max abs error 1e-2 (bf16) / 3e-2 (FP8, FP4),
 relative L2 1e-4, rows past a query length exactly zero.
 """
@@ -52,6 +53,31 @@ CASES = draw_cases(24, 2170)
 # head groups that are not powers of two: partly filled head tiles (decode)
 # and row groups that split a query's heads (multi-query)
 CASES += [(24 + c[0],) + c[1:] for c in draw_cases(12, 2171, (3, 5, 6, 7, 12, 20, 24, 40))]
+
+
+
+def draw_long_cases(n, seed):
+    """Longer contexts (to 20,000 tokens) and larger query counts (to 520),
+    d 128, so the LDS kernels and their partitions see many chunks."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dt = [W.BF16, W.FP8, W.FP4][i % 3]
+        bs = int(rng.choice([16, 32]))
+        n_kv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16, 32, 64]))
+        while G * n_kv > 64 and n_kv > 1:
+            n_kv //= 2
+        B = int(rng.integers(1, 3))
+        lens = [int(x) for x in rng.integers(1, 20001, size=B)]
+        P = 0 if rng.random() < 0.5 else bs * int(rng.integers(1, 300))
+        Q = int(rng.choice([1, 4, 20, 64, 96, 128, 300, 520]))
+        qlens = [int(min(Q, L, rng.integers(0, Q + 1))) for L in lens]
+        cases.append((i, lens, G * n_kv, n_kv, 128, bs, dt, P, Q, qlens))
+    return cases
+
+
+CASES += [(100 + c[0],) + c[1:] for c in draw_long_cases(12, 2172)]
 
 
 @pytest.fixture(scope="module")
