@@ -90,6 +90,9 @@ def parse():
     ap.add_argument("--plain", type=int, default=1,
                     help="shared-prefix workload: also time plain decode on the same tables "
                          "(0: the cascade alone, e.g. for counter runs)")
+    ap.add_argument("--bf16-weights", action="store_true",
+                    help="multi-query workloads: PKV_BF16_WEIGHTS (one bf16 weight per product "
+                         "with V, ~1e-3 relative error)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB block copy (for scaling HBM counters) and exit")
     return ap.parse_args()
@@ -667,7 +670,7 @@ def bench_multi_query(args, w, pkv, W, np, torch, dev):
                 ev[layer][1].record(stream)
             pkv.paged_multi_query_attention(q[layer], qld, kc, vc, bt, cl, w.scale, max_ctx,
                                             k_scale=ks, v_scale=vs, partition_size=P, out=out,
-                                            workspace=ws)
+                                            workspace=ws, bf16_weights=args.bf16_weights)
             if ev is not None:
                 ev[layer][2].record(stream)
 
@@ -699,6 +702,8 @@ def bench_multi_query(args, w, pkv, W, np, torch, dev):
     flops, att_bytes = multi_query_work(w, P_max)
     intensity = flops / att_bytes
     kname = multi_query_kernel_name(w, Q)
+    if args.bf16_weights and kname == "multi_query_lds_pp":
+        kname += " (single bf16 weights)"
     if P_max > 1:
         kname += " + splitk_reduce"
     mfma_bound = intensity > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -714,7 +719,7 @@ def bench_multi_query(args, w, pkv, W, np, torch, dev):
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "bytes_per_launch": att_bytes, "traffic": None}
     traffic = None
-    if os.path.exists(MQ_COUNTERS):
+    if os.path.exists(MQ_COUNTERS) and not args.bf16_weights:
         c = json.load(open(MQ_COUNTERS)).get(w.name, {})
         if c.get("kernel_hash") == kernel_hash(MQ_KERNEL_SOURCES) and c.get("partition") == P:
             traffic = c.get("traffic_bytes_per_launch")
@@ -732,7 +737,8 @@ def bench_multi_query(args, w, pkv, W, np, torch, dev):
         "config": {"workload": w.name, "B": B, "Q": Q, "query_tokens": new_tokens,
                    "tokens_per_layer": w.total_tokens, "n_q": n_q, "n_kv": n_kv, "d_head": d,
                    "block_size": bs, "layers": layers, "kv_dtype": w.kv_dtype,
-                   "partition_size": P, "accumulate": "fp32"},
+                   "partition_size": P, "accumulate": "fp32",
+                   "weights": "bf16" if args.bf16_weights else "bf16 head + tail"},
         "kv_gbs": round(kv_bytes_layer * layers / (ms_step * 1e-3) / 1e9, 2),
         "attention_tflops": round(flops / (ms_att * 1e-3) / 1e12, 2),
         "kernels_ms": {"kv_append": round(avg(t_app), 5),

@@ -27,6 +27,9 @@ PKV_FP8_E4M3 = 1
 PKV_FP32 = 2
 PKV_FP4_E2M1 = 3
 
+# option flags of pkv_paged_multi_query_attention_ex
+PKV_BF16_WEIGHTS = 1
+
 
 class PkvError(RuntimeError):
     def __init__(self, status, what):
@@ -77,6 +80,10 @@ SIGNATURES = {
     "pkv_paged_multi_query_attention": (_i32, [ctypes.POINTER(CacheDesc), _vp, _i32, _vp, _i32,
                                                _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                                _f32, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "pkv_paged_multi_query_attention_ex": (_i32, [ctypes.POINTER(CacheDesc), _vp, _i32, _vp,
+                                                  _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
+                                                  _i32, _i32, _f32, _vp, _vp, _i32, _vp, _sz,
+                                                  _i32, _vp]),
     "pkv_cascade_workspace_bytes": (_sz, [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32,
                                           _i32, _i32]),
     "pkv_cascade_suffix_partition": (_i32, [ctypes.POINTER(CacheDesc), _i32, _i32, _i32, _i32,
@@ -378,10 +385,12 @@ def multi_query_partition_size(k_cache, B, Q, n_q, max_context_len):
 def paged_multi_query_attention(q, query_lens, k_cache, v_cache, block_tables, context_lens,
                                 scale, max_context_len, k_scale=None, v_scale=None,
                                 partition_size=0, out=None, out_dtype=torch.float32,
-                                workspace=None, stream=None):
+                                workspace=None, bf16_weights=False, stream=None):
     """Causal attention of the last query_lens[b] tokens of each sequence (see pkv.h).
 
     q: bfloat16 [B, Q, n_q, d]; returns [B, Q, n_q, d] (rows past query_lens zero).
+    bf16_weights: pass PKV_BF16_WEIGHTS (single bf16 weights in the products
+    with V where the kernel takes them; about 1e-3 relative error).
     """
     _need(query_lens, torch.int32, "query_lens")
     if q.dim() != 4:
@@ -399,12 +408,13 @@ def paged_multi_query_attention(q, query_lens, k_cache, v_cache, block_tables, c
         nbytes = int(lib().pkv_multi_query_workspace_bytes(B, Q, n_q, d, int(max_context_len), P))
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     _check_workspace(workspace, q.device)
-    _check(lib().pkv_paged_multi_query_attention(
+    _check(lib().pkv_paged_multi_query_attention_ex(
         ctypes.byref(desc), _ptr(out), _out_code(out.dtype), _ptr(q), Q, _ptr(query_lens),
         _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), B, n_q, int(max_context_len), float(scale), _ptr(k_scale),
-        _ptr(v_scale), P, _ptr(workspace), workspace.numel(), _stream(stream)),
-        "pkv_paged_multi_query_attention")
+        _ptr(v_scale), P, _ptr(workspace), workspace.numel(),
+        PKV_BF16_WEIGHTS if bf16_weights else 0, _stream(stream)),
+        "pkv_paged_multi_query_attention_ex")
     return out
 
 

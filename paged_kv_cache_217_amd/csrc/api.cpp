@@ -513,7 +513,25 @@ pkv_status pkv_paged_multi_query_attention(const pkv_cache_desc* desc, void* out
                                            const float* k_scale, const float* v_scale,
                                            int32_t partition_size, void* workspace,
                                            size_t workspace_bytes_, void* stream) {
-  if (Q <= 0) return PKV_ERR_INVALID_ARG;
+  return pkv_paged_multi_query_attention_ex(desc, out, out_dtype, q, Q, query_lens, k_cache,
+                                            v_cache, block_tables, max_blocks_per_seq,
+                                            context_lens, B, n_q, max_context_len, scale,
+                                            k_scale, v_scale, partition_size, workspace,
+                                            workspace_bytes_, 0, stream);
+}
+
+pkv_status pkv_paged_multi_query_attention_ex(const pkv_cache_desc* desc, void* out,
+                                              int32_t out_dtype, const void* q, int32_t Q,
+                                              const int32_t* query_lens, const void* k_cache,
+                                              const void* v_cache, const int32_t* block_tables,
+                                              int32_t max_blocks_per_seq,
+                                              const int32_t* context_lens, int32_t B,
+                                              int32_t n_q, int32_t max_context_len, float scale,
+                                              const float* k_scale, const float* v_scale,
+                                              int32_t partition_size, void* workspace,
+                                              size_t workspace_bytes_, int32_t flags,
+                                              void* stream) {
+  if (Q <= 0 || (flags & ~PKV_BF16_WEIGHTS) != 0) return PKV_ERR_INVALID_ARG;
   if (desc && check_desc(desc) == PKV_OK && n_q > 0 && n_q % desc->n_kv == 0 &&
       partition_size == 0 && B >= 0 && max_context_len >= 0)
     partition_size = pick_partition_mq(desc, B, Q, n_q, max_context_len);
@@ -532,6 +550,7 @@ pkv_status pkv_paged_multi_query_attention(const pkv_cache_desc* desc, void* out
   a.query_lens = query_lens;
   a.out = out;
   a.out_dtype = out_dtype;
+  a.bf16_weights = (flags & PKV_BF16_WEIGHTS) != 0;
   const hipStream_t s = as_stream(stream);
   if (g_debug) {
     st = debug_take(s);

@@ -503,7 +503,12 @@ void multi_query_lds_mfma(DecodeArgs a) {
 // registers loaded two phases earlier. In the matrix phase the LDS reads are
 // interleaved with the products (a dozen reads ahead, then one read per two
 // products), so that the reads' latency is covered.
-template <int BS, int FMT>
+//
+// SPLIT_P false (PKV_BF16_WEIGHTS): the weights enter the P V products as one
+// bf16 value each instead of a bf16 head and tail, 64 products per matrix
+// phase instead of 96 (the row sums keep the fp32 weights).
+
+template <int BS, int FMT, bool SPLIT_P = true>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void multi_query_lds_pp(DecodeArgs a) {
   constexpr int D = 128;
@@ -709,7 +714,7 @@ void multi_query_lds_pp(DecodeArgs a) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         asm volatile("" : "+v"(pop_hi[t][ks]));
-        asm volatile("" : "+v"(pop_lo[t][ks]));
+        if constexpr (SPLIT_P) asm volatile("" : "+v"(pop_lo[t][ks]));
       }
       asm volatile("" : "+v"(l[t]));
     }
@@ -733,8 +738,9 @@ void multi_query_lds_pp(DecodeArgs a) {
         for (int t = 0; t < TPW; ++t) {
           acc[t][jj] =
               __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi[t][ks], acc[t][jj], 0, 0, 0);
-          acc[t][jj] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[t][ks], acc[t][jj], 0, 0, 0);
+          if constexpr (SPLIT_P)
+            acc[t][jj] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[t][ks], acc[t][jj], 0, 0, 0);
         }
       }
     }
@@ -765,20 +771,23 @@ void multi_query_lds_pp(DecodeArgs a) {
         for (int i = 0; i < 4; ++i) s[t][4 * rg + i] = sc[rg][t][i];
   };
   // the matrix phase's order: 12 LDS reads, then one read per two products
-  // (48 reads and 96 products in all). bf16 writes its share of the next
+  // (48 reads and 96 products in all; one read per product and 64 products
+  // with single bf16 weights). bf16 writes its share of the next
   // chunks into LDS first; FP8 and FP4 write (and widen) theirs after the
   // products, where the widening overlaps the last products and the wait for
   // the staged loads comes later (2-4% faster than first, measured; bf16 1%
   // slower there).
   auto matrix_order = [&]() __attribute__((always_inline)) {
+    constexpr int MPR = SPLIT_P ? 2 : 1;      // products per LDS read in the middle
+    constexpr int NMF = SPLIT_P ? 96 : 64;    // products per phase
     if constexpr (FMT == kFmtBf16) __builtin_amdgcn_sched_group_barrier(0x200, 2 * PIECES, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
     for (int i = 0; i < 36; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF - 36 * MPR, 0);
     if constexpr (FMT != kFmtBf16) {
       __builtin_amdgcn_sched_group_barrier(0x200, 4 * PIECES, 0);   // two 16-byte stores a piece
       __builtin_amdgcn_sched_group_barrier(0x020, 2 * PIECES, 0);
@@ -837,9 +846,14 @@ void multi_query_lds_pp(DecodeArgs a) {
         uint32_t ph[4], pl[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const Bf16Split sp = split_bf16(p[2 * u], p[2 * u + 1]);
-          ph[u] = sp.hi;
-          pl[u] = sp.lo;
+          if constexpr (SPLIT_P) {
+            const Bf16Split sp = split_bf16(p[2 * u], p[2 * u + 1]);
+            ph[u] = sp.hi;
+            pl[u] = sp.lo;
+          } else {
+            ph[u] = pack_bf16(p[2 * u], p[2 * u + 1]);
+            pl[u] = 0;
+          }
         }
         pop_hi[t][ks] = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
         pop_lo[t][ks] = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
@@ -984,7 +998,10 @@ static hipError_t launch_lds(const DecodeArgs& a, hipStream_t s) {
     const int groups = (rows + 255) / 256;
     if (rows >= 256 && 10 * (2 * groups) <= 11 * ((rows + 127) / 128)) {
       const dim3 grid(a.n_kv * groups, a.B, a.P_max);
-      multi_query_lds_pp<BS, FMT><<<grid, 512, 0, s>>>(a);
+      if (a.bf16_weights)
+        multi_query_lds_pp<BS, FMT, false><<<grid, 512, 0, s>>>(a);
+      else
+        multi_query_lds_pp<BS, FMT, true><<<grid, 512, 0, s>>>(a);
       return hipGetLastError();
     }
   }

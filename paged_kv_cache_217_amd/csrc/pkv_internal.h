@@ -40,6 +40,7 @@ struct DecodeArgs {
   const int32_t* query_lens;  // [B]; nullptr for single-token decode
   bool non_causal;            // multi-query only: every row sees the whole context
   int fixed_ctx;              // context length of every sequence when context_lens is null
+  bool bf16_weights;          // multi-query only: weights may enter P V as one bf16 value
 };
 
 // Schedule buffer: int32 header of kScheduleHeader words, then int2 items.

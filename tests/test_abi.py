@@ -198,6 +198,12 @@ def test_fp4_validation_on_every_attention_entry_point():
     assert _decode(f64, ks=fake, vs=fake) == _lib.PKV_ERR_UNSUPPORTED
     assert _decode(f128) == _lib.PKV_ERR_INVALID_ARG                  # no scales
     assert mq(f64, fake) == _lib.PKV_ERR_UNSUPPORTED
+    # option flags: an unknown bit is refused, a known one passes validation
+    mqx = lambda flags, B=0: L.pkv_paged_multi_query_attention_ex(
+        ctypes.byref(f128), fake, _lib.PKV_FP32, fake, 4, fake, fake, fake, fake, 4, fake, B, 4,
+        64, 0.1, fake, fake, 0, None, 0, flags, None)
+    assert mqx(2) == _lib.PKV_ERR_INVALID_ARG
+    assert mqx(_lib.PKV_BF16_WEIGHTS) == _lib.PKV_OK
     assert mq(f128, None) == _lib.PKV_ERR_INVALID_ARG
     assert mq(f128, fake, B=0) == _lib.PKV_OK
     assert cascade(f64, fake) == _lib.PKV_ERR_UNSUPPORTED

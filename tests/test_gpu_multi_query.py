@@ -30,7 +30,8 @@ def pkv():
     return m
 
 
-def run_mq(pkv, w, Q, qlens, partition_size=0, out_dtype=torch.float32, seed_offset=0):
+def run_mq(pkv, w, Q, qlens, partition_size=0, out_dtype=torch.float32, seed_offset=0,
+           bf16_weights=False):
     kc, vc, ks, vs = W.make_cache(w, seed_offset=seed_offset)
     q = W.make_multi_query(w, Q, seed_offset=seed_offset)
     ql = np.asarray(qlens, dtype=np.int32)
@@ -39,7 +40,7 @@ def run_mq(pkv, w, Q, qlens, partition_size=0, out_dtype=torch.float32, seed_off
         q.to(DEV), torch.from_numpy(ql).to(DEV), kc.to(DEV), vc.to(DEV),
         torch.from_numpy(w.block_tables).to(DEV), torch.from_numpy(w.context_lens).to(DEV),
         w.scale, int(w.context_lens.max()), k_scale=t(ks), v_scale=t(vs),
-        partition_size=partition_size, out_dtype=out_dtype)
+        partition_size=partition_size, out_dtype=out_dtype, bf16_weights=bf16_weights)
     torch.cuda.synchronize()
     expect = ref.multi_query_attention(W.bits(q), W.bits(kc), W.bits(vc), w.block_tables,
                                        w.context_lens, ql, w.scale, w.kv_dtype,
@@ -231,3 +232,40 @@ def test_bf16_output_of_the_lds_kernels_is_the_rounded_fp32_output(pkv, Q):
     out16, _, _ = run_mq(pkv, w, Q, qlens, partition_size=4096, out_dtype=torch.bfloat16)
     check(out32, expect, ql, W.BF16, f"fp32 Q={Q}")
     assert torch.equal(out16, out32.to(torch.bfloat16))
+
+
+# PKV_BF16_WEIGHTS: the ping-pong kernel (256 or more rows per KV head, d 128)
+# feeds each weight to the products with V as one bf16 value, about 1e-3
+# relative error; the max abs bars still hold. Kernels that do not take the
+# flag return the default result bit for bit.
+BF16_WEIGHT_CASES = [
+    # lengths, Q, query lengths, bs, dtype, partition
+    ([700, 1900, 64], 64, [64, 32, 64], 16, W.BF16, 0),       # 512 rows: ping-pong
+    ([1500, 300], 64, [64, 64], 32, W.FP8, 256),               # ping-pong, split
+    ([2100, 900], 32, [32, 17], 32, W.FP4, 0),                 # 256 rows: ping-pong
+    ([2100, 900], 40, [40, 17], 16, W.BF16, 0),                # 320 rows: 128-row kernel
+    ([500, 77], 4, [4, 3], 16, W.FP8, 0),                      # 32 rows: register kernel
+]
+REL_L2_BF16_WEIGHTS = 4e-3
+
+
+@pytest.mark.parametrize("case", BF16_WEIGHT_CASES, ids=[str(i) for i in range(len(BF16_WEIGHT_CASES))])
+def test_bf16_weights_option(pkv, case):
+    lens, Q, qlens, bs, dt, P = case
+    w = W.custom("mqbw", lens, 64, 8, 128, bs, dt, seed=2200 + BF16_WEIGHT_CASES.index(case))
+    out, expect, ql = run_mq(pkv, w, Q, qlens, partition_size=P)
+    outw, _, _ = run_mq(pkv, w, Q, qlens, partition_size=P, bf16_weights=True)
+    rows = Q * 8
+    on_pp = rows >= 256 and 10 * 2 * -(-rows // 256) <= 11 * -(-rows // 128)
+    if not on_pp:
+        assert torch.equal(outw, out)
+        return
+    got = outw.cpu().double().numpy()
+    assert np.all(np.isfinite(got))
+    for b, n in enumerate(ql):
+        assert not np.any(got[b, n:])
+    err = np.max(np.abs(got - expect))
+    rel = np.linalg.norm(got - expect) / np.linalg.norm(expect)
+    print(f"[bf16 weights] {dt} Q={Q}: max abs {err:.2e}, relative L2 {rel:.2e}", flush=True)
+    assert err <= MAX_ABS[dt] and rel <= REL_L2_BF16_WEIGHTS, (err, rel)
+    assert not torch.equal(outw, out)                          # the option took effect
