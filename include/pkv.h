@@ -323,9 +323,10 @@ pkv_status pkv_paged_multi_query_attention(const pkv_cache_desc* desc, void* out
  * bf16 value each instead of a bf16 head and tail (the row sums keep the
  * fp32 weights): a relative error of about 1e-3 instead of about 1e-6, well
  * inside a max abs error of 1e-2 on N(0,1) data, for a third fewer matrix
- * products. Only the kernel for 256 or more rows per KV head at d_head 128
- * takes it (20-23% faster on prompt chunks, measured); the others keep the
- * head and tail.
+ * products. The kernels for 128 or more query rows per KV head (Q times
+ * n_q / n_kv), which share K/V through LDS, take it (measured 1.2-1.4x
+ * faster on prompt chunks); the kernel for fewer rows is bound by memory,
+ * keeps the head and tail, and returns the flag-free result.
  */
 #define PKV_BF16_WEIGHTS 1
 

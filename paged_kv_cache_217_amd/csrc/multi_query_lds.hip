@@ -32,6 +32,9 @@
 // A second form at d = 128 (multi_query_lds_pp, below) takes 256 rows per
 // workgroup and splits each chunk's work into a matrix phase and a vector
 // phase that the two waves of a SIMD run in opposite order.
+// In both, SPLIT_P false (PKV_BF16_WEIGHTS) feeds each weight to the P V
+// products as one bf16 value instead of a bf16 head and tail: half the
+// products with V, while the row sums keep the fp32 weights.
 #include <float.h>
 
 #include <type_traits>
@@ -83,7 +86,7 @@ __device__ __forceinline__ uint2 zero_if(const uint2& w, bool z) {
   return make_uint2(z ? 0u : w.x, z ? 0u : w.y);
 }
 
-template <int D, int BS, int FMT>
+template <int D, int BS, int FMT, bool SPLIT_P = true>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void multi_query_lds_mfma(DecodeArgs a) {
   constexpr bool FP8 = FMT == kFmtFp8;
@@ -373,9 +376,14 @@ void multi_query_lds_mfma(DecodeArgs a) {
         uint32_t ph[4], pl[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const Bf16Split sp = split_bf16(p[2 * u], p[2 * u + 1]);
-          ph[u] = sp.hi;
-          pl[u] = sp.lo;
+          if constexpr (SPLIT_P) {
+            const Bf16Split sp = split_bf16(p[2 * u], p[2 * u + 1]);
+            ph[u] = sp.hi;
+            pl[u] = sp.lo;
+          } else {
+            ph[u] = pack_bf16(p[2 * u], p[2 * u + 1]);
+            pl[u] = 0u;
+          }
         }
         pop_hi[t] = as_bf16x8(ph[0], ph[1], ph[2], ph[3]);
         pop_lo[t] = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
@@ -392,8 +400,9 @@ void multi_query_lds_mfma(DecodeArgs a) {
         for (int t = 0; t < TPW; ++t) {
           acc[t][jj] =
               __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi[t], acc[t][jj], 0, 0, 0);
-          acc[t][jj] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[t], acc[t][jj], 0, 0, 0);
+          if constexpr (SPLIT_P)
+            acc[t][jj] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[t], acc[t][jj], 0, 0, 0);
         }
       }
     }
@@ -504,9 +513,7 @@ void multi_query_lds_mfma(DecodeArgs a) {
 // interleaved with the products (a dozen reads ahead, then one read per two
 // products), so that the reads' latency is covered.
 //
-// SPLIT_P false (PKV_BF16_WEIGHTS): the weights enter the P V products as one
-// bf16 value each instead of a bf16 head and tail, 64 products per matrix
-// phase instead of 96 (the row sums keep the fp32 weights).
+// SPLIT_P false: 64 products per matrix phase instead of 96.
 
 template <int BS, int FMT, bool SPLIT_P = true>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
@@ -1007,7 +1014,10 @@ static hipError_t launch_lds(const DecodeArgs& a, hipStream_t s) {
   }
   const int groups = (rows + 127) / 128;
   const dim3 grid(a.n_kv * groups, a.B, a.P_max);
-  multi_query_lds_mfma<D, BS, FMT><<<grid, 256, 0, s>>>(a);
+  if (a.bf16_weights)
+    multi_query_lds_mfma<D, BS, FMT, false><<<grid, 256, 0, s>>>(a);
+  else
+    multi_query_lds_mfma<D, BS, FMT, true><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -234,30 +234,33 @@ def test_bf16_output_of_the_lds_kernels_is_the_rounded_fp32_output(pkv, Q):
     assert torch.equal(out16, out32.to(torch.bfloat16))
 
 
-# PKV_BF16_WEIGHTS: the ping-pong kernel (256 or more rows per KV head, d 128)
-# feeds each weight to the products with V as one bf16 value, about 1e-3
-# relative error; the max abs bars still hold. Kernels that do not take the
-# flag return the default result bit for bit.
+# PKV_BF16_WEIGHTS: the kernels that share K/V through LDS (128 or more rows
+# per KV head: the ping-pong kernel and the 128-row kernel) feed each weight
+# to the products with V as one bf16 value, about 1e-3 relative error; the
+# max abs bars still hold. The register kernel (fewer rows) does not take the
+# flag and returns the default result bit for bit.
 BF16_WEIGHT_CASES = [
-    # lengths, Q, query lengths, bs, dtype, partition
-    ([700, 1900, 64], 64, [64, 32, 64], 16, W.BF16, 0),       # 512 rows: ping-pong
-    ([1500, 300], 64, [64, 64], 32, W.FP8, 256),               # ping-pong, split
-    ([2100, 900], 32, [32, 17], 32, W.FP4, 0),                 # 256 rows: ping-pong
-    ([2100, 900], 40, [40, 17], 16, W.BF16, 0),                # 320 rows: 128-row kernel
-    ([500, 77], 4, [4, 3], 16, W.FP8, 0),                      # 32 rows: register kernel
+    # lengths, Q, query lengths, bs, dtype, partition, d
+    ([700, 1900, 64], 64, [64, 32, 64], 16, W.BF16, 0, 128),   # 512 rows: ping-pong
+    ([1500, 300], 64, [64, 64], 32, W.FP8, 256, 128),           # ping-pong, split
+    ([2100, 900], 32, [32, 17], 32, W.FP4, 0, 128),             # 256 rows: ping-pong
+    ([2100, 900], 40, [40, 17], 16, W.BF16, 0, 128),            # 320 rows: 128-row kernel
+    ([3000, 40], 15, [15, 15], 16, W.BF16, 512, 128),           # 120 rows: 128-row, split
+    ([1300, 2500], 32, [32, 9], 32, W.FP8, 0, 64),              # d 64: 128-row kernel
+    ([1700, 600], 48, [48, 48], 16, W.BF16, 1024, 64),          # d 64, split
+    ([500, 77], 4, [4, 3], 16, W.FP8, 0, 128),                  # 32 rows: register kernel
 ]
 REL_L2_BF16_WEIGHTS = 4e-3
 
 
 @pytest.mark.parametrize("case", BF16_WEIGHT_CASES, ids=[str(i) for i in range(len(BF16_WEIGHT_CASES))])
 def test_bf16_weights_option(pkv, case):
-    lens, Q, qlens, bs, dt, P = case
-    w = W.custom("mqbw", lens, 64, 8, 128, bs, dt, seed=2200 + BF16_WEIGHT_CASES.index(case))
+    lens, Q, qlens, bs, dt, P, d = case
+    w = W.custom("mqbw", lens, 64, 8, d, bs, dt, seed=2200 + BF16_WEIGHT_CASES.index(case))
     out, expect, ql = run_mq(pkv, w, Q, qlens, partition_size=P)
     outw, _, _ = run_mq(pkv, w, Q, qlens, partition_size=P, bf16_weights=True)
-    rows = Q * 8
-    on_pp = rows >= 256 and 10 * 2 * -(-rows // 256) <= 11 * -(-rows // 128)
-    if not on_pp:
+    on_lds = -(-(Q * 8) // 16) >= 8
+    if not on_lds:
         assert torch.equal(outw, out)
         return
     got = outw.cpu().double().numpy()
@@ -266,6 +269,6 @@ def test_bf16_weights_option(pkv, case):
         assert not np.any(got[b, n:])
     err = np.max(np.abs(got - expect))
     rel = np.linalg.norm(got - expect) / np.linalg.norm(expect)
-    print(f"[bf16 weights] {dt} Q={Q}: max abs {err:.2e}, relative L2 {rel:.2e}", flush=True)
+    print(f"[bf16 weights] {dt} d={d} Q={Q}: max abs {err:.2e}, relative L2 {rel:.2e}", flush=True)
     assert err <= MAX_ABS[dt] and rel <= REL_L2_BF16_WEIGHTS, (err, rel)
     assert not torch.equal(outw, out)                          # the option took effect
