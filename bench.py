@@ -349,6 +349,19 @@ def counter_traffic(name, P):
     return e.get("traffic_bytes_per_launch") if e.get("partition") == P else None
 
 
+def mq_counter_traffic(name, P):
+    """HBM bytes per launch of the multi-query kernel for workload `name` at
+    partition size P, from the committed rocprofv3 counters, or None as for
+    counter_traffic (the source hash is kept once, for every workload)."""
+    if not os.path.exists(MQ_COUNTERS):
+        return None
+    c = json.load(open(MQ_COUNTERS))
+    if c.get("kernel_hash") != kernel_hash(MQ_KERNEL_SOURCES):
+        return None
+    e = c.get(name, {})
+    return e.get("traffic_bytes_per_launch") if e.get("partition") == P else None
+
+
 def kv_bytes(w):
     """K and V bytes one layer's attention reads: every attended token's K and
     V rows of every KV head (2 * n_kv * d_head * bytes per element)."""
@@ -720,9 +733,7 @@ def bench_multi_query(args, w, pkv, W, np, torch, dev):
                 "bytes_per_launch": att_bytes, "traffic": None}
     traffic = None
     if os.path.exists(MQ_COUNTERS) and not args.bf16_weights:
-        c = json.load(open(MQ_COUNTERS)).get(w.name, {})
-        if c.get("kernel_hash") == kernel_hash(MQ_KERNEL_SOURCES) and c.get("partition") == P:
-            traffic = c.get("traffic_bytes_per_launch")
+        traffic = mq_counter_traffic(w.name, P)
     roof["traffic"] = traffic["total"] if traffic else None
     roof["traffic_read"] = traffic["read"] if traffic else None
     roof["traffic_written"] = traffic["written"] if traffic else None

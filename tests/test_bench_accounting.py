@@ -104,3 +104,24 @@ def test_counter_traffic_is_reported_only_for_measured_configurations():
         assert abs(t["total"] - algo) <= tol * algo, (w.name, t["total"], algo)
         assert t["total"] == t["read"] + t["written"]
         assert bench.counter_traffic(w.name, P // 2) is None
+
+
+def test_multi_query_counter_traffic_resolves_while_sources_match():
+    """The multi-query workloads' committed counters are found at their bench
+    partition while the sources match (verification reads its context once,
+    within 1% of its algorithmic bytes); other partitions give None."""
+    current = bench.kernel_hash(bench.MQ_KERNEL_SOURCES)
+    import json
+    committed = json.load(open(bench.MQ_COUNTERS))["kernel_hash"]
+    for w in (W.spec_verify_70b(), W.chunked_prefill_70b()):
+        t = bench.mq_counter_traffic(w.name, 8192)
+        if committed != current:
+            assert t is None
+            continue
+        assert t is not None, w.name
+        assert t["total"] == t["read"] + t["written"]
+        assert bench.mq_counter_traffic(w.name, 4096) is None
+    t = bench.mq_counter_traffic(W.spec_verify_70b().name, 8192)
+    if t is not None:
+        _, algo = bench.multi_query_work(W.spec_verify_70b(), 1)
+        assert abs(t["total"] - algo) <= 0.01 * algo, (t["total"], algo)
