@@ -91,8 +91,9 @@ def parse():
                     help="shared-prefix workload: also time plain decode on the same tables "
                          "(0: the cascade alone, e.g. for counter runs)")
     ap.add_argument("--bf16-weights", action="store_true",
-                    help="multi-query workloads: PKV_BF16_WEIGHTS (one bf16 weight per product "
-                         "with V, ~1e-3 relative error)")
+                    help="multi-query and shared-prompt workloads: PKV_BF16_WEIGHTS (one bf16 "
+                         "weight per product with V in the multi-query kernels, ~1e-3 relative "
+                         "error)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB block copy (for scaling HBM counters) and exit")
     return ap.parse_args()
@@ -555,7 +556,8 @@ def bench_cascade(args, w, pkv, W, np, torch, dev):
                 pkv.cascade_decode_attention(q[layer], kc, vc, pt, plen, st, slen, w.scale, max_s,
                                              prefix_partition=args.prefix_partition,
                                              suffix_partition=args.partition, out=out,
-                                             workspace=cws, schedule=sched)
+                                             workspace=cws, schedule=sched,
+                                             bf16_weights=args.bf16_weights)
             else:
                 pkv.paged_decode_attention(q[layer], kc, vc, bt, cl, w.scale, max_ctx,
                                            partition_size=P, out=out, workspace=dws,
@@ -598,7 +600,8 @@ def bench_cascade(args, w, pkv, W, np, torch, dev):
         "config": {"workload": w.name, "B": B, "prefix_len": plen,
                    "suffix_partition": args.partition or "library default",
                    "suffix_len": [int(slen_np.min()), max_s], "n_q": n_q, "n_kv": n_kv,
-                   "d_head": d, "block_size": bs, "layers": layers, "kv_dtype": w.kv_dtype},
+                   "d_head": d, "block_size": bs, "layers": layers, "kv_dtype": w.kv_dtype,
+                   "prefix_weights": "bf16" if args.bf16_weights else "bf16 head + tail"},
         "attention_us_per_layer": {"cascade": round(ms_att * 1000, 1),
                                    "plain_decode": round(res[False][1] * 1000, 1)
                                    if False in res else None},
@@ -612,7 +615,8 @@ def bench_cascade(args, w, pkv, W, np, torch, dev):
     # HBM bytes of one call (all its launches), from the committed counters,
     # while the sources they were taken on are unchanged and the call is the
     # library's default one
-    if os.path.exists(CASCADE_COUNTERS) and not args.partition and not args.prefix_partition:
+    if (os.path.exists(CASCADE_COUNTERS) and not args.partition and not args.prefix_partition
+            and not args.bf16_weights):
         c = json.load(open(CASCADE_COUNTERS))
         if c.get("kernel_hash") == kernel_hash(CASCADE_KERNEL_SOURCES):
             t = c["traffic_bytes_per_call"]

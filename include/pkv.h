@@ -445,6 +445,22 @@ pkv_status pkv_cascade_decode_attention(
     const float* v_scale, int32_t prefix_partition, int32_t suffix_partition,
     const void* suffix_schedule, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same with option flags (pkv_cascade_decode_attention is this with
+ * flags == 0); a flag bit other than PKV_BF16_WEIGHTS returns
+ * PKV_ERR_INVALID_ARG. PKV_BF16_WEIGHTS applies to the prefix pass, which
+ * runs on the multi-token-query kernels, as it does to
+ * pkv_paged_multi_query_attention_ex (about 1e-3 relative error on the
+ * prefix's share of the output); the suffix pass and the merge are
+ * unchanged. */
+pkv_status pkv_cascade_decode_attention_ex(
+    const pkv_cache_desc* desc, void* out, int32_t out_dtype, const void* q, const void* k_cache,
+    const void* v_cache, const int32_t* prefix_table, int32_t prefix_len,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* suffix_lens,
+    int32_t B, int32_t n_q, int32_t max_suffix_len, float scale, const float* k_scale,
+    const float* v_scale, int32_t prefix_partition, int32_t suffix_partition,
+    const void* suffix_schedule, void* workspace, size_t workspace_bytes, int32_t flags,
+    void* stream);
+
 /* ---------------------------------------------------------------------------
  * Swap of KV blocks to host memory and back ([LLMI] "9. Failure modes and
  * limitations": under memory pressure a request is preempted by evicting its

@@ -27,7 +27,7 @@ PKV_FP8_E4M3 = 1
 PKV_FP32 = 2
 PKV_FP4_E2M1 = 3
 
-# option flags of pkv_paged_multi_query_attention_ex
+# option flags of pkv_paged_multi_query_attention_ex and pkv_cascade_decode_attention_ex
 PKV_BF16_WEIGHTS = 1
 
 
@@ -91,6 +91,10 @@ SIGNATURES = {
     "pkv_cascade_decode_attention": (_i32, [ctypes.POINTER(CacheDesc), _vp, _i32, _vp, _vp, _vp,
                                             _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
                                             _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "pkv_cascade_decode_attention_ex": (_i32, [ctypes.POINTER(CacheDesc), _vp, _i32, _vp, _vp,
+                                               _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
+                                               _f32, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _i32,
+                                               _vp]),
     "pkv_decode_schedule_bytes": (_sz, [_i32, _i32, _i32]),
     "pkv_decode_schedule": (_i32, [_vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "pkv_splitk_reduce": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -443,9 +447,13 @@ def cascade_decode_attention(q, k_cache, v_cache, prefix_table, prefix_len, bloc
                              suffix_lens, scale, max_suffix_len, k_scale=None, v_scale=None,
                              prefix_partition=0, suffix_partition=0, out=None,
                              out_dtype=torch.float32, workspace=None, schedule=None,
-                             stream=None):
+                             bf16_weights=False, stream=None):
     """Decode attention over prefix_table ++ block_tables[b] with the shared
-    prefix's K/V read once for the whole batch (see pkv.h)."""
+    prefix's K/V read once for the whole batch (see pkv.h).
+
+    bf16_weights: pass PKV_BF16_WEIGHTS to the prefix pass (single bf16
+    weights in its products with V; about 1e-3 relative error).
+    """
     desc, B, n_q, d = _decode_common(q, k_cache, v_cache, block_tables, suffix_lens,
                                      k_scale, v_scale)
     if prefix_len:
@@ -463,13 +471,14 @@ def cascade_decode_attention(q, k_cache, v_cache, prefix_table, prefix_len, bloc
     _check_workspace(workspace, q.device)
     if schedule is not None:
         _need(schedule, torch.int32, "schedule")
-    _check(lib().pkv_cascade_decode_attention(
+    _check(lib().pkv_cascade_decode_attention_ex(
         ctypes.byref(desc), _ptr(out), _out_code(out.dtype), _ptr(q), _ptr(k_cache),
         _ptr(v_cache), _ptr(prefix_table) if prefix_len else None, int(prefix_len),
         _ptr(block_tables), block_tables.shape[1], _ptr(suffix_lens), B, n_q,
         int(max_suffix_len), float(scale), _ptr(k_scale), _ptr(v_scale), int(prefix_partition),
         int(suffix_partition), _ptr(schedule), _ptr(workspace), workspace.numel(),
-        _stream(stream)), "pkv_cascade_decode_attention")
+        PKV_BF16_WEIGHTS if bf16_weights else 0, _stream(stream)),
+        "pkv_cascade_decode_attention_ex")
     return out
 
 

@@ -659,6 +659,22 @@ pkv_status pkv_cascade_decode_attention(
     int32_t B, int32_t n_q, int32_t max_suffix_len, float scale, const float* k_scale,
     const float* v_scale, int32_t prefix_partition, int32_t suffix_partition,
     const void* suffix_schedule, void* workspace, size_t workspace_bytes_, void* stream) {
+  return pkv_cascade_decode_attention_ex(desc, out, out_dtype, q, k_cache, v_cache, prefix_table,
+                                         prefix_len, block_tables, max_blocks_per_seq,
+                                         suffix_lens, B, n_q, max_suffix_len, scale, k_scale,
+                                         v_scale, prefix_partition, suffix_partition,
+                                         suffix_schedule, workspace, workspace_bytes_, 0, stream);
+}
+
+pkv_status pkv_cascade_decode_attention_ex(
+    const pkv_cache_desc* desc, void* out, int32_t out_dtype, const void* q, const void* k_cache,
+    const void* v_cache, const int32_t* prefix_table, int32_t prefix_len,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* suffix_lens,
+    int32_t B, int32_t n_q, int32_t max_suffix_len, float scale, const float* k_scale,
+    const float* v_scale, int32_t prefix_partition, int32_t suffix_partition,
+    const void* suffix_schedule, void* workspace, size_t workspace_bytes_, int32_t flags,
+    void* stream) {
+  if ((flags & ~PKV_BF16_WEIGHTS) != 0) return PKV_ERR_INVALID_ARG;
   CascadePlan pl;
   pkv_status st = plan_cascade(desc, B, n_q, prefix_len, prefix_partition, max_suffix_len,
                                suffix_partition, &pl);
@@ -710,6 +726,7 @@ pkv_status pkv_cascade_decode_attention(
     a.B = 1;
     a.Q = B;
     a.non_causal = true;
+    a.bf16_weights = (flags & PKV_BF16_WEIGHTS) != 0;
     a.n_q = n_q;
     a.n_kv = desc->n_kv;
     a.d = desc->d_head;

@@ -204,6 +204,11 @@ def test_fp4_validation_on_every_attention_entry_point():
         64, 0.1, fake, fake, 0, None, 0, flags, None)
     assert mqx(2) == _lib.PKV_ERR_INVALID_ARG
     assert mqx(_lib.PKV_BF16_WEIGHTS) == _lib.PKV_OK
+    cx = lambda flags, B=0: L.pkv_cascade_decode_attention_ex(
+        ctypes.byref(f128), fake, _lib.PKV_FP32, fake, fake, fake, fake, 32, fake, 4, fake, B, 4,
+        32, 0.1, fake, fake, 0, 0, None, fake, 1 << 20, flags, None)
+    assert cx(2) == _lib.PKV_ERR_INVALID_ARG
+    assert cx(_lib.PKV_BF16_WEIGHTS) == _lib.PKV_OK
     assert mq(f128, None) == _lib.PKV_ERR_INVALID_ARG
     assert mq(f128, fake, B=0) == _lib.PKV_OK
     assert cascade(f64, fake) == _lib.PKV_ERR_UNSUPPORTED

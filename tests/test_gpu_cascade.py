@@ -158,3 +158,42 @@ def test_bf16_output_is_the_rounded_fp32_output(pkv):
     torch.cuda.synchronize()
     assert out16.dtype == torch.bfloat16
     assert torch.equal(out16, out32.to(torch.bfloat16))
+
+
+# PKV_BF16_WEIGHTS through the cascade: the prefix pass takes single bf16
+# weights where it runs on an LDS kernel (128 or more prefix rows, B x G);
+# about 1e-3 relative error, the max abs bars still hold. With fewer rows the
+# register kernel runs and the result is the default one bit for bit.
+BF16_WEIGHT_CASES = [0, 2, 3, 7, 8, 10]
+
+
+@pytest.mark.parametrize("ci", BF16_WEIGHT_CASES)
+def test_cascade_bf16_weights_option(pkv, ci):
+    suffix, plen, n_q, n_kv, d, bs, dt, Pp, Ps = CASES[ci]
+    w, kc, vc, ks, vs, pt, tables, slen, q = shared_prefix_case(
+        suffix, plen, n_q, n_kv, d, bs, dt, seed=100 + ci)
+    t = lambda x: None if x is None else x.to(DEV)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    max_s = int(slen.max())
+    args = (q.to(DEV), kd, vd, torch.from_numpy(pt).to(DEV), plen,
+            torch.from_numpy(tables).to(DEV), torch.from_numpy(slen).to(DEV), w.scale, max_s)
+    kw = dict(k_scale=t(ks), v_scale=t(vs), prefix_partition=Pp, suffix_partition=Ps)
+    out = pkv.cascade_decode_attention(*args, **kw)
+    outw = pkv.cascade_decode_attention(*args, bf16_weights=True, **kw)
+    torch.cuda.synchronize()
+    rows = len(suffix) * (n_q // n_kv)
+    if plen == 0 or -(-rows // 16) < 8:
+        assert torch.equal(outw, out)
+        return
+    expect = ref.cascade_decode_attention(W.bits(q), W.bits(kc), W.bits(vc), pt, plen, tables,
+                                          slen, w.scale, dt,
+                                          None if ks is None else ks.numpy(),
+                                          None if vs is None else vs.numpy())
+    got = outw.cpu().double().numpy()
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - expect))
+    rel = np.linalg.norm(got - expect) / max(np.linalg.norm(expect), 1e-30)
+    print(f"[cascade bf16 weights] case {ci} {dt}: max abs {err:.2e}, relative L2 {rel:.2e}",
+          flush=True)
+    assert err <= MAX_ABS[dt] and rel <= 4e-3, (err, rel)
+    assert not torch.equal(outw, out)                       # the option took effect
